@@ -1,0 +1,325 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against a
+value the pages print, a hand derivation, a closed form of the method, a
+library routine on a reduction of the method, or a pure-Python brute force.
+
+P1 = abeam.tech SmoothQuant explainer; P4 = blogs.itmedia.co.jp 量子化 blog.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Quantiser: P4 section 3 worked example, ties, bounds
+
+def test_p4_worked_example(ref):
+    g = _golden("p4_worked_example.json")
+    q = ref.quantize_value(g["value"], g["step"])
+    assert q == g["code"]
+    assert q * g["step"] == g["dequantized"]
+    assert g["value"] - q * g["step"] == g["error"]
+
+
+@pytest.mark.parametrize("v,expect", [(62.5, 63), (-62.5, -63), (0.5, 1), (-0.5, -1),
+                                      (0.49999997, 0), (-0.49999997, 0), (126.5, 127),
+                                      (127.0, 127), (-127.0, -127), (1.5, 2), (2.5, 3),
+                                      (0.0, 0)])
+def test_ties_round_away_from_zero(ref, v, expect):
+    # step 1 exactly (absmax 127): v / step == v, so only the rounding rule acts.
+    assert ref.step(127.0) == 1.0
+    assert ref.quantize_value(v, 1.0) == expect
+
+
+def test_clamp_to_127(ref):
+    # A value beyond the range (static steps) clamps to the symmetric code range.
+    assert ref.quantize_value(500.0, 1.0) == 127
+    assert ref.quantize_value(-500.0, 1.0) == -127
+
+
+def test_zero_vector_has_zero_step_and_codes(ref):
+    q, st = ref.quantize_vector(np.zeros(33, np.float32))
+    assert st == 0.0 and not q.any()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_quantizer_matches_bruteforce(ref, seed):
+    r = np.random.default_rng([7, seed])
+    v = (r.standard_normal(97) * r.choice([1e-3, 1.0, 37.0])).astype(np.float32)
+    v[r.integers(0, 97)] *= 40  # an outlier sets the range
+    q, st = ref.quantize_vector(v)
+    qb, stb = brute.quantize_vector(v)
+    assert st == stb
+    assert q.tolist() == qb
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_quantizer_error_bound_and_full_range(ref, seed):
+    r = np.random.default_rng([8, seed])
+    x = r.standard_normal((64, 301)).astype(np.float32) * 3
+    xq, sx = ref.quant_act_pertoken(x)
+    # every non-zero row uses the extreme code (the range is set by the absmax)
+    assert (np.abs(xq.astype(np.int32)).max(axis=1) == 127).all()
+    assert xq.min() >= -127
+    # |v - q*step| <= step * (1/2 + 2^-17) elementwise, evaluated in fp64
+    err = np.abs(x.astype(np.float64) - xq.astype(np.float64) * sx[:, None].astype(np.float64))
+    assert (err <= sx[:, None].astype(np.float64) * (0.5 + 2.0 ** -17)).all()
+    # the step is absmax/127 of each row (library reduction of the same data)
+    np.testing.assert_array_equal(sx, (np.abs(x).max(axis=1) / np.float32(127)).astype(np.float32))
+
+
+def test_weight_quant_is_per_output_channel_and_transposed(ref):
+    r = np.random.default_rng(11)
+    w = (r.standard_normal((37, 5)) * 0.02).astype(np.float32)
+    w[:, 3] *= 50  # one loud output channel must not coarsen the others
+    wq, sw = ref.quant_weight_perchannel(w)
+    assert wq.shape == (5, 37) and sw.shape == (5,)
+    for n in range(5):
+        codes, st = brute.quantize_vector(w[:, n])
+        assert sw[n] == st
+        assert wq[n].tolist() == codes
+
+
+# --------------------------------------------------------------------------
+# INT8 GEMM: brute force over Python integers
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (17, 9, 64), (8, 33, 129), (5, 4, 300)])
+def test_gemm_matches_python_ints(ref, shape):
+    M, N, K = shape
+    xq = synth.random_int8(M * 1000 + K, M, K)
+    wq = synth.random_int8(N * 1000 + K + 1, N, K)
+    xq[0, :] = 127
+    wq[0, :] = -127  # extremes included
+    acc = ref.gemm_i32(xq, wq)
+    assert acc.tolist() == brute.gemm_int(xq, wq)
+
+
+def test_gemm_sampled_equals_full(ref):
+    xq = synth.random_int8(1, 40, 200)
+    wq = synth.random_int8(2, 30, 200)
+    rows = np.array([0, 7, 39, 7])
+    cols = np.array([29, 0, 3])
+    sub = ref.gemm_i32_sampled(xq, wq, rows, cols)
+    assert sub.tolist() == [[r[c] for c in cols] for r in np.array(brute.gemm_int(xq[rows], wq)).tolist()]
+
+
+def test_gemm_int32_worst_case_fits():
+    # |acc| <= K * 127^2 < 2^31 at the largest accepted K.
+    assert 133144 * 127 * 127 == 2147479576 < 2 ** 31
+    assert 133145 * 127 * 127 >= 2 ** 31
+
+
+def test_gemm_worst_case_value(ref):
+    K = 133144
+    xq = np.full((1, K), 127, np.int8)
+    wq = np.full((2, K), 127, np.int8)
+    wq[1] = -127
+    acc = ref.gemm_i32_sampled(xq, wq, np.array([0]), np.array([0, 1]))
+    assert acc.tolist() == [[2147479576, -2147479576]]
+    with pytest.raises(ValueError):
+        ref.gemm_i32(np.zeros((1, K + 1), np.int8), np.zeros((1, K + 1), np.int8))
+
+
+def test_int8_numpy_wrap_pitfall_is_avoided(ref):
+    a = np.array([[127, 127]], np.int8)
+    assert int(np.dot(a[0], a[0])) != 2 * 127 * 127  # numpy int8 dot wraps
+    assert ref.gemm_i32(a, a)[0, 0] == 2 * 127 * 127
+
+
+# --------------------------------------------------------------------------
+# Calibration and smoothing factor (P1 smoothing factor section, identity)
+
+def test_calibration_is_columnwise_absmax_and_running(ref):
+    r = np.random.default_rng(3)
+    x = r.standard_normal((50, 70)).astype(np.float32)
+    a = ref.calibrate_absmax(x)
+    np.testing.assert_array_equal(a, np.abs(x).max(axis=0))
+    a2 = ref.calibrate_absmax(x[30:], ref.calibrate_absmax(x[:30]))
+    np.testing.assert_array_equal(a, a2)
+
+
+def test_hand_chain_golden(ref):
+    g = _golden("hand_chain_2x2.json")
+    a = ref.calibrate_absmax(np.array(g["X_cal"], np.float32))
+    assert a.tolist() == g["a"]
+    W = np.array(g["W"], np.float32)
+    assert ref.weight_row_absmax(W).tolist() == g["b"]
+    s, w_hat, _, _ = ref.smooth_fold(a, W, g["alpha"])
+    assert s.tolist() == g["s"]
+    assert w_hat.tolist() == g["W_hat"]
+    wq, sw = ref.quant_weight_perchannel(w_hat)
+    assert wq.tolist() == g["Wq"]
+    np.testing.assert_array_equal(sw, np.array(g["sw_absmax"], np.float32) / np.float32(127))
+    x_hat = ref.smooth_activation(np.array(g["X"], np.float32), s)
+    np.testing.assert_array_equal(x_hat, np.array(g["X_hat"], np.float32))
+    xq, sx = ref.quant_act_pertoken(x_hat)
+    assert xq.tolist() == g["Xq"]
+    acc = ref.gemm_i32(xq, wq)
+    assert acc.tolist() == g["acc"]
+    y = ref.dequant(acc, sx, sw)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=1e-6)
+    np.testing.assert_allclose(y, np.array(g["XW"]), rtol=2e-3)
+    np.testing.assert_array_equal(ref.linear_w8a8(x_hat, wq, sw), y)
+
+
+def _outlier_problem(seed, K=96, N=40, T=128, M=24, factor=40.0):
+    r = np.random.default_rng([5, seed])
+    cols = r.choice(K, 4, replace=False)
+    xc = r.standard_normal((T, K)).astype(np.float32)
+    xc[:, cols] *= factor
+    x = r.standard_normal((M, K)).astype(np.float32)
+    x[:, cols] *= factor
+    w = (r.standard_normal((K, N)) * 0.02).astype(np.float32)
+    return xc, x, w
+
+
+@pytest.mark.parametrize("alpha", [0.4, 0.5, 0.6, 0.75])
+def test_identity_holds_fp64(ref, alpha):
+    # (X diag(s)^-1)(diag(s) W) == X W  [P1 数学的に何をしているのか]
+    xc, x, w = _outlier_problem(1)
+    s, w_hat, _, _ = ref.smooth_fold(ref.calibrate_absmax(xc), w, alpha)
+    s64 = s.astype(np.float64)
+    lhs = (x.astype(np.float64) / s64) @ (s64[:, None] * w.astype(np.float64))
+    rhs = x.astype(np.float64) @ w.astype(np.float64)
+    assert np.abs(lhs - rhs).max() / np.abs(rhs).max() <= 1e-12
+    # and the oracle's fp32 fold realises it up to fp32 rounding
+    lhs32 = ref.smooth_activation(x, s).astype(np.float64) @ w_hat.astype(np.float64)
+    assert np.abs(lhs32 - rhs).max() / np.abs(rhs).max() <= 1e-6
+
+
+def test_alpha_half_balances_maxima(ref):
+    # At alpha = 0.5: max|X_hat_j| = max|W_hat_j| = sqrt(max|X_j| max|W_j|)
+    xc, _, w = _outlier_problem(2)
+    a = ref.calibrate_absmax(xc)
+    b = np.abs(w).max(axis=1)
+    s, w_hat, _, _ = ref.smooth_fold(a, w, 0.5)
+    xm = np.abs(ref.smooth_activation(xc, s)).max(axis=0).astype(np.float64)
+    wm = np.abs(w_hat).max(axis=1).astype(np.float64)
+    target = np.sqrt(a.astype(np.float64) * b.astype(np.float64))
+    ulp = np.spacing(target.astype(np.float32)).astype(np.float64)
+    assert (np.abs(xm - target) <= 4 * ulp).all()
+    assert (np.abs(wm - target) <= 4 * ulp).all()
+
+
+@pytest.mark.parametrize("alpha", [0.4, 0.6, 0.75])
+def test_alpha_closed_form(ref, alpha):
+    # s = a^alpha / b^(1-alpha) gives max|X_hat_j| = a/s = (a b)^(1-alpha) and
+    # max|W_hat_j| = s b = (a b)^alpha; their product is a_j b_j for every alpha.
+    xc, _, w = _outlier_problem(3)
+    a = ref.calibrate_absmax(xc).astype(np.float64)
+    b = np.abs(w).max(axis=1).astype(np.float64)
+    s, w_hat, _, _ = ref.smooth_fold(a.astype(np.float32), w, alpha)
+    xm = np.abs(ref.smooth_activation(xc, s)).max(axis=0).astype(np.float64)
+    wm = np.abs(w_hat).max(axis=1).astype(np.float64)
+    np.testing.assert_allclose(xm, (a * b) ** (1 - alpha), rtol=4e-7)
+    np.testing.assert_allclose(wm, (a * b) ** alpha, rtol=4e-7)
+    np.testing.assert_allclose(xm * wm, a * b, rtol=8e-7)
+
+
+def test_alpha_one_flattens_activations_exactly(ref):
+    # alpha = 1: s_j = max|X_j| exactly, so every calibration channel's max is 1.0
+    xc, _, w = _outlier_problem(4)
+    a = ref.calibrate_absmax(xc)
+    s, _, _, _ = ref.smooth_fold(a, w, 1.0)
+    np.testing.assert_array_equal(s, a)
+    np.testing.assert_array_equal(np.abs(ref.smooth_activation(xc, s)).max(axis=0), 1.0)
+
+
+def test_alpha_zero_normalises_weights(ref):
+    xc, _, w = _outlier_problem(5)
+    a = ref.calibrate_absmax(xc)
+    s, w_hat, _, _ = ref.smooth_fold(a, w, 0.0)
+    b = np.abs(w).max(axis=1)
+    np.testing.assert_array_equal(s, (np.float32(1) / b).astype(np.float32))
+    wm = np.abs(w_hat).max(axis=1)
+    assert (np.abs(wm - 1.0) <= 2.0 ** -23).all()
+
+
+def test_zero_channel_gets_unit_factor(ref):
+    a = np.array([0.0, 2.0, 3.0], np.float32)
+    w = np.array([[1.0, 2.0], [0.0, 0.0], [0.5, -4.0]], np.float32)
+    s, _, _, _ = ref.smooth_fold(a, w, 0.5)
+    assert s[0] == 1.0 and s[1] == 1.0
+    assert s[2] == np.float32(math.sqrt(3.0) / math.sqrt(4.0))
+
+
+def test_layernorm_fold(ref):
+    # LN(x)/s = (gamma/s) n + beta/s: folding diag(s)^-1 into LN gives the
+    # same smoothed activations as dividing the LN output by s.
+    r = np.random.default_rng(9)
+    K = 64
+    s = (np.exp(r.standard_normal(K))).astype(np.float32)
+    gamma = (1 + 0.1 * r.standard_normal(K)).astype(np.float32)
+    beta = (0.1 * r.standard_normal(K)).astype(np.float32)
+    g2, b2 = ref.fold_norm(s, gamma, beta)
+    n = r.standard_normal((8, K))
+    lhs = n * g2.astype(np.float64) + b2.astype(np.float64)
+    rhs = (n * gamma.astype(np.float64) + beta.astype(np.float64)) / s.astype(np.float64)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-6, atol=1e-7)
+
+
+# --------------------------------------------------------------------------
+# Whole chain
+
+@pytest.mark.parametrize("alpha", [0.5, 0.75])
+def test_chain_error_bound(ref, alpha):
+    # |Y_q - X_hat W_hat| <= sum_k (|x|dw/2 + |w|dx/2 + dx dw/4) (+ tiny fp slack)
+    xc, x, w = _outlier_problem(6)
+    s, w_hat, _, _ = ref.smooth_fold(ref.calibrate_absmax(xc), w, alpha)
+    x_hat = ref.smooth_activation(x, s)
+    wq, sw = ref.quant_weight_perchannel(w_hat)
+    xq, sx = ref.quant_act_pertoken(x_hat)
+    y = ref.dequant(ref.gemm_i32(xq, wq), sx, sw)
+    exact = x_hat.astype(np.float64) @ w_hat.astype(np.float64)
+    dx = sx.astype(np.float64)[:, None]
+    dw = sw.astype(np.float64)[None, :]
+    ax = np.abs(x_hat.astype(np.float64)).sum(axis=1)[:, None]
+    aw = np.abs(w_hat.astype(np.float64)).sum(axis=0)[None, :]
+    K = x.shape[1]
+    bound = (ax * dw + aw * dx) * (0.5 + 2.0 ** -17) + K * dx * dw / 4
+    assert (np.abs(y - exact) <= bound * (1 + 1e-9) + 1e-12).all()
+
+
+def test_smoothing_beats_naive_w8a8_on_outliers(ref):
+    # P1 結果 / 精度: naive W8A8 (no smoothing) degrades on outlier activations,
+    # SmoothQuant (alpha = 0.5) stays close to the float result.
+    xc, x, w = _outlier_problem(7, K=256, N=64, factor=60.0)
+    exact = x.astype(np.float64) @ w.astype(np.float64)
+
+    def err(alpha):
+        if alpha is None:
+            x_hat, w_hat = x, w
+        else:
+            s, w_hat, _, _ = ref.smooth_fold(ref.calibrate_absmax(xc), w, alpha)
+            x_hat = ref.smooth_activation(x, s)
+        wq, sw = ref.quant_weight_perchannel(w_hat)
+        y = ref.linear_w8a8(x_hat, wq, sw)
+        return np.linalg.norm(y - exact) / np.linalg.norm(exact)
+
+    assert err(0.5) < 0.5 * err(None)
+
+
+def test_synth_outliers_persist():
+    cfg = synth.CONFIGS[1]
+    idx = synth.outlier_channels(cfg, "toy")
+    assert len(idx) == 5
+    xc = synth.activations(cfg, "toy", 64, calibration=True).numpy()
+    xe = synth.activations(cfg, "toy", 16).numpy()
+    for x in (xc, xe):
+        col = np.abs(x).max(axis=0)
+        assert set(np.argsort(col)[-5:]) == set(idx.tolist())
+    assert not np.array_equal(xc[:16], xe)
