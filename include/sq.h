@@ -1,0 +1,153 @@
+/*
+ * sq.h -- C ABI of the SmoothQuant W8A8 linear-layer library for AMD MI355X
+ * (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   [P1] abeam.tech explainer of Xiao et al., "SmoothQuant: Accurate and
+ *        Efficient Post-Training Quantization for Large Language Models"
+ *        (arXiv 2211.10438).
+ *   [P4] blogs.itmedia.co.jp, 「LLMのダイエット術、『量子化（Quantization）』」.
+ *
+ *   offline : calibrate per-input-channel activation absmax; smoothing
+ *             factor s_j; fold diag(s) into W and diag(s)^-1 into the
+ *             preceding LayerNorm; quantise W to INT8 per output channel.
+ *   runtime : quantise each token of X_hat to INT8 by its own absmax; INT8 x
+ *             INT8 -> INT32 GEMM; scale back by token step x channel step.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous and
+ *     row-major, each 16-byte aligned.  Sizes are element counts.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Each call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising; results are ready when the
+ *     stream reaches that point.
+ *   - On a validation error nothing is launched and nothing is written; the
+ *     status says which rule failed.  A launch failure returns SQ_ERR_HIP.
+ *     Faults inside a kernel surface at the caller's next synchronisation,
+ *     as with any HIP call.
+ *   - Inputs must be finite (NaN/Inf are outside the contract).
+ *   - Every input and output buffer must be distinct (no aliasing) unless a
+ *     description says otherwise.
+ *   - The library keeps no state between calls and allocates no device
+ *     memory; calls on different streams are independent.
+ *
+ * Quantiser used everywhere [P1 なぜ活性値が量子化しづらいのか: the range is
+ * set by the largest absolute value; P4 section 3: range -> scale -> round
+ * to nearest; scale back at inference]:
+ *   step = absmax / 127.0f (fp32 IEEE division);
+ *   code = clamp(round_half_away_from_zero(v / step), -127, 127), v / step an
+ *          fp32 IEEE division; an all-zero vector has step 0 and codes 0.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    SQ_ERR_SHAPE = 2,       /* a size is < 1 or > SQ_MAX_DIM */
+    SQ_ERR_DTYPE = 3,       /* dtype code not accepted by this entry point */
+    SQ_ERR_K_OVERFLOW = 4,  /* K > SQ_MAX_K: int32 accumulators could overflow */
+    SQ_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
+    SQ_ERR_ALPHA = 6,       /* alpha outside [0, 1] or not finite */
+    SQ_ERR_HIP = 7          /* the HIP runtime reported a launch error */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
+
+/* |sum_k xq*wq| <= K * 127 * 127 < 2^31 holds for K <= 133144. */
+#define SQ_MAX_K 133144
+/* Largest accepted M, N, K, T (rows and columns are indexed with int). */
+#define SQ_MAX_DIM 4194304
+
+/* ---------------------------------------------------------------- offline */
+
+/* Calibration statistic [P1 用語解説 "Calibration"; 学習方法; the max(|X_j|)
+ * of the s_j equation in smoothing factor はどう決めるのか]:
+ *   a[j] = max(accumulate ? a[j] : 0, max_t |x[t, j]|)
+ * x: [T x K] of dtype xdt (F32, F16, BF16).  a: fp32 [K], read (accumulate
+ * != 0) and written.  Call once per calibration batch with accumulate = 1
+ * after the first to keep a running maximum over batches. */
+sq_status sq_calibrate_absmax(const void* x, sq_dtype xdt, int64_t T, int64_t K,
+                              float* a, int accumulate, void* stream);
+
+/* Smoothing factor and offline fold [P1 smoothing factor はどう決めるのか:
+ * s_j = max(|X_j|)^alpha / max(|W_j|)^(1-alpha); 数学的に何をしているのか:
+ * Y = (X diag(s)^-1)(diag(s) W), diag(s) folded into W and diag(s)^-1 into
+ * the preceding LayerNorm]:
+ *   b_j     = max_n |w[j, n]|               (row j multiplies input channel j)
+ *   s_out[j] = (float)(pow(a_j, alpha) / pow(b_j, 1 - alpha)) in double;
+ *             1.0f when a_j == 0 or b_j == 0 (the channel adds nothing to Y)
+ *   w_out[j, n] = s_j * w[j, n]             (one fp32 multiply)
+ *   gamma[j] /= s_j, beta[j] /= s_j         (fp32 division; in place)
+ * a: fp32 [K].  w: [K x N] of dtype wdt (F32, F16, BF16).  alpha in [0, 1]
+ * (a double, used as given: both pow calls take exactly this value).
+ * s_out: fp32 [K].  w_out: fp32 [K x N].  gamma, beta: fp32 [K] or NULL.
+ * s is evaluated with the device's double pow; it may differ from another
+ * libm's result by one fp32 ulp when the two double results straddle an fp32
+ * rounding boundary. */
+sq_status sq_smooth_fold(const float* a, const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                         double alpha, float* s_out, float* w_out, float* gamma, float* beta,
+                         void* stream);
+
+/* Per-output-channel weight quantisation (each column n of w gets its own
+ * step; P1 推論方法 names per-tensor weights for O1, the special case of a
+ * constant step vector):
+ *   w_scale[n] = max_j |w[j, n]| / 127;   wq[n, j] = code(w[j, n], w_scale[n])
+ * w: [K x N] of dtype wdt (F32, F16, BF16), normally the folded W_hat.
+ * wq: int8 [N x K] (output channel n's K codes contiguous -- the transpose of
+ * w's layout).  w_scale: fp32 [N]. */
+sq_status sq_quant_weight_perchannel(const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                                     int8_t* wq, float* w_scale, void* stream);
+
+/* ---------------------------------------------------------------- runtime */
+
+/* Per-token dynamic activation quantisation [P1 推論方法, O1: activations per
+ * token, dynamic]:
+ *   v[m, k]    = smooth ? fp32(x[m, k]) / smooth[k] : fp32(x[m, k])
+ *   x_scale[m] = max_k |v[m, k]| / 127;   xq[m, k] = code(v[m, k], x_scale[m])
+ * x: [M x K] of dtype xdt (F32, F16, BF16), normally X_hat as the folded
+ * LayerNorm emits it.  smooth: fp32 [K] or NULL (NULL: x is already
+ * smoothed).  xq: int8 [M x K].  x_scale: fp32 [M]. */
+sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                const float* smooth, int8_t* xq, float* x_scale, void* stream);
+
+/* INT8 GEMM with fused scale back [P1 用語解説 "INT8 GEMM", 推論方法;
+ * P4 section 3: multiply the scale factor back]:
+ *   acc[m, n] = sum_k xq[m, k] * wq[n, k]              (exact int32)
+ *   y[m, n]   = ydt( (fp32(acc) * x_scale[m]) * w_scale[n] )
+ * two fp32 multiplies in that order, then round-to-nearest-even to ydt.
+ * xq: int8 [M x K].  x_scale: fp32 [M].  wq: int8 [N x K].  w_scale: fp32 [N].
+ * y: [M x N] of dtype ydt (F16, BF16, F32).  K <= SQ_MAX_K. */
+sq_status sq_w8a8_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K,
+                               void* y, sq_dtype ydt, void* stream);
+
+/* ------------------------------------------------------------- auxiliary */
+
+/* The INT8 GEMM's raw accumulators, for exact checking of the GEMM kernels:
+ *   acc[m, n] = sum_k xq[m, k] * wq[n, k]   (int32 [M x N]).
+ * Uses the same kernels and tiling that sq_w8a8_gemm_dequant selects for
+ * (M, N, K). */
+sq_status sq_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                           int32_t* acc, void* stream);
+
+/* X diag(s)^-1 at run time, for inputs whose LayerNorm was not folded [P1
+ * 数学的に何をしているのか]:  x_hat[m, k] = dt(fp32(x[m, k]) / s[k]), rounded to
+ * nearest even when dt is 16-bit.  x, x_hat: [M x K] of dtype dt.  s: fp32 [K]. */
+sq_status sq_smooth_activation(const void* x, sq_dtype dt, int64_t M, int64_t K,
+                               const float* s, void* x_hat, void* stream);
+
+/* Library version string (static storage). */
+const char* sq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

@@ -1,0 +1,93 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/sq.h, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_post_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(sq_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(sq.LIB_PATH)
+    names = _declared()
+    assert {"sq_calibrate_absmax", "sq_smooth_fold", "sq_quant_weight_perchannel",
+            "sq_quant_act_pertoken", "sq_w8a8_gemm_dequant"} <= names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_version():
+    assert "gfx950" in sq.version()
+
+
+A = 4096  # a 16-byte aligned fake address: validation never dereferences
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sq.load_library()
+
+
+def test_null_pointers(lib):
+    assert lib.sq_calibrate_absmax(None, 0, 4, 4, A, 0, None) == 1
+    assert lib.sq_smooth_fold(A, A, 0, 4, 4, 0.5, None, A, None, None, None) == 1
+    assert lib.sq_quant_weight_perchannel(A, 1, 4, 4, None, A, None) == 1
+    assert lib.sq_quant_act_pertoken(A, 1, 4, 4, None, A, None, None) == 1
+    assert lib.sq_w8a8_gemm_dequant(A, A, None, A, 4, 4, 16, A, 1, None) == 1
+    assert lib.sq_w8a8_gemm_i32(A, A, 4, 4, 16, None, None) == 1
+    assert lib.sq_smooth_activation(A, 1, 4, 4, None, A, None) == 1
+
+
+@pytest.mark.parametrize("dims", [(0, 4), (4, 0), (-1, 4), (4, 4194305)])
+def test_bad_shapes(lib, dims):
+    a, b = dims
+    assert lib.sq_calibrate_absmax(A, 0, a, b, A, 0, None) == 2
+    assert lib.sq_quant_act_pertoken(A, 1, a, b, None, A, A, None) == 2
+    assert lib.sq_quant_weight_perchannel(A, 1, a, b, A, A, None) == 2
+    assert lib.sq_smooth_fold(A, A, 1, a, b, 0.5, A, A, None, None, None) == 2
+    assert lib.sq_w8a8_gemm_dequant(A, A, A, A, a, b, 16, A, 1, None) == 2
+    assert lib.sq_smooth_activation(A, 1, a, b, A, A, None) == 2
+
+
+def test_k_overflow(lib):
+    assert lib.sq_w8a8_gemm_i32(A, A, 4, 4, 133145, A, None) == 4
+    assert lib.sq_w8a8_gemm_dequant(A, A, A, A, 4, 4, 133145, A, 1, None) == 4
+    assert lib.sq_w8a8_gemm_i32(A, A, 4, 4, 0, A, None) == 2
+
+
+def test_bad_dtype(lib):
+    assert lib.sq_calibrate_absmax(A, 7, 4, 4, A, 0, None) == 3
+    assert lib.sq_quant_act_pertoken(A, -1, 4, 4, None, A, A, None) == 3
+    assert lib.sq_w8a8_gemm_dequant(A, A, A, A, 4, 4, 16, A, 3, None) == 3
+
+
+def test_misaligned(lib):
+    assert lib.sq_calibrate_absmax(A + 2, 1, 4, 4, A, 0, None) == 5
+    assert lib.sq_w8a8_gemm_i32(A, A + 8, 4, 4, 16, A, None) == 5
+    assert lib.sq_quant_act_pertoken(A, 1, 4, 4, A + 4, A, A, None) == 5
+
+
+@pytest.mark.parametrize("alpha", [-0.1, 1.5, float("nan"), float("inf")])
+def test_bad_alpha(lib, alpha):
+    assert lib.sq_smooth_fold(A, A, 0, 4, 4, alpha, A, A, None, None, None) == 6
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        sq.quant_act_pertoken(x)

@@ -1,0 +1,220 @@
+"""SmoothQuant W8A8 linear layer on AMD MI355X (gfx950).
+
+Thin Python binding of ``libsq.so`` (C ABI in ``include/sq.h``).  The
+functions below carry the C names and only marshal arguments: torch tensors
+provide device memory and the HIP stream; every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if ``libsq.so`` is not
+built, or a tensor is not on the GPU, the call raises.
+
+Method pages (title, section): abeam.tech explainer of "SmoothQuant: Accurate
+and Efficient Post-Training Quantization for Large Language Models"
+(calibration, smoothing factor, fold, O1 per-token activations, INT8 GEMM);
+blogs.itmedia.co.jp 「LLMのダイエット術、『量子化（Quantization）』」 section 3
+(range -> scale -> round, scale back).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SQError", "load_library", "version",
+    "sq_calibrate_absmax", "sq_smooth_fold", "sq_quant_weight_perchannel",
+    "sq_quant_act_pertoken", "sq_w8a8_gemm_dequant", "sq_w8a8_gemm_i32",
+    "sq_smooth_activation",
+    "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
+    "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
+
+STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE",
+          4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP"}
+SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
+_DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
+MAX_K = 133144
+
+
+class SQError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s returned %s" % (fn, STATUS.get(code, code)))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libsq.so and declare the C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsq.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, E = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sigs = {
+            "sq_calibrate_absmax": [P, E, I64, I64, P, E, P],
+            "sq_smooth_fold": [P, P, E, I64, I64, ctypes.c_double, P, P, P, P, P],
+            "sq_quant_weight_perchannel": [P, E, I64, I64, P, P, P],
+            "sq_quant_act_pertoken": [P, E, I64, I64, P, P, P, P],
+            "sq_w8a8_gemm_dequant": [P, P, P, P, I64, I64, I64, P, E, P],
+            "sq_w8a8_gemm_i32": [P, P, I64, I64, I64, P, P],
+            "sq_smooth_activation": [P, E, I64, I64, P, P, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.sq_version.argtypes = []
+        lib.sq_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return load_library().sq_version().decode()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s has dtype %s" % (name, t.dtype))
+    return t.data_ptr()
+
+
+def _opt(t, name, dtype=None):
+    return None if t is None else _dev(t, name, dtype)
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _call(name: str, *args):
+    rc = getattr(load_library(), name)(*args)
+    if rc != 0:
+        raise SQError(name, rc)
+
+
+# --------------------------------------------------------------------------
+# C entry points (same names, same argument order, tensors for pointers)
+
+def sq_calibrate_absmax(x, a, accumulate: bool = False, stream=None):
+    T, K = x.shape
+    _call("sq_calibrate_absmax", _dev(x, "x"), _DT[x.dtype], T, K, _dev(a, "a", torch.float32),
+          1 if accumulate else 0, _stream(x, stream))
+
+
+def sq_smooth_fold(a, w, alpha: float, s_out, w_out, gamma=None, beta=None, stream=None):
+    K, N = w.shape
+    _call("sq_smooth_fold", _dev(a, "a", torch.float32), _dev(w, "w"), _DT[w.dtype], K, N,
+          float(alpha), _dev(s_out, "s_out", torch.float32), _dev(w_out, "w_out", torch.float32),
+          _opt(gamma, "gamma", torch.float32), _opt(beta, "beta", torch.float32),
+          _stream(w, stream))
+
+
+def sq_quant_weight_perchannel(w, wq, w_scale, stream=None):
+    K, N = w.shape
+    _call("sq_quant_weight_perchannel", _dev(w, "w"), _DT[w.dtype], K, N,
+          _dev(wq, "wq", torch.int8), _dev(w_scale, "w_scale", torch.float32), _stream(w, stream))
+
+
+def sq_quant_act_pertoken(x, xq, x_scale, smooth=None, stream=None):
+    M, K = x.shape
+    _call("sq_quant_act_pertoken", _dev(x, "x"), _DT[x.dtype], M, K,
+          _opt(smooth, "smooth", torch.float32), _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _stream(x, stream))
+
+
+def sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream=None):
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _call("sq_w8a8_gemm_dequant", _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32),
+          _dev(wq, "wq", torch.int8), _dev(w_scale, "w_scale", torch.float32), M, N, K,
+          _dev(y, "y"), _DT[y.dtype], _stream(xq, stream))
+
+
+def sq_w8a8_gemm_i32(xq, wq, acc, stream=None):
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(acc.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _call("sq_w8a8_gemm_i32", _dev(xq, "xq", torch.int8), _dev(wq, "wq", torch.int8), M, N, K,
+          _dev(acc, "acc", torch.int32), _stream(xq, stream))
+
+
+def sq_smooth_activation(x, s, x_hat, stream=None):
+    M, K = x.shape
+    if x_hat.dtype != x.dtype or x_hat.shape != x.shape:
+        raise ValueError("x_hat must match x")
+    _call("sq_smooth_activation", _dev(x, "x"), _DT[x.dtype], M, K, _dev(s, "s", torch.float32),
+          _dev(x_hat, "x_hat"), _stream(x, stream))
+
+
+# --------------------------------------------------------------------------
+# Allocating conveniences (outputs from torch.empty on the input's device)
+
+def calibrate_absmax(x, a=None, stream=None):
+    if a is None:
+        a = torch.empty(x.shape[1], dtype=torch.float32, device=x.device)
+        sq_calibrate_absmax(x, a, False, stream)
+    else:
+        sq_calibrate_absmax(x, a, True, stream)
+    return a
+
+
+def smooth_fold(a, w, alpha: float, gamma=None, beta=None, stream=None):
+    K, N = w.shape
+    s = torch.empty(K, dtype=torch.float32, device=w.device)
+    w_hat = torch.empty(K, N, dtype=torch.float32, device=w.device)
+    sq_smooth_fold(a, w, alpha, s, w_hat, gamma, beta, stream)
+    return s, w_hat
+
+
+def quant_weight_perchannel(w, stream=None):
+    K, N = w.shape
+    wq = torch.empty(N, K, dtype=torch.int8, device=w.device)
+    sw = torch.empty(N, dtype=torch.float32, device=w.device)
+    sq_quant_weight_perchannel(w, wq, sw, stream)
+    return wq, sw
+
+
+def quant_act_pertoken(x, smooth=None, stream=None):
+    M, K = x.shape
+    xq = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_quant_act_pertoken(x, xq, sx, smooth, stream)
+    return xq, sx
+
+
+def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, out_dtype=torch.float16, stream=None):
+    y = torch.empty(xq.shape[0], wq.shape[0], dtype=out_dtype, device=xq.device)
+    sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream)
+    return y
+
+
+def w8a8_gemm_i32(xq, wq, stream=None):
+    acc = torch.empty(xq.shape[0], wq.shape[0], dtype=torch.int32, device=xq.device)
+    sq_w8a8_gemm_i32(xq, wq, acc, stream)
+    return acc
+
+
+def smooth_activation(x, s, stream=None):
+    out = torch.empty_like(x)
+    sq_smooth_activation(x, s, out, stream)
+    return out
+
+
+def linear_w8a8(x_hat, wq, w_scale, out_dtype=torch.float16, stream=None):
+    """Run-time layer: per-token quantisation then INT8 GEMM + scale back."""
+    xq, sx = quant_act_pertoken(x_hat, None, stream)
+    return w8a8_gemm_dequant(xq, sx, wq, w_scale, out_dtype, stream)

@@ -1,0 +1,203 @@
+// sq_act.hip -- per-token dynamic activation quantisation on gfx950.
+//
+// P1 = abeam.tech explainer of "SmoothQuant: Accurate and Efficient
+// Post-Training Quantization for Large Language Models", section 推論方法
+// (O1: activations quantised per token, dynamically) and section
+// 数学的に何をしているのか (X diag(s)^-1 when the scale is not folded).
+//
+// One workgroup per token row.  Each thread keeps its slice of the row in
+// registers between the absmax reduction and the quantisation, so the row is
+// read from HBM once; loads are 16 bytes per lane and consecutive lanes read
+// consecutive 16-byte pieces of the row.  Rows longer than the register
+// budget take a two-pass variant (the second pass re-reads the row).
+#include "sq_device.h"
+#include "sq_launch.h"
+
+namespace sq {
+namespace {
+
+template <class D, bool SMOOTH>
+__device__ inline void load_smoothed(const typename D::T* p, const float* smooth, int64_t k,
+                                     float (&v)[D::VEC]) {
+    load_vec<D>(p, v);
+    if constexpr (SMOOTH) {
+#pragma unroll
+        for (int e = 0; e < D::VEC; e += 4) {
+            const float4 s4 = *reinterpret_cast<const float4*>(smooth + k + e);
+            v[e] = v[e] / s4.x;
+            v[e + 1] = v[e + 1] / s4.y;
+            v[e + 2] = v[e + 2] / s4.z;
+            v[e + 3] = v[e + 3] / s4.w;
+        }
+    }
+}
+
+template <int V>
+__device__ inline void store_codes(int8_t* dst, const float (&v)[V], float step) {
+    if constexpr (V == 8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lo |= (uint32_t)(uint8_t)quant_code(v[e], step) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code(v[4 + e], step) << (8 * e);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code(v[e], step) << (8 * e);
+        *reinterpret_cast<uint32_t*>(dst) = w;
+    }
+}
+
+// Register-resident variant: K / VEC <= NT * NCH.
+template <class D, int NT, int NCH, bool SMOOTH>
+__global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* __restrict__ x,
+                                                           const float* __restrict__ smooth,
+                                                           int64_t K, int8_t* __restrict__ xq,
+                                                           float* __restrict__ sx) {
+    constexpr int V = D::VEC;
+    __shared__ float red[NT / 64];
+    const int64_t m = blockIdx.x;
+    const typename D::T* row = x + m * K;
+    const int64_t nch = K / V;
+    float v[NCH][V];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t ci = (int64_t)c * NT + threadIdx.x;
+        if (ci < nch) {
+            load_smoothed<D, SMOOTH>(row + ci * V, smooth, ci * V, v[c]);
+#pragma unroll
+            for (int e = 0; e < V; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][e]));
+        }
+    }
+    amax = block_max<NT>(amax, red);
+    const float step = quant_step(amax);
+    if (threadIdx.x == 0) sx[m] = step;
+    int8_t* qrow = xq + m * K;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t ci = (int64_t)c * NT + threadIdx.x;
+        if (ci < nch) store_codes<V>(qrow + ci * V, v[c], step);
+    }
+}
+
+// Two-pass variant for any K (element-wise when K is not a multiple of VEC).
+template <class D, int NT, bool SMOOTH>
+__global__ __launch_bounds__(NT) void act_quant_2pass_kernel(const typename D::T* __restrict__ x,
+                                                             const float* __restrict__ smooth,
+                                                             int64_t K, int8_t* __restrict__ xq,
+                                                             float* __restrict__ sx) {
+    __shared__ float red[NT / 64];
+    const int64_t m = blockIdx.x;
+    const typename D::T* row = x + m * K;
+    float amax = 0.0f;
+    for (int64_t k = threadIdx.x; k < K; k += NT) {
+        float v = D::to_f32(row[k]);
+        if constexpr (SMOOTH) v = v / smooth[k];
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(v));
+    }
+    amax = block_max<NT>(amax, red);
+    const float step = quant_step(amax);
+    if (threadIdx.x == 0) sx[m] = step;
+    int8_t* qrow = xq + m * K;
+    for (int64_t k = threadIdx.x; k < K; k += NT) {
+        float v = D::to_f32(row[k]);
+        if constexpr (SMOOTH) v = v / smooth[k];
+        qrow[k] = (int8_t)quant_code(v, step);
+    }
+}
+
+template <class D, bool SMOOTH>
+hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* smooth, int8_t* xq,
+                           float* sx, hipStream_t s) {
+    const typename D::T* x = static_cast<const typename D::T*>(xv);
+    const dim3 grid((unsigned)M);
+    const int64_t nch = K / D::VEC;
+    if (K % D::VEC == 0 && nch <= 256 * 4) {
+        hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, SMOOTH>), grid, dim3(256), 0, s, x,
+                           smooth, K, xq, sx);
+    } else if (K % D::VEC == 0 && nch <= 512 * 12) {
+        hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 12, SMOOTH>), grid, dim3(512), 0, s, x,
+                           smooth, K, xq, sx);
+    } else {
+        hipLaunchKernelGGL((act_quant_2pass_kernel<D, 512, SMOOTH>), grid, dim3(512), 0, s, x,
+                           smooth, K, xq, sx);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// x_hat = dt(fp32(x) / s[k]), element-wise with 16-byte accesses.
+template <class D, bool VECT>
+__global__ __launch_bounds__(256) void smooth_act_kernel(const typename D::T* __restrict__ x,
+                                                         const float* __restrict__ smooth,
+                                                         int64_t M, int64_t K,
+                                                         typename D::T* __restrict__ out) {
+    constexpr int V = VECT ? D::VEC : 1;
+    const int64_t total = M * K / V;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t e0 = i * V;
+        const int64_t k = e0 % K;
+        if constexpr (VECT) {
+            float v[V];
+            load_smoothed<D, true>(x + e0, smooth, k, v);
+            typename D::T o[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = D::from_f32(v[e]);
+            *reinterpret_cast<uint4*>(out + e0) = *reinterpret_cast<const uint4*>(o);
+        } else {
+            out[e0] = D::from_f32(D::to_f32(x[e0]) / smooth[k]);
+        }
+    }
+}
+
+template <class D>
+hipError_t smooth_act_typed(const void* xv, int64_t M, int64_t K, const float* smooth, void* ov,
+                            hipStream_t s) {
+    const typename D::T* x = static_cast<const typename D::T*>(xv);
+    typename D::T* o = static_cast<typename D::T*>(ov);
+    const bool vect = K % D::VEC == 0;
+    const int64_t items = vect ? M * K / D::VEC : M * K;
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (vect)
+        hipLaunchKernelGGL((smooth_act_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, x,
+                           smooth, M, K, o);
+    else
+        hipLaunchKernelGGL((smooth_act_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           x, smooth, M, K, o);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
+                            int8_t* xq, float* x_scale, hipStream_t s) {
+    const bool sm = smooth != nullptr;
+    switch (dt) {
+        case Dt::F32:
+            return sm ? act_quant_typed<F32, true>(x, M, K, smooth, xq, x_scale, s)
+                      : act_quant_typed<F32, false>(x, M, K, smooth, xq, x_scale, s);
+        case Dt::F16:
+            return sm ? act_quant_typed<F16, true>(x, M, K, smooth, xq, x_scale, s)
+                      : act_quant_typed<F16, false>(x, M, K, smooth, xq, x_scale, s);
+        case Dt::BF16:
+            return sm ? act_quant_typed<BF16, true>(x, M, K, smooth, xq, x_scale, s)
+                      : act_quant_typed<BF16, false>(x, M, K, smooth, xq, x_scale, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
+                             void* x_hat, hipStream_t s) {
+    switch (dt) {
+        case Dt::F32: return smooth_act_typed<F32>(x, M, K, smooth, x_hat, s);
+        case Dt::F16: return smooth_act_typed<F16>(x, M, K, smooth, x_hat, s);
+        case Dt::BF16: return smooth_act_typed<BF16>(x, M, K, smooth, x_hat, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sq

@@ -1,0 +1,108 @@
+// sq_api.hip -- the library's extern "C" entry points (declared in include/sq.h).
+//
+// Each entry point validates its arguments on the host, before any HIP call,
+// then enqueues its kernels on the caller's stream and returns.  No device
+// memory is allocated and no state is kept between calls.
+#include "sq.h"
+#include "sq_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = SQ_MAX_DIM;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dt_ok(sq_dtype d) { return d == SQ_F32 || d == SQ_F16 || d == SQ_BF16; }
+
+sq::Dt to_dt(sq_dtype d) { return static_cast<sq::Dt>(static_cast<int>(d)); }
+
+bool dims_ok(int64_t a, int64_t b) { return a >= 1 && b >= 1 && a <= kMaxDim && b <= kMaxDim; }
+
+sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_version(void) { return "sq-mi355x 0.1 (gfx950)"; }
+
+sq_status sq_calibrate_absmax(const void* x, sq_dtype xdt, int64_t T, int64_t K, float* a,
+                              int accumulate, void* stream) {
+    if (!x || !a) return SQ_ERR_NULL;
+    if (!dims_ok(T, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(xdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(a)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_colmax(x, to_dt(xdt), T, K, a, accumulate == 0, as_stream(stream)));
+}
+
+sq_status sq_smooth_fold(const float* a, const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                         double alpha, float* s_out, float* w_out, float* gamma, float* beta,
+                         void* stream) {
+    if (!a || !w || !s_out || !w_out) return SQ_ERR_NULL;
+    if (!dims_ok(K, N)) return SQ_ERR_SHAPE;
+    if (!dt_ok(wdt)) return SQ_ERR_DTYPE;
+    if (!(alpha >= 0.0 && alpha <= 1.0)) return SQ_ERR_ALPHA;  // also rejects NaN
+    if (!aligned16(a) || !aligned16(w) || !aligned16(s_out) || !aligned16(w_out) ||
+        (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+        return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_smooth_fold(a, w, to_dt(wdt), K, N, alpha, s_out, w_out, gamma,
+                                             beta, as_stream(stream)));
+}
+
+sq_status sq_quant_weight_perchannel(const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                                     int8_t* wq, float* w_scale, void* stream) {
+    if (!w || !wq || !w_scale) return SQ_ERR_NULL;
+    if (!dims_ok(K, N)) return SQ_ERR_SHAPE;
+    if (!dt_ok(wdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_quant_weight(w, to_dt(wdt), K, N, wq, w_scale, as_stream(stream)));
+}
+
+sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                const float* smooth, int8_t* xq, float* x_scale, void* stream) {
+    if (!x || !xq || !x_scale) return SQ_ERR_NULL;
+    if (!dims_ok(M, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(xdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || (smooth && !aligned16(smooth)))
+        return SQ_ERR_ALIGN;
+    return hip_status(
+        sq::launch_act_quant(x, to_dt(xdt), M, K, smooth, xq, x_scale, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                               sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(
+        sq::launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y, out, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
+                           int32_t* acc, void* stream) {
+    if (!xq || !wq || !acc) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(acc)) return SQ_ERR_ALIGN;
+    return hip_status(
+        sq::launch_gemm(xq, nullptr, wq, nullptr, M, N, K, acc, sq::Out::I32, as_stream(stream)));
+}
+
+sq_status sq_smooth_activation(const void* x, sq_dtype dt, int64_t M, int64_t K, const float* s,
+                               void* x_hat, void* stream) {
+    if (!x || !s || !x_hat) return SQ_ERR_NULL;
+    if (!dims_ok(M, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(dt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(s) || !aligned16(x_hat)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_smooth_act(x, to_dt(dt), M, K, s, x_hat, as_stream(stream)));
+}
+
+}  // extern "C"

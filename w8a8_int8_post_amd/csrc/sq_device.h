@@ -1,0 +1,93 @@
+// sq_device.h -- device helpers shared by the library's HIP kernels (gfx950).
+//
+// Element types, 16-byte vector loads, the symmetric 8-bit quantiser and
+// wavefront/workgroup max reductions.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- dtypes
+
+struct F32 {
+    typedef float T;
+    static constexpr int VEC = 4;  // elements per 16 bytes
+    __device__ static float to_f32(T v) { return v; }
+    __device__ static T from_f32(float f) { return f; }
+};
+
+struct F16 {
+    typedef _Float16 T;
+    static constexpr int VEC = 8;
+    __device__ static float to_f32(T v) { return (float)v; }         // exact
+    __device__ static T from_f32(float f) { return (_Float16)f; }    // round to nearest even
+};
+
+struct BF16 {
+    typedef uint16_t T;  // raw bits
+    static constexpr int VEC = 8;
+    __device__ static float to_f32(T v) { return __uint_as_float((uint32_t)v << 16); }  // exact
+    // Round to nearest, ties to even, on the bit pattern (finite inputs).
+    __device__ static T from_f32(float f) {
+        uint32_t u = __float_as_uint(f);
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        return (T)(u >> 16);
+    }
+};
+
+// Load VEC consecutive elements (16 bytes, 16-byte aligned) widened to fp32.
+template <class D>
+__device__ inline void load_vec(const typename D::T* p, float (&out)[D::VEC]) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const typename D::T* e = reinterpret_cast<const typename D::T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < D::VEC; ++i) out[i] = D::to_f32(e[i]);
+}
+
+// ------------------------------------------------------------- quantiser
+// step = absmax / 127 (fp32 IEEE division); code = clamp(round half away
+// from zero (v / step), -127, 127); a zero step gives code 0.
+__device__ inline float quant_step(float absmax) { return absmax / 127.0f; }
+
+__device__ inline int quant_code(float v, float step) {
+    if (step == 0.0f) return 0;
+    float r = __builtin_roundf(v / step);
+    r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// ------------------------------------------------------------ reductions
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Max over the workgroup; every thread gets the result.  `red` holds one
+// float per wave.  Contains __syncthreads().
+template <int NT>
+__device__ inline float block_max(float v, float* red) {
+    constexpr int NW = NT / 64;
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = __builtin_fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+}
+
+// Non-negative floats order like their bit patterns as unsigned integers, so
+// an unsigned atomic max is an exact, order-independent float max for them.
+__device__ inline void atomic_max_nonneg(float* addr, float v) {
+    atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace sq

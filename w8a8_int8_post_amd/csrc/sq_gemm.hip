@@ -1,0 +1,321 @@
+// sq_gemm.hip -- INT8 x INT8 -> INT32 GEMM with fused scale back, gfx950.
+//
+// P1 = abeam.tech explainer of "SmoothQuant: Accurate and Efficient
+// Post-Training Quantization for Large Language Models": 用語解説 "INT8 GEMM"
+// and 推論方法 (the heavy linear layers run as INT8 GEMMs after the offline
+// transform).  P4 = blogs.itmedia.co.jp 量子化 blog, section 3 (multiply the
+// scale factor back at inference).
+//
+//   acc[m, n] = sum_k xq[m, k] * wq[n, k]          (exact int32)
+//   y[m, n]   = out( (fp32(acc) * x_scale[m]) * w_scale[n] )
+//
+// Both operands are K-contiguous ("TN"), the natural feed of the MFMA
+// matrix cores: every lane's 16-byte fragment is one contiguous load.
+//
+// Two kernels, chosen by M alone:
+//  * tiled (M > 64): workgroup tile BM x BN, K staged through LDS in BK-byte
+//    slices (double-buffered, XOR-swizzled 16-byte chunks against bank
+//    conflicts), v_mfma_i32_32x32x32_i8 on 32 x 32 sub-tiles, XCD-aware tile
+//    order so that tiles sharing operand panels run on the same XCD's L2.
+//  * skinny (M <= 64, the decode regime): the weight matrix is streamed once
+//    from HBM straight into MFMA fragments (no LDS staging); one workgroup
+//    per 16 output channels, its waves interleave over K in 256-byte steps,
+//    v_mfma_i32_16x16x64_i8 with the weights as the 16-row operand and up to
+//    four 16-token blocks of activations as the other; the waves' partial
+//    sums are added in LDS before the epilogue.
+//
+// The MFMA sums over K inside one instruction in whatever order the hardware
+// takes; the A and B fragments give each lane the same K positions, so any
+// order yields the same integer sum.
+#include "sq_device.h"
+#include "sq_launch.h"
+
+namespace sq {
+namespace {
+
+__device__ inline float dequant(int acc, float sxm, float swn) {
+    float f = (float)acc;  // round to nearest even
+    f = f * sxm;
+    f = f * swn;
+    return f;
+}
+
+template <Out O>
+__device__ inline void store_out(void* y, int64_t idx, int acc, float sxm, float swn) {
+    if constexpr (O == Out::I32) {
+        static_cast<int*>(y)[idx] = acc;
+    } else if constexpr (O == Out::F32) {
+        static_cast<float*>(y)[idx] = dequant(acc, sxm, swn);
+    } else if constexpr (O == Out::F16) {
+        static_cast<_Float16*>(y)[idx] = (_Float16)dequant(acc, sxm, swn);
+    } else {
+        static_cast<uint16_t*>(y)[idx] = BF16::from_f32(dequant(acc, sxm, swn));
+    }
+}
+
+// 16 bytes of row r starting at column k of a row-major [R x K] int8 matrix;
+// zero outside the matrix.  KVEC: K % 16 == 0, so a chunk is wholly inside or
+// wholly outside and is one aligned 16-byte load.
+template <bool KVEC>
+__device__ inline v4i load_chunk(const int8_t* __restrict__ base, int r, int R, int k, int K) {
+    v4i z = {0, 0, 0, 0};
+    if (r >= R || k >= K) return z;
+    const int8_t* p = base + (int64_t)r * K + k;
+    if constexpr (KVEC) {
+        return *reinterpret_cast<const v4i*>(p);
+    } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < 16; ++b)
+            if (k + b < K) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
+        v4i v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        return v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel.
+template <int BM, int BN, int BK, int WM, int WN, int SWS, Out O, bool KVEC>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_tiled_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    constexpr int WAVES_N = BN / WN;
+    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int CPR = BK / 16;  // 16-byte chunks per tile row
+    constexpr int A_PER_T = BM * CPR / NT;
+    constexpr int B_PER_T = BN * CPR / NT;
+    static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
+    static_assert(BK % 32 == 0, "BK must be a multiple of the MFMA K (32)");
+    constexpr int STAGE = (BM + BN) * BK;
+    __shared__ __attribute__((aligned(16))) int8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+
+    // Workgroup -> tile.  Hardware places workgroup b on XCD b % 8; give each
+    // XCD a contiguous range of the logical order, and walk the logical order
+    // in groups of GM tile rows so that concurrently running tiles share A
+    // rows and B columns.
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+    const int total = nbm * nbn;
+    const int bid = blockIdx.x;
+    const int q = total >> 3, rr = total & 7, xcd = bid & 7, idx = bid >> 3;
+    const int logical = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + idx;
+    constexpr int GM = 8;
+    const int group_size = GM * nbn;
+    const int group = logical / group_size;
+    const int first_m = group * GM;
+    const int gsz = (nbm - first_m) < GM ? (nbm - first_m) : GM;
+    const int in_group = logical - group * group_size;
+    const int m0 = (first_m + in_group % gsz) * BM;
+    const int n0 = (in_group / gsz) * BN;
+
+    v4i ra[A_PER_T], rb[B_PER_T];
+
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int c = tid + i * NT;
+            ra[i] = load_chunk<KVEC>(A, m0 + c / CPR, M, k0 + (c % CPR) * 16, K);
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int c = tid + i * NT;
+            rb[i] = load_chunk<KVEC>(B, n0 + c / CPR, N, k0 + (c % CPR) * 16, K);
+        }
+    };
+    auto lds_off = [](int row, int chunk) {
+        return row * BK + ((chunk ^ ((row >> SWS) & (CPR - 1))) << 4);
+    };
+    auto sstore = [&](int buf) {
+        int8_t* sA = smem + buf * STAGE;
+        int8_t* sB = sA + BM * BK;
+#pragma unroll
+        for (int i = 0; i < A_PER_T; ++i) {
+            const int c = tid + i * NT;
+            *reinterpret_cast<v4i*>(sA + lds_off(c / CPR, c % CPR)) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_PER_T; ++i) {
+            const int c = tid + i * NT;
+            *reinterpret_cast<v4i*>(sB + lds_off(c / CPR, c % CPR)) = rb[i];
+        }
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int nk = (K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+        const int8_t* sA = smem + cur * STAGE;
+        const int8_t* sB = sA + BM * BK;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            const int chunk = s * 2 + (lane >> 5);
+            v4i af[TM], bf[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm0 + i * 32 + (lane & 31);
+                af[i] = *reinterpret_cast<const v4i*>(sA + lds_off(row, chunk));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn0 + j * 32 + (lane & 31);
+                bf[j] = *reinterpret_cast<const v4i*>(sB + lds_off(row, chunk));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue.  32 x 32 accumulator layout: lane l, element r holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the sub-tile.
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + j * 32 + (lane & 31);
+        const bool nok = n < N;
+        const float swn = (O != Out::I32 && nok) ? sw[n] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (nok && m < M) {
+                    const float sxm = (O != Out::I32) ? sx[m] : 0.0f;
+                    store_out<O>(Y, (int64_t)m * N + n, acc[i][j][r], sxm, swn);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel (M <= 16 * TB).
+template <int TB, int NW, Out O, bool KVEC>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    constexpr int U = 2;  // 256-byte K steps in flight per wave
+    __shared__ v4i red[NW][TB][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int nsteps = (K + 255) >> 8;
+
+    v4i acc[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
+
+    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
+        v4i wf[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (st0 + u * NW) * 256;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                wf[u][t] = load_chunk<KVEC>(W, n0 + r, N, kb + t * 64 + g * 16, K);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kb = (st0 + u * NW) * 256;
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const v4i xf = load_chunk<KVEC>(X, b * 16 + r, M, kb + t * 64 + g * 16, K);
+                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc[b], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
+    __syncthreads();
+    if (threadIdx.x < TB * 64) {
+        const int b = wave;
+        v4i tot = red[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tot += red[w][b][lane];
+        // 16 x 16 accumulator layout: lane l, element q holds row 4*(l/16) + q
+        // (output channel) and column l%16 (token).
+        const int tok = b * 16 + (lane & 15);
+        if (tok < M) {
+            const float sxm = (O != Out::I32) ? sx[tok] : 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + 4 * g + qq;
+                if (n < N) {
+                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
+                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
+                }
+            }
+        }
+    }
+}
+
+template <Out O, bool KVEC>
+hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
+                         int M, int N, int K, void* y, hipStream_t s) {
+    if (M <= 64) {
+        constexpr int NW = 8;
+        const dim3 grid((unsigned)((N + 15) / 16)), block(NW * 64);
+        if (M <= 16)
+            hipLaunchKernelGGL((gemm_skinny_kernel<1, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
+                               sw, y, M, N, K);
+        else if (M <= 32)
+            hipLaunchKernelGGL((gemm_skinny_kernel<2, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
+                               sw, y, M, N, K);
+        else if (M <= 48)
+            hipLaunchKernelGGL((gemm_skinny_kernel<3, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
+                               sw, y, M, N, K);
+        else
+            hipLaunchKernelGGL((gemm_skinny_kernel<4, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
+                               sw, y, M, N, K);
+    } else {
+        constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, SWS = 1;
+        const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, BK, WM, WN, SWS, O, KVEC>), dim3(tiles),
+                           dim3((BM / WM) * (BN / WN) * 64), 0, s, xq, wq, sx, sw, y, M, N, K);
+    }
+    return hipGetLastError();
+}
+
+template <Out O>
+hipError_t gemm_out(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M,
+                    int N, int K, void* y, hipStream_t s) {
+    if (K % 16 == 0) return gemm_dispatch<O, true>(xq, sx, wq, sw, M, N, K, y, s);
+    return gemm_dispatch<O, false>(xq, sx, wq, sw, M, N, K, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                       const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
+                       hipStream_t s) {
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (out) {
+        case Out::I32: return gemm_out<Out::I32>(xq, x_scale, wq, w_scale, m, n, k, y, s);
+        case Out::F16: return gemm_out<Out::F16>(xq, x_scale, wq, w_scale, m, n, k, y, s);
+        case Out::BF16: return gemm_out<Out::BF16>(xq, x_scale, wq, w_scale, m, n, k, y, s);
+        case Out::F32: return gemm_out<Out::F32>(xq, x_scale, wq, w_scale, m, n, k, y, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sq

@@ -1,0 +1,29 @@
+// sq_launch.h -- host-side launchers of the library's kernels (internal).
+// Each enqueues its kernels on `s` and returns the launch status; argument
+// validation happens in sq_api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
+enum class Out : int { I32 = 0, F16 = 1, BF16 = 2, F32 = 3 };
+
+hipError_t launch_colmax(const void* x, Dt dt, int64_t R, int64_t C, float* out, bool zero_first,
+                         hipStream_t s);
+hipError_t launch_smooth_fold(const float* a, const void* w, Dt dt, int64_t K, int64_t N,
+                              double alpha, float* s_out, float* w_out, float* gamma, float* beta,
+                              hipStream_t s);
+hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
+                               float* w_scale, hipStream_t s);
+hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
+                            int8_t* xq, float* x_scale, hipStream_t s);
+hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
+                             void* x_hat, hipStream_t s);
+hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                       const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
+                       hipStream_t s);
+
+}  // namespace sq

@@ -1,0 +1,279 @@
+// sq_offline.hip -- offline steps of the SmoothQuant transform on gfx950.
+//
+// Pages (title, section):
+//   P1 = abeam.tech explainer of "SmoothQuant: Accurate and Efficient
+//        Post-Training Quantization for Large Language Models".
+//
+//   * column absmax   : calibration statistic max_t |X[t, j]| (P1 用語解説
+//                       "Calibration", 学習方法) and the per-output-channel
+//                       weight range max_j |W_hat[j, n]|;
+//   * smooth + fold   : s_j = max|X_j|^alpha / max|W_j|^(1-alpha) (P1
+//                       smoothing factor はどう決めるのか) and diag(s) W,
+//                       gamma/s, beta/s (P1 数学的に何をしているのか);
+//   * weight quantise : per-output-channel step, codes transposed to [N x K].
+//
+// All of these stream their input once or twice from HBM; the layouts keep
+// every global access coalesced along the contiguous axis.
+#include "sq_device.h"
+#include "sq_launch.h"
+
+namespace sq {
+namespace {
+
+constexpr int kColThreads = 256;
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// out[c] = max(out[c], max_{r in this block's rows} |x[r, c]|) via atomic max.
+// Vector path: each thread owns VEC consecutive columns (one 16-byte load per
+// row); consecutive threads own consecutive 16-byte pieces of a row.
+template <class D, bool VECT>
+__global__ __launch_bounds__(kColThreads) void colmax_kernel(const typename D::T* __restrict__ x,
+                                                             int64_t R, int64_t C,
+                                                             int64_t rows_per_block,
+                                                             float* __restrict__ out) {
+    constexpr int V = VECT ? D::VEC : 1;
+    const int64_t c0 = ((int64_t)blockIdx.x * kColThreads + threadIdx.x) * V;
+    if (c0 >= C) return;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < R ? r0 + rows_per_block : R;
+    float m[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) m[i] = 0.0f;
+    if constexpr (VECT) {
+        int64_t r = r0;
+        for (; r + 4 <= r1; r += 4) {
+            float v[4][V];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) load_vec<D>(x + (r + u) * C + c0, v[u]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < V; ++i) m[i] = __builtin_fmaxf(m[i], __builtin_fabsf(v[u][i]));
+        }
+        for (; r < r1; ++r) {
+            float v[V];
+            load_vec<D>(x + r * C + c0, v);
+#pragma unroll
+            for (int i = 0; i < V; ++i) m[i] = __builtin_fmaxf(m[i], __builtin_fabsf(v[i]));
+        }
+    } else {
+        for (int64_t r = r0; r < r1; ++r)
+            m[0] = __builtin_fmaxf(m[0], __builtin_fabsf(D::to_f32(x[r * C + c0])));
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) atomic_max_nonneg(out + c0 + i, m[i]);
+}
+
+template <class D>
+hipError_t colmax_typed(const void* xv, int64_t R, int64_t C, float* out, hipStream_t s) {
+    const typename D::T* x = static_cast<const typename D::T*>(xv);
+    const bool vect = (C % D::VEC) == 0;
+    const int64_t per_thread = vect ? D::VEC : 1;
+    const int64_t col_blocks = (C + kColThreads * per_thread - 1) / (kColThreads * per_thread);
+    // Split rows so that the grid has a few thousand workgroups.
+    int64_t splits = (4096 + col_blocks - 1) / col_blocks;
+    if (splits > R) splits = R;
+    if (splits > 65535) splits = 65535;
+    if (splits < 1) splits = 1;
+    const int64_t rows_per_block = (R + splits - 1) / splits;
+    splits = (R + rows_per_block - 1) / rows_per_block;
+    dim3 grid((unsigned)col_blocks, (unsigned)splits);
+    if (vect)
+        hipLaunchKernelGGL((colmax_kernel<D, true>), grid, dim3(kColThreads), 0, s, x, R, C,
+                           rows_per_block, out);
+    else
+        hipLaunchKernelGGL((colmax_kernel<D, false>), grid, dim3(kColThreads), 0, s, x, R, C,
+                           rows_per_block, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per row j of W [K x N]:
+//   b_j = max_n |w[j, n]|;  s_j = pow(a_j, alpha) / pow(b_j, 1 - alpha) in
+//   double, rounded once to fp32 (1 for an all-zero channel);
+//   w_out[j, :] = s_j * w[j, :];  gamma_j /= s_j;  beta_j /= s_j.
+constexpr int kFoldThreads = 256;
+
+template <class D, bool VECT>
+__global__ __launch_bounds__(kFoldThreads) void smooth_fold_kernel(
+    const float* __restrict__ a, const typename D::T* __restrict__ w, int64_t N, double alpha,
+    float* __restrict__ s_out, float* __restrict__ w_out, float* __restrict__ gamma,
+    float* __restrict__ beta) {
+    __shared__ float red[kFoldThreads / 64];
+    __shared__ float s_shared;
+    const int64_t j = blockIdx.x;
+    const typename D::T* row = w + j * N;
+    float* orow = w_out + j * N;
+    constexpr int V = VECT ? D::VEC : 1;
+    const int64_t nvec = N / V;
+
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < nvec; i += kFoldThreads) {
+        if constexpr (VECT) {
+            float v[V];
+            load_vec<D>(row + i * V, v);
+#pragma unroll
+            for (int e = 0; e < V; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[e]));
+        } else {
+            m = __builtin_fmaxf(m, __builtin_fabsf(D::to_f32(row[i])));
+        }
+    }
+    const float b = block_max<kFoldThreads>(m, red);
+
+    if (threadIdx.x == 0) {
+        const float aj = a[j];
+        float sj = 1.0f;
+        if (aj != 0.0f && b != 0.0f)
+            sj = (float)(pow((double)aj, alpha) / pow((double)b, 1.0 - alpha));
+        s_out[j] = sj;
+        if (gamma) gamma[j] = gamma[j] / sj;
+        if (beta) beta[j] = beta[j] / sj;
+        s_shared = sj;
+    }
+    __syncthreads();
+    const float sj = s_shared;
+
+    for (int64_t i = threadIdx.x; i < nvec; i += kFoldThreads) {
+        if constexpr (VECT) {
+            float v[V];
+            load_vec<D>(row + i * V, v);
+#pragma unroll
+            for (int e = 0; e < V; e += 4) {
+                float4 o = make_float4(sj * v[e], sj * v[e + 1], sj * v[e + 2], sj * v[e + 3]);
+                *reinterpret_cast<float4*>(orow + i * V + e) = o;
+            }
+        } else {
+            orow[i] = sj * D::to_f32(row[i]);
+        }
+    }
+}
+
+template <class D>
+hipError_t smooth_fold_typed(const float* a, const void* wv, int64_t K, int64_t N, double alpha,
+                             float* s_out, float* w_out, float* gamma, float* beta,
+                             hipStream_t s) {
+    const typename D::T* w = static_cast<const typename D::T*>(wv);
+    if (N % D::VEC == 0)
+        hipLaunchKernelGGL((smooth_fold_kernel<D, true>), dim3((unsigned)K), dim3(kFoldThreads), 0,
+                           s, a, w, N, alpha, s_out, w_out, gamma, beta);
+    else
+        hipLaunchKernelGGL((smooth_fold_kernel<D, false>), dim3((unsigned)K), dim3(kFoldThreads),
+                           0, s, a, w, N, alpha, s_out, w_out, gamma, beta);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weight quantisation, transposing [K x N] -> [N x K] through a 64 x 64 LDS
+// tile.  `absmax[n]` holds max_j |w[j, n]| when this kernel runs; the step
+// absmax/127 is recomputed per element (the same fp32 division every time).
+constexpr int kTile = 64;
+constexpr int kTileThreads = 256;
+
+template <class D>
+__global__ __launch_bounds__(kTileThreads) void quant_transpose_kernel(
+    const typename D::T* __restrict__ w, int64_t K, int64_t N, const float* __restrict__ absmax,
+    int8_t* __restrict__ wq) {
+    __shared__ int8_t tile[kTile][kTile + 4];
+    const int64_t j0 = (int64_t)blockIdx.y * kTile;
+    const int64_t n0 = (int64_t)blockIdx.x * kTile;
+    const int t = threadIdx.x;
+    const int nn = t & (kTile - 1);
+    const float step = (n0 + nn < N) ? quant_step(absmax[n0 + nn]) : 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < kTile * kTile / kTileThreads; ++i) {
+        const int jj = (i * kTileThreads + t) >> 6;
+        int8_t q = 0;
+        if (j0 + jj < K && n0 + nn < N)
+            q = (int8_t)quant_code(D::to_f32(w[(j0 + jj) * N + n0 + nn]), step);
+        tile[nn][jj] = q;
+    }
+    __syncthreads();
+    // Write: 16 threads cover one output row n (64 bytes of j), 4 bytes each.
+    for (int i = 0; i < kTile * kTile / (4 * kTileThreads); ++i) {
+        const int idx = i * kTileThreads + t;
+        const int rn = idx >> 4;       // 0..63
+        const int cj = (idx & 15) * 4; // 0..60
+        const int64_t n = n0 + rn;
+        if (n >= N) continue;
+        const int64_t jb = j0 + cj;
+        if (jb + 4 <= K && (K % 4) == 0) {
+            uint32_t packed = (uint32_t)(uint8_t)tile[rn][cj] |
+                              ((uint32_t)(uint8_t)tile[rn][cj + 1] << 8) |
+                              ((uint32_t)(uint8_t)tile[rn][cj + 2] << 16) |
+                              ((uint32_t)(uint8_t)tile[rn][cj + 3] << 24);
+            *reinterpret_cast<uint32_t*>(wq + n * K + jb) = packed;
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (jb + e < K) wq[n * K + jb + e] = tile[rn][cj + e];
+        }
+    }
+}
+
+__global__ void absmax_to_step_kernel(float* p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = quant_step(p[i]);
+}
+
+}  // namespace
+
+hipError_t launch_colmax(const void* x, Dt dt, int64_t R, int64_t C, float* out, bool zero_first,
+                         hipStream_t s) {
+    if (zero_first) {
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, s,
+                           out, C);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    switch (dt) {
+        case Dt::F32: return colmax_typed<F32>(x, R, C, out, s);
+        case Dt::F16: return colmax_typed<F16>(x, R, C, out, s);
+        case Dt::BF16: return colmax_typed<BF16>(x, R, C, out, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_smooth_fold(const float* a, const void* w, Dt dt, int64_t K, int64_t N,
+                              double alpha, float* s_out, float* w_out, float* gamma, float* beta,
+                              hipStream_t s) {
+    switch (dt) {
+        case Dt::F32: return smooth_fold_typed<F32>(a, w, K, N, alpha, s_out, w_out, gamma, beta, s);
+        case Dt::F16: return smooth_fold_typed<F16>(a, w, K, N, alpha, s_out, w_out, gamma, beta, s);
+        case Dt::BF16:
+            return smooth_fold_typed<BF16>(a, w, K, N, alpha, s_out, w_out, gamma, beta, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class D>
+static hipError_t quant_transpose_typed(const void* wv, int64_t K, int64_t N, const float* absmax,
+                                        int8_t* wq, hipStream_t s) {
+    dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile));
+    hipLaunchKernelGGL((quant_transpose_kernel<D>), grid, dim3(kTileThreads), 0, s,
+                       static_cast<const typename D::T*>(wv), K, N, absmax, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
+                               float* w_scale, hipStream_t s) {
+    // 1) w_scale <- per-column absmax (zeroed first)
+    hipError_t e = launch_colmax(w, dt, K, N, w_scale, true, s);
+    if (e != hipSuccess) return e;
+    // 2) codes, transposed
+    switch (dt) {
+        case Dt::F32: e = quant_transpose_typed<F32>(w, K, N, w_scale, wq, s); break;
+        case Dt::F16: e = quant_transpose_typed<F16>(w, K, N, w_scale, wq, s); break;
+        case Dt::BF16: e = quant_transpose_typed<BF16>(w, K, N, w_scale, wq, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    // 3) w_scale <- absmax / 127
+    hipLaunchKernelGGL(absmax_to_step_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                       w_scale, N);
+    return hipGetLastError();
+}
+
+}  // namespace sq
