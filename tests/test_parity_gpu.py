@@ -148,8 +148,10 @@ def test_smooth_activation(ref, dev, M, K, dt):
 GEMM_SHAPES = [
     (1, 1, 16), (1, 12288, 4096), (16, 512, 512), (3, 37, 77), (17, 4099, 4096),
     (64, 1000, 2000), (48, 64, 512), (33, 200, 1040),            # skinny kernel
-    (65, 300, 1040), (300, 513, 2064), (257, 256, 4096), (70, 100, 100),
-    (1000, 1000, 1008), (512, 2048, 4096), (129, 255, 48),       # tiled kernel
+    (65, 300, 1040), (300, 513, 2064), (70, 100, 100),
+    (1000, 1000, 1008), (129, 255, 48),                          # register-staged tiles
+    (512, 2048, 4096), (257, 256, 4096), (300, 130, 128),        # 128 x 128 DMA tiles
+    (2048, 12288, 256), (2000, 12300, 128),                      # 256 x 256 DMA tiles
 ]
 
 

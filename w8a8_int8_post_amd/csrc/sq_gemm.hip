@@ -12,11 +12,17 @@
 // Both operands are K-contiguous ("TN"), the natural feed of the MFMA
 // matrix cores: every lane's 16-byte fragment is one contiguous load.
 //
-// Two kernels, chosen by M alone:
-//  * tiled (M > 64): workgroup tile BM x BN, K staged through LDS in BK-byte
-//    slices (double-buffered, XOR-swizzled 16-byte chunks against bank
-//    conflicts), v_mfma_i32_32x32x32_i8 on 32 x 32 sub-tiles, XCD-aware tile
-//    order so that tiles sharing operand panels run on the same XCD's L2.
+// Three kernels, chosen by the shape:
+//  * dma (M > 64, K % 128 == 0): workgroup tile BM x BN; 128-byte K slices go
+//    from global memory straight into LDS (global_load_lds_dwordx4, no
+//    register staging), double-buffered, as XOR-swizzled 16-byte chunks
+//    (conflict-free ds_read_b128 fragment reads); v_mfma_i32_32x32x32_i8 with
+//    the weight tile as the row operand, so each lane ends with four
+//    consecutive output channels; the scaled 16-bit tile is staged through
+//    LDS and written as coalesced 16-byte row pieces; XCD-aware tile order so
+//    that tiles sharing operand panels run on the same XCD's L2.
+//  * tiled (M > 64, other K): the same tiling with register-staged loads and
+//    byte-granular masking of the K tail.
 //  * skinny (M <= 64, the decode regime): the weight matrix is streamed once
 //    from HBM straight into MFMA fragments (no LDS staging); one workgroup
 //    per 16 output channels, its waves interleave over K in 256-byte steps,
@@ -205,6 +211,207 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_tiled_kern
 }
 
 // ---------------------------------------------------------------------------
+// DMA kernel (K % BK == 0).  Out-of-range rows of a tile are clamped to the
+// last valid row: they only feed output rows/columns that are never stored.
+template <Out O> struct Half;
+template <> struct Half<Out::F16> {
+    typedef _Float16 T;
+    __device__ static T cvt(float f) { return (_Float16)f; }
+};
+template <> struct Half<Out::BF16> {
+    typedef uint16_t T;
+    __device__ static T cvt(float f) { return BF16::from_f32(f); }
+};
+
+template <int BM, int BN, int WM, int WN, Out O>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel(
+    const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    constexpr int BK = 128, SWS = 1, GM = 8;
+    constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NT = NW * 64;
+    constexpr int TM = WM / 32, TN = WN / 32, CPR = BK / 16, S = BK / 32;
+    constexpr int A_INS = BM * CPR / NT, B_INS = BN * CPR / NT;  // 1 KB wave loads per thread
+    static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
+    constexpr int STAGE = (BM + BN) * BK;
+    constexpr bool HALF_OUT = (O == Out::F16 || O == Out::BF16);
+    constexpr int EPI_LD = BN * 2 + 16;  // staged output row pitch (bytes): padded, 16-byte aligned
+    constexpr int EPI = HALF_OUT ? BM * EPI_LD : 0;
+    constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+    __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+    const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN, total = nbm * nbn;
+    const int bid = blockIdx.x;
+    const int q = total >> 3, rr = total & 7, xcd = bid & 7, idx = bid >> 3;
+    const int logical = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + idx;
+    const int group_size = GM * nbn, group = logical / group_size, first_m = group * GM;
+    const int gsz = (nbm - first_m) < GM ? (nbm - first_m) : GM;
+    const int in_group = logical - group * group_size;
+    const int m0 = (first_m + in_group % gsz) * BM, n0 = (in_group / gsz) * BN;
+
+    auto swz = [](int row) { return (row >> SWS) & (CPR - 1); };
+    auto off = [&](int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 4); };
+    // Each wave load fills 64 consecutive 16-byte LDS slots; slot p of a
+    // stage holds row p / CPR, logical chunk (p % CPR) ^ swz(row).
+    const int8_t* asrc[A_INS];
+    const int8_t* bsrc[B_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+        const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
+        const int gm = m0 + row < M ? m0 + row : M - 1;
+        asrc[i] = A + (int64_t)gm * K + c * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
+        const int gn = n0 + row < N ? n0 + row : N - 1;
+        bsrc[i] = B + (int64_t)gn * K + c * 16;
+    }
+    auto issue = [&](int buf, int k0) {
+        int8_t* sA = smem + buf * STAGE;
+        int8_t* sB = sA + BM * BK;
+#pragma unroll
+        for (int i = 0; i < A_INS; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(asrc[i] + k0),
+                (__attribute__((address_space(3))) void*)(sA + (i * NW + wave) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + k0),
+                (__attribute__((address_space(3))) void*)(sB + (i * NW + wave) * 1024), 16, 0, 0);
+    };
+
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
+
+    const int nk = K / BK;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        // This wave's loads of tile kt have landed; after the barrier every
+        // wave's have, and every wave is done reading the other stage.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        const int8_t* sA = smem + (kt & 1) * STAGE;
+        const int8_t* sB = sA + BM * BK;
+        v4i af[2][TM], bf[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            af[0][i] = *reinterpret_cast<const v4i*>(sA + off(wm0 + i * 32 + (lane & 31), lane >> 5));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            bf[0][j] = *reinterpret_cast<const v4i*>(sB + off(wn0 + j * 32 + (lane & 31), lane >> 5));
+        if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int cb = s & 1, nb = cb ^ 1;
+            if (s + 1 < S) {
+                const int ch = (s + 1) * 2 + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    af[nb][i] = *reinterpret_cast<const v4i*>(sA + off(wm0 + i * 32 + (lane & 31), ch));
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    bf[nb][j] = *reinterpret_cast<const v4i*>(sB + off(wn0 + j * 32 + (lane & 31), ch));
+            }
+            // D = W_tile * X_tile^T: D's rows are output channels, its columns tokens.
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
+        }
+        __builtin_amdgcn_iglp_opt(0);  // interleave the LDS reads with the MFMAs
+    }
+
+    // Epilogue.  Sub-tile (j, i), lane l: token m = i*32 + l%32; elements
+    // 4g..4g+3 are output channels 8g + 4*(l/32) + 0..3.
+    if constexpr (!HALF_OUT) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm0 + i * 32 + (lane & 31);
+            if (m >= M) continue;
+            const float sxm = (O == Out::F32) ? sx[m] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) {
+                            const float swn = (O == Out::F32) ? sw[n + e] : 0.0f;
+                            store_out<O>(Y, (int64_t)m * N + n + e, acc[j][i][4 * g + e], sxm, swn);
+                        }
+                }
+        }
+    } else {
+        typedef typename Half<O>::T T;
+        float sxv[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm0 + i * 32 + (lane & 31);
+            sxv[i] = m < M ? sx[m] : 0.0f;
+        }
+        float4 swv[TN][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (n + 3 < N)
+                    swv[j][g] = *reinterpret_cast<const float4*>(sw + n);  // n % 4 == 0
+                else
+                    swv[j][g] = make_float4(n < N ? sw[n] : 0.f, n + 1 < N ? sw[n + 1] : 0.f,
+                                            n + 2 < N ? sw[n + 2] : 0.f, 0.f);
+            }
+        asm volatile("s_barrier" ::: "memory");  // all waves are done with the operand stages
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int ml = wm0 + i * 32 + (lane & 31);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+                    const float4 w4 = swv[j][g];
+                    T o[4];
+                    o[0] = Half<O>::cvt(dequant(acc[j][i][4 * g + 0], sxv[i], w4.x));
+                    o[1] = Half<O>::cvt(dequant(acc[j][i][4 * g + 1], sxv[i], w4.y));
+                    o[2] = Half<O>::cvt(dequant(acc[j][i][4 * g + 2], sxv[i], w4.z));
+                    o[3] = Half<O>::cvt(dequant(acc[j][i][4 * g + 3], sxv[i], w4.w));
+                    *reinterpret_cast<uint2*>(smem + ml * EPI_LD + nl * 2) =
+                        *reinterpret_cast<const uint2*>(o);
+                }
+        }
+        __syncthreads();
+        // Write-out: 16 bytes (8 outputs) of one row per thread per step.
+        constexpr int CH_ROW = BN / 8;
+        const bool full_n = (n0 + BN <= N) && (N % 8 == 0);
+        for (int c = tid; c < BM * CH_ROW; c += NT) {
+            const int row = c / CH_ROW, col = (c % CH_ROW) * 8;
+            const int m = m0 + row;
+            if (m >= M) continue;
+            T* y = static_cast<T*>(Y) + (int64_t)m * N + n0 + col;
+            const int8_t* src = smem + row * EPI_LD + col * 2;
+            if (full_n) {
+                *reinterpret_cast<uint4*>(y) = *reinterpret_cast<const uint4*>(src);
+            } else {
+                const T* s16 = reinterpret_cast<const T*>(src);
+                for (int e = 0; e < 8; ++e)
+                    if (n0 + col + e < N) y[e] = s16[e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny kernel (M <= 16 * TB).
 template <int TB, int NW, Out O, bool KVEC>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
@@ -287,6 +494,18 @@ hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, co
         else
             hipLaunchKernelGGL((gemm_skinny_kernel<4, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
                                sw, y, M, N, K);
+    } else if (KVEC && K % 128 == 0) {
+        // 256 x 256 tiles when there are enough of them to fill the GPU about
+        // one and a half times; otherwise 128 x 128 (two workgroups per CU).
+        const int t256 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (t256 >= 384) {
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O>), dim3(t256), dim3(512), 0, s,
+                               xq, wq, sx, sw, y, M, N, K);
+        } else {
+            const int t128 = ((M + 127) / 128) * ((N + 127) / 128);
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O>), dim3(t128), dim3(256), 0, s,
+                               xq, wq, sx, sw, y, M, N, K);
+        }
     } else {
         constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, SWS = 1;
         const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
