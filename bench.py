@@ -62,6 +62,7 @@ class Layer:
         a = sq.calibrate_absmax(xc)
         self.s, w_hat = sq.smooth_fold(a, w, ALPHA)
         self.wq, self.sw = sq.quant_weight_perchannel(w_hat)
+        self.wp = sq.pack_weight(self.wq)  # fragment-packed copy (offline re-layout)
         x = self.x_eval_host.to(dev)
         self.x_hat = sq.smooth_activation(x, self.s)   # what a folded LayerNorm emits
         torch.cuda.synchronize()
@@ -109,30 +110,38 @@ def offline_time(dev):
 
 
 class Bufs:
-    """One rotating set of run-time buffers for every layer at M tokens."""
+    """One rotating set of run-time buffers for every layer at M tokens, with
+    the weights either row-major (canonical) or fragment-packed."""
 
-    def __init__(self, layers, M, dev):
+    def __init__(self, layers, M, dev, packed):
         self.items = []
+        self.packed = packed
         for ly in layers:
             x_hat = ly.x_hat[:M].clone()
-            wq = ly.wq.clone()
+            w = (ly.wp if packed else ly.wq).clone()
             sw = ly.sw.clone()
             xq = torch.empty(M, ly.K, dtype=torch.int8, device=dev)
             sx = torch.empty(M, dtype=torch.float32, device=dev)
             y = torch.empty(M, ly.N, dtype=torch.float16, device=dev)
-            self.items.append((x_hat, wq, sw, xq, sx, y))
+            self.items.append((x_hat, w, sw, xq, sx, y, ly.N))
+
+    def _gemm(self, xq, sx, w, sw, y, N):
+        if self.packed:
+            sq.sq_w8a8_gemm_dequant_packed(xq, sx, w, sw, N, y)
+        else:
+            sq.sq_w8a8_gemm_dequant(xq, sx, w, sw, y)
 
     def step(self):
-        for (x_hat, wq, sw, xq, sx, y) in self.items:
+        for (x_hat, w, sw, xq, sx, y, N) in self.items:
             sq.sq_quant_act_pertoken(x_hat, xq, sx)
-            sq.sq_w8a8_gemm_dequant(xq, sx, wq, sw, y)
+            self._gemm(xq, sx, w, sw, y, N)
 
     def gemm_only(self):
-        for (x_hat, wq, sw, xq, sx, y) in self.items:
-            sq.sq_w8a8_gemm_dequant(xq, sx, wq, sw, y)
+        for (x_hat, w, sw, xq, sx, y, N) in self.items:
+            self._gemm(xq, sx, w, sw, y, N)
 
     def quant_only(self):
-        for (x_hat, wq, sw, xq, sx, y) in self.items:
+        for (x_hat, w, sw, xq, sx, y, N) in self.items:
             sq.sq_quant_act_pertoken(x_hat, xq, sx)
 
 
@@ -183,10 +192,12 @@ def cpu_baseline(layers, target_s=12.0):
             oracle.linear_w8a8(x[:rows], wq, sw)
         return time.perf_counter() - t0
 
-    probe_rows = 2
-    t = run(probe_rows)
-    rows = max(probe_rows, min(PREFILL_M, int(probe_rows * target_s / max(t, 1e-3))))
+    rows = 2
+    run(rows)  # warm the thread pool
     t = run(rows)
+    while t < 0.5 * target_s and rows < PREFILL_M:
+        rows = max(rows + 1, min(PREFILL_M, int(rows * target_s / max(t, 1e-3))))
+        t = run(rows)
     ops = sum(2.0 * rows * ly.N * ly.K for ly in layers)
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
@@ -229,26 +240,31 @@ def main():
     log("setting up layers", [(ly.name, ly.K, ly.N) for ly in CFG.layers])
     layers = [Layer(ly.name, dev) for ly in CFG.layers]
 
-    # ---- prefill: the headline step
+    # ---- prefill: the headline step, with row-major and with packed weights
     M = PREFILL_M
-    foot = sum(ly.N * ly.K + M * ly.K * 3 + M * ly.N * 2 for ly in layers)
-    R = 2
-    sets = [Bufs(layers, M, dev) for _ in range(R)]
-    step_graphs = [capture(b.step) for b in sets]
-    ms = time_graphs(step_graphs, args.steps, args.warmup)
     ops_step = sum(2.0 * M * ly.N * ly.K for ly in layers)
-    tops = ops_step / (ms * 1e-3) / 1e12
-    log("prefill step %.3f ms  %.1f TOPS" % (ms, tops))
-
-    # per-kernel averages on the same stream (graph of the launches alone)
-    gemm_graphs = [capture(b.gemm_only) for b in sets]
-    quant_graphs = [capture(b.quant_only) for b in sets]
-    gemm_ms = time_graphs(gemm_graphs, args.steps, args.warmup) / len(layers)
-    quant_ms = time_graphs(quant_graphs, args.steps, args.warmup) / len(layers)
-    gemm_tops = ops_step / len(layers) / (gemm_ms * 1e-3) / 1e12
     quant_bytes = sum(M * ly.K * 2 + M * ly.K + 4 * M for ly in layers) / len(layers)
-    log("gemm avg %.1f us (%.1f TOPS), quant avg %.1f us (%.0f GB/s)"
-        % (gemm_ms * 1e3, gemm_tops, quant_ms * 1e3, quant_bytes / quant_ms / 1e6))
+    res = {}
+    for packed in (False, True):
+        sets = [Bufs(layers, M, dev, packed) for _ in range(2)]
+        step_graphs = [capture(b.step) for b in sets]
+        ms = time_graphs(step_graphs, args.steps, args.warmup)
+        gemm_graphs = [capture(b.gemm_only) for b in sets]
+        gemm_ms = time_graphs(gemm_graphs, args.steps, args.warmup) / len(layers)
+        quant_graphs = [capture(b.quant_only) for b in sets]
+        quant_ms = time_graphs(quant_graphs, args.steps, args.warmup) / len(layers)
+        res[packed] = (ms, gemm_ms, quant_ms)
+        log("prefill (%s weights): step %.3f ms  %.1f TOPS; gemm avg %.1f us (%.1f TOPS); "
+            "quant avg %.1f us (%.0f GB/s)" % ("packed" if packed else "row-major", ms,
+                                               ops_step / ms / 1e9, gemm_ms * 1e3,
+                                               ops_step / len(layers) / gemm_ms / 1e9,
+                                               quant_ms * 1e3, quant_bytes / quant_ms / 1e6))
+        del sets, step_graphs, gemm_graphs, quant_graphs
+        torch.cuda.synchronize()
+    packed_best = res[True][0] < res[False][0]
+    ms, gemm_ms, quant_ms = res[packed_best]
+    tops = ops_step / (ms * 1e-3) / 1e12
+    gemm_tops = ops_step / len(layers) / (gemm_ms * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -268,12 +284,15 @@ def main():
                         "16384x4096; fp16 activations/weights/output; 2048 tokens per layer "
                         "call; 0.5% persistent outlier channels x60; alpha 0.5",
             "tokens": M,
-            "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant (3 layers)",
+            "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant%s (3 layers)"
+                    % ("_packed" if packed_best else ""),
+            "weights": "fragment-packed" if packed_best else "row-major",
+            "other_weight_layout_ms_per_step": round(res[not packed_best][0], 4),
             "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "gemm_tiled_kernel (i8 MFMA GEMM + fused scale back)",
+            "kernel": "gemm_dma_kernel (i8 MFMA GEMM + fused scale back)",
             "bound": "mfma",
             "achieved": round(gemm_tops, 2),
             "peak": PEAK_I8_TOPS,
@@ -287,34 +306,34 @@ def main():
                       "gbs": round(quant_bytes / quant_ms / 1e6, 1),
                       "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
     }
-    del sets, step_graphs, gemm_graphs, quant_graphs
-    torch.cuda.synchronize()
-
     # ---- decode shapes
     if not args.no_decode:
         dec = {}
         for Md in DECODE_M:
             foot = sum(ly.N * ly.K + Md * ly.K * 3 + Md * ly.N * 2 for ly in layers)
             R = n_sets(foot)
-            sets = [Bufs(layers, Md, dev) for _ in range(R)]
-            g_step = [capture(b.step) for b in sets]
-            g_gemm = [capture(b.gemm_only) for b in sets]
-            ms_d = time_graphs(g_step, max(args.steps, 4 * R), args.warmup)
-            ms_g = time_graphs(g_gemm, max(args.steps, 4 * R), args.warmup) / len(layers)
             nbytes = sum(ly.N * ly.K + 4 * ly.N + 2 * Md * ly.K + 2 * Md * ly.N + 4 * Md
                          for ly in layers)
-            gbs = nbytes / (ms_d * 1e-3) / 1e9
-            gemm_bytes = nbytes / len(layers)
-            gbs_g = gemm_bytes / (ms_g * 1e-3) / 1e9
-            dec["M=%d" % Md] = {
-                "us_per_step": round(ms_d * 1e3, 2), "gbs": round(gbs, 1),
-                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "buffer_sets": R,
-                "gemm_kernel": "gemm_skinny_kernel", "gemm_avg_launch_us": round(ms_g * 1e3, 2),
-                "gemm_gbs": round(gbs_g, 1), "gemm_hbm_frac": round(gbs_g / PEAK_HBM_GBS, 4)}
-            log("decode M=%d: %.2f us/step, %.0f GB/s (%.1f%% HBM); gemm %.2f us, %.0f GB/s"
-                % (Md, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS, ms_g * 1e3, gbs_g))
-            del sets, g_step, g_gemm
-            torch.cuda.synchronize()
+            entry = {"buffer_sets": R}
+            for packed in (True, False):
+                sets = [Bufs(layers, Md, dev, packed) for _ in range(R)]
+                g_step = [capture(b.step) for b in sets]
+                g_gemm = [capture(b.gemm_only) for b in sets]
+                ms_d = time_graphs(g_step, max(args.steps, 4 * R), args.warmup)
+                ms_g = time_graphs(g_gemm, max(args.steps, 4 * R), args.warmup) / len(layers)
+                gbs = nbytes / (ms_d * 1e-3) / 1e9
+                gbs_g = nbytes / len(layers) / (ms_g * 1e-3) / 1e9
+                key = "packed" if packed else "row_major"
+                entry[key] = {"us_per_step": round(ms_d * 1e3, 2), "gbs": round(gbs, 1),
+                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "gemm_avg_launch_us": round(ms_g * 1e3, 2),
+                              "gemm_gbs": round(gbs_g, 1),
+                              "gemm_hbm_frac": round(gbs_g / PEAK_HBM_GBS, 4)}
+                log("decode M=%d (%s): %.2f us/step, %.0f GB/s (%.1f%% HBM); gemm %.2f us, %.0f GB/s"
+                    % (Md, key, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS, ms_g * 1e3, gbs_g))
+                del sets, g_step, g_gemm
+                torch.cuda.synchronize()
+            dec["M=%d" % Md] = entry
         out["decode"] = dec
 
     if not args.no_offline:

@@ -143,6 +143,28 @@ sq_status sq_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_
 sq_status sq_smooth_activation(const void* x, sq_dtype dt, int64_t M, int64_t K,
                                const float* s, void* x_hat, void* stream);
 
+/* ------------------------------------------------- fragment-packed weights */
+
+/* The quantised weight in a layout the GEMM kernels read as whole contiguous
+ * kilobytes (an offline re-layout of wq, no arithmetic; the row-major wq of
+ * sq_quant_weight_perchannel stays the canonical form).  Row block b (output
+ * channels 16b .. 16b+15) and 64-byte k-group c form one 1024-byte block at
+ * byte (b * (K / 64) + c) * 1024; its 16-byte piece l holds channel
+ * 16b + l % 16, inputs 64c + 16 (l / 16) .. +15.  Channels past N are zero.
+ * Size in bytes: sq_packed_weight_bytes(N, K) = ceil(N / 16) * (K / 64) * 1024.
+ * Requires K % 128 == 0 (SQ_ERR_SHAPE otherwise). */
+int64_t sq_packed_weight_bytes(int64_t N, int64_t K);
+sq_status sq_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wq_packed,
+                         void* stream);
+
+/* sq_w8a8_gemm_dequant / sq_w8a8_gemm_i32 with the weights in the packed
+ * layout; identical results.  K % 128 == 0. */
+sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_packed, const float* w_scale, int64_t M,
+                                      int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream);
+sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,
+                                  int64_t K, int32_t* acc, void* stream);
+
 /* Library version string (static storage). */
 const char* sq_version(void);
 

@@ -83,6 +83,7 @@ def test_config_layer(ref, dev, cid, layer):
         cols_d = torch.from_numpy(cols).to(dev)
         assert_equal(wq[cols_d], wq_r, "Wq (sampled channels)")
         assert_equal(sw[cols_d], sw_r, "w_scale (sampled channels)")
+        wp = sq.pack_weight(wq)
 
         for M in cfg.M:
             x_hat = sq.smooth_activation(xe_d[:M].contiguous(), s)
@@ -90,6 +91,9 @@ def test_config_layer(ref, dev, cid, layer):
             y = torch.empty(M, N, dtype=ydt, device=dev)
             sq.sq_w8a8_gemm_dequant(xq, sx, wq, sw, y)
             acc = sq.w8a8_gemm_i32(xq, wq)
+            y_p = torch.empty(M, N, dtype=ydt, device=dev)
+            sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y_p)
+            acc_p = sq.w8a8_gemm_i32_packed(xq, wp, N)
             torch.cuda.synchronize()
             rows = _sample(M, NSAMPLE, 3000 * cid + M)
             rows_d = torch.from_numpy(rows).to(dev)
@@ -102,8 +106,11 @@ def test_config_layer(ref, dev, cid, layer):
             assert_equal(sx[rows_d], sx_r, "x_scale (sampled tokens)")
             acc_r = ref.gemm_i32(xq_r, wq_r)
             assert_equal(acc[rows_d][:, cols_d], acc_r, "acc (sampled)")
-            same = assert_y_close(y[rows_d][:, cols_d], ref.dequant(acc_r, sx_r, sw_r), "y")
+            assert_equal(acc_p[rows_d][:, cols_d], acc_r, "acc, packed weights (sampled)")
+            y_r = ref.dequant(acc_r, sx_r, sw_r)
+            same = assert_y_close(y[rows_d][:, cols_d], y_r, "y")
+            assert_y_close(y_p[rows_d][:, cols_d], y_r, "y, packed weights")
             log("  alpha %.2f M %5d: ok (y bit-equal to RNE(oracle) %.4f)" % (alpha, M, same))
-            del x_hat, xq, sx, y, acc
-        del s, w_hat, wq, sw
+            del x_hat, xq, sx, y, acc, y_p, acc_p
+        del s, w_hat, wq, sw, wp
         torch.cuda.empty_cache()

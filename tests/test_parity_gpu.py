@@ -202,6 +202,49 @@ def test_gemm_dequant(ref, dev, M, N, K, ydt):
     log("  bit-equal to RNE(oracle):", same)
 
 
+# --------------------------------------------------------------- packed weights
+
+def _pack_ref(wq):
+    """The documented packed layout, re-laid out with numpy (no arithmetic)."""
+    N, K = wq.shape
+    NB, KG = (N + 15) // 16, K // 64
+    pad = np.zeros((NB * 16, K), np.int8)
+    pad[:N] = wq
+    # [NB, 16 rows, KG, 4 subgroups, 16 bytes] -> [NB, KG, 4 subgroups, 16 rows, 16 bytes]
+    t = pad.reshape(NB, 16, KG, 4, 16).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (37, 256), (4099, 4096), (300, 1280)])
+def test_pack_weight_layout(dev, N, K):
+    wq = synth.random_int8(N + K, N, K)
+    wp = sq.pack_weight(_gpu(torch.from_numpy(wq), dev))
+    torch.cuda.synchronize()
+    assert wp.numel() == sq.sq_packed_weight_bytes(N, K)
+    assert_equal(wp, _pack_ref(wq), "packed weight bytes")
+
+
+PACKED_SHAPES = [s for s in GEMM_SHAPES if s[2] % 128 == 0] + [(1, 4096, 16384), (16, 300, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", PACKED_SHAPES)
+def test_gemm_packed(ref, dev, M, N, K):
+    log("gemm_packed", M, N, K)
+    xq, wq = _codes(M, N, K, M * 13 + N * 3 + K)
+    r = np.random.default_rng([M, N, K, 1])
+    sx = (r.uniform(0.01, 2.0, M) / 127).astype(np.float32)
+    sw = (r.uniform(1e-4, 0.05, N) / 127).astype(np.float32)
+    xq_d = _gpu(torch.from_numpy(xq), dev)
+    wp = sq.pack_weight(_gpu(torch.from_numpy(wq), dev))
+    sw_d = _gpu(torch.from_numpy(sw), dev)
+    acc = sq.w8a8_gemm_i32_packed(xq_d, wp, N)
+    y = sq.w8a8_gemm_dequant_packed(xq_d, _gpu(torch.from_numpy(sx), dev), wp, sw_d, torch.float16)
+    torch.cuda.synchronize()
+    acc_r = ref.gemm_i32(xq, wq)
+    assert_equal(acc, acc_r, "acc (packed)")
+    assert_y_close(y, ref.dequant(acc_r, sx, sw), "y (packed)")
+
+
 # --------------------------------------------------------------- whole chain
 
 @pytest.mark.parametrize("ydt", ["f16", "f32"])

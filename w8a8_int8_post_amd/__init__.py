@@ -23,7 +23,9 @@ __all__ = [
     "SQError", "load_library", "version",
     "sq_calibrate_absmax", "sq_smooth_fold", "sq_quant_weight_perchannel",
     "sq_quant_act_pertoken", "sq_w8a8_gemm_dequant", "sq_w8a8_gemm_i32",
-    "sq_smooth_activation",
+    "sq_smooth_activation", "sq_packed_weight_bytes", "sq_pack_weight",
+    "sq_w8a8_gemm_dequant_packed", "sq_w8a8_gemm_i32_packed", "pack_weight",
+    "w8a8_gemm_dequant_packed", "w8a8_gemm_i32_packed", "linear_w8a8_packed",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -62,11 +64,16 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_gemm_dequant": [P, P, P, P, I64, I64, I64, P, E, P],
             "sq_w8a8_gemm_i32": [P, P, I64, I64, I64, P, P],
             "sq_smooth_activation": [P, E, I64, I64, P, P, P],
+            "sq_pack_weight": [P, I64, I64, P, P],
+            "sq_w8a8_gemm_dequant_packed": [P, P, P, P, I64, I64, I64, P, E, P],
+            "sq_w8a8_gemm_i32_packed": [P, P, I64, I64, I64, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        lib.sq_packed_weight_bytes.argtypes = [I64, I64]
+        lib.sq_packed_weight_bytes.restype = I64
         lib.sq_version.argtypes = []
         lib.sq_version.restype = ctypes.c_char_p
         _lib = lib
@@ -160,6 +167,44 @@ def sq_smooth_activation(x, s, x_hat, stream=None):
           _dev(x_hat, "x_hat"), _stream(x, stream))
 
 
+def sq_packed_weight_bytes(N: int, K: int) -> int:
+    return int(load_library().sq_packed_weight_bytes(N, K))
+
+
+def sq_pack_weight(wq, wq_packed, stream=None):
+    N, K = wq.shape
+    _check_packed(wq_packed, N, K)
+    _call("sq_pack_weight", _dev(wq, "wq", torch.int8), N, K, _dev(wq_packed, "wq_packed", torch.int8),
+          _stream(wq, stream))
+
+
+def _check_packed(wq_packed, N, K):
+    need = sq_packed_weight_bytes(N, K)
+    if need < 0 or wq_packed.numel() * wq_packed.element_size() < need:
+        raise ValueError("packed weight buffer too small for N=%d K=%d" % (N, K))
+
+
+def sq_w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, N, y, stream=None):
+    M, K = xq.shape
+    if tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_gemm_dequant_packed", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype],
+          _stream(xq, stream))
+
+
+def sq_w8a8_gemm_i32_packed(xq, wq_packed, N, acc, stream=None):
+    M, K = xq.shape
+    if tuple(acc.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_gemm_i32_packed", _dev(xq, "xq", torch.int8),
+          _dev(wq_packed, "wq_packed", torch.int8), M, N, K, _dev(acc, "acc", torch.int32),
+          _stream(xq, stream))
+
+
 # --------------------------------------------------------------------------
 # Allocating conveniences (outputs from torch.empty on the input's device)
 
@@ -212,6 +257,37 @@ def smooth_activation(x, s, stream=None):
     out = torch.empty_like(x)
     sq_smooth_activation(x, s, out, stream)
     return out
+
+
+def pack_weight(wq, stream=None):
+    """Fragment-packed copy of wq [N x K] (1-D int8 tensor)."""
+    N, K = wq.shape
+    nbytes = sq_packed_weight_bytes(N, K)
+    if nbytes < 0:
+        raise SQError("sq_packed_weight_bytes", 2)
+    wp = torch.empty(nbytes, dtype=torch.int8, device=wq.device)
+    sq_pack_weight(wq, wp, stream)
+    return wp
+
+
+def w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, out_dtype=torch.float16,
+                             stream=None):
+    N = w_scale.shape[0]
+    y = torch.empty(xq.shape[0], N, dtype=out_dtype, device=xq.device)
+    sq_w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, N, y, stream)
+    return y
+
+
+def w8a8_gemm_i32_packed(xq, wq_packed, N, stream=None):
+    acc = torch.empty(xq.shape[0], N, dtype=torch.int32, device=xq.device)
+    sq_w8a8_gemm_i32_packed(xq, wq_packed, N, acc, stream)
+    return acc
+
+
+def linear_w8a8_packed(x_hat, wq_packed, w_scale, out_dtype=torch.float16, stream=None):
+    """Run-time layer on packed weights: per-token quantisation then GEMM."""
+    xq, sx = quant_act_pertoken(x_hat, None, stream)
+    return w8a8_gemm_dequant_packed(xq, sx, wq_packed, w_scale, out_dtype, stream)
 
 
 def linear_w8a8(x_hat, wq, w_scale, out_dtype=torch.float16, stream=None):

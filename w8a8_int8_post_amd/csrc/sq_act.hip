@@ -5,11 +5,14 @@
 // (O1: activations quantised per token, dynamically) and section
 // 数学的に何をしているのか (X diag(s)^-1 when the scale is not folded).
 //
-// One workgroup per token row.  Each thread keeps its slice of the row in
-// registers between the absmax reduction and the quantisation, so the row is
-// read from HBM once; loads are 16 bytes per lane and consecutive lanes read
-// consecutive 16-byte pieces of the row.  Rows longer than the register
-// budget take a two-pass variant (the second pass re-reads the row).
+// One or more wavefronts per token row.  Each lane keeps its slice of the row
+// in registers between the absmax reduction and the quantisation, so the row
+// is read from HBM once; loads are 16 bytes per lane and consecutive lanes
+// read consecutive 16-byte pieces of the row.  Many short rows (prefill) take
+// one wavefront each, reduced without LDS; few rows (decode) are spread over
+// up to 16 wavefronts.  Rows whose length is not a multiple of 16 bytes, or
+// longer than the register budget, take a two-pass variant (the second pass
+// re-reads the row).
 #include "sq_device.h"
 #include "sq_launch.h"
 
@@ -49,35 +52,51 @@ __device__ inline void store_codes(int8_t* dst, const float (&v)[V], float step)
     }
 }
 
-// Register-resident variant: K / VEC <= NT * NCH.
-template <class D, int NT, int NCH, bool SMOOTH>
+// Register-resident variant: WPR waves per token row, each lane holding up to
+// NCH 16-byte pieces of the row (K / VEC <= 64 * WPR * NCH).  A workgroup of
+// NT threads handles NT / (64 * WPR) rows; with WPR == 1 the reduction is a
+// wavefront reduction only (no LDS, no barrier).
+template <class D, int NT, int WPR, int NCH, bool SMOOTH>
 __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* __restrict__ x,
                                                            const float* __restrict__ smooth,
-                                                           int64_t K, int8_t* __restrict__ xq,
+                                                           int64_t M, int64_t K,
+                                                           int8_t* __restrict__ xq,
                                                            float* __restrict__ sx) {
     constexpr int V = D::VEC;
+    constexpr int RPW = NT / (64 * WPR);  // rows per workgroup
     __shared__ float red[NT / 64];
-    const int64_t m = blockIdx.x;
-    const typename D::T* row = x + m * K;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const int part = wave % WPR;  // which of the row's waves
+    const bool live = m < M;
+    const typename D::T* row = x + (live ? m : 0) * K;
     const int64_t nch = K / V;
     float v[NCH][V];
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int64_t ci = (int64_t)c * NT + threadIdx.x;
-        if (ci < nch) {
+        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+        if (live && ci < nch) {
             load_smoothed<D, SMOOTH>(row + ci * V, smooth, ci * V, v[c]);
 #pragma unroll
             for (int e = 0; e < V; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][e]));
         }
     }
-    amax = block_max<NT>(amax, red);
+    amax = wave_max(amax);
+    if constexpr (WPR > 1) {
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        const int w0 = wave - part;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) amax = __builtin_fmaxf(amax, red[w0 + w]);
+    }
+    if (!live) return;
     const float step = quant_step(amax);
-    if (threadIdx.x == 0) sx[m] = step;
+    if (part == 0 && lane == 0) sx[m] = step;
     int8_t* qrow = xq + m * K;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int64_t ci = (int64_t)c * NT + threadIdx.x;
+        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
         if (ci < nch) store_codes<V>(qrow + ci * V, v[c], step);
     }
 }
@@ -112,17 +131,33 @@ template <class D, bool SMOOTH>
 hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* smooth, int8_t* xq,
                            float* sx, hipStream_t s) {
     const typename D::T* x = static_cast<const typename D::T*>(xv);
-    const dim3 grid((unsigned)M);
-    const int64_t nch = K / D::VEC;
-    if (K % D::VEC == 0 && nch <= 256 * 4) {
-        hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, SMOOTH>), grid, dim3(256), 0, s, x,
-                           smooth, K, xq, sx);
-    } else if (K % D::VEC == 0 && nch <= 512 * 12) {
-        hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 12, SMOOTH>), grid, dim3(512), 0, s, x,
-                           smooth, K, xq, sx);
+    const int64_t nch = K / D::VEC;  // 16-byte pieces per row
+    auto grid = [&](int rows_per_wg) { return dim3((unsigned)((M + rows_per_wg - 1) / rows_per_wg)); };
+    if (K % D::VEC != 0 || nch > 16 * 64 * 8) {
+        hipLaunchKernelGGL((act_quant_2pass_kernel<D, 512, SMOOTH>), dim3((unsigned)M), dim3(512), 0,
+                           s, x, smooth, K, xq, sx);
+    } else if (M >= 512) {
+        // Many rows: as few waves per row as hold the row at 8 pieces per lane.
+        if (nch <= 64 * 8)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 8, SMOOTH>), grid(4), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 128 * 8)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 2, 8, SMOOTH>), grid(2), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 256 * 8)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, 8, SMOOTH>), grid(1), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 8, SMOOTH>), grid(1), dim3(1024),
+                               0, s, x, smooth, M, K, xq, sx);
     } else {
-        hipLaunchKernelGGL((act_quant_2pass_kernel<D, 512, SMOOTH>), grid, dim3(512), 0, s, x,
-                           smooth, K, xq, sx);
+        // Few rows (decode): spread each row over up to 16 waves.
+        if (nch <= 256 * 4)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, 4, SMOOTH>), grid(1), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 8, SMOOTH>), grid(1), dim3(1024),
+                               0, s, x, smooth, M, K, xq, sx);
     }
     return hipGetLastError();
 }

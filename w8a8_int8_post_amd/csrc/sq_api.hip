@@ -105,4 +105,41 @@ sq_status sq_smooth_activation(const void* x, sq_dtype dt, int64_t M, int64_t K,
     return hip_status(sq::launch_smooth_act(x, to_dt(dt), M, K, s, x_hat, as_stream(stream)));
 }
 
+int64_t sq_packed_weight_bytes(int64_t N, int64_t K) {
+    if (!dims_ok(N, K) || K % 128 != 0) return -1;
+    return sq::packed_weight_bytes(N, K);
+}
+
+sq_status sq_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wq_packed, void* stream) {
+    if (!wq || !wq_packed) return SQ_ERR_NULL;
+    if (!dims_ok(N, K) || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (!aligned16(wq) || !aligned16(wq_packed)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_pack_weight(wq, N, K, wq_packed, as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
+                                      const int8_t* wq_packed, const float* w_scale, int64_t M,
+                                      int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq_packed || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq_packed) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_gemm_packed(xq, x_scale, wq_packed, w_scale, M, N, K, y, out,
+                                             as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,
+                                  int64_t K, int32_t* acc, void* stream) {
+    if (!xq || !wq_packed || !acc) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!aligned16(xq) || !aligned16(wq_packed) || !aligned16(acc)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_gemm_packed(xq, nullptr, wq_packed, nullptr, M, N, K, acc,
+                                             sq::Out::I32, as_stream(stream)));
+}
+
 }  // extern "C"

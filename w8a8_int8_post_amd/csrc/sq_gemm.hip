@@ -23,6 +23,11 @@
 //    that tiles sharing operand panels run on the same XCD's L2.
 //  * tiled (M > 64, other K): the same tiling with register-staged loads and
 //    byte-granular masking of the K tail.
+//  * packed variants of dma and skinny read the weights in a fragment-packed
+//    layout (see pack_weight_kernel) where every wave load of weights is one
+//    contiguous kilobyte, independent of K: with the row-major layout the 16
+//    rows of one skinny-kernel fragment lie K bytes apart, which for K a
+//    multiple of 16 KB puts them all on the same HBM channel.
 //  * skinny (M <= 64, the decode regime): the weight matrix is streamed once
 //    from HBM straight into MFMA fragments (no LDS staging); one workgroup
 //    per 16 output channels, its waves interleave over K in 256-byte steps,
@@ -223,7 +228,7 @@ template <> struct Half<Out::BF16> {
     __device__ static T cvt(float f) { return BF16::from_f32(f); }
 };
 
-template <int BM, int BN, int WM, int WN, Out O>
+template <int BM, int BN, int WM, int WN, Out O, bool PACKED_B>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
@@ -252,6 +257,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
 
     auto swz = [](int row) { return (row >> SWS) & (CPR - 1); };
     auto off = [&](int row, int chunk) { return row * BK + ((chunk ^ swz(row)) << 4); };
+    // Packed B stage: 1 KB blocks (row block, k-group); inside a block the
+    // 16-byte piece of row r, k-subgroup g sits at (g * 16 + r) * 16.
+    auto boff = [&](int row, int chunk) {
+        if constexpr (PACKED_B)
+            return ((row >> 4) * 2 + (chunk >> 2)) * 1024 + (((chunk & 3) << 4) + (row & 15)) * 16;
+        else
+            return off(row, chunk);
+    };
     // Each wave load fills 64 consecutive 16-byte LDS slots; slot p of a
     // stage holds row p / CPR, logical chunk (p % CPR) ^ swz(row).
     const int8_t* asrc[A_INS];
@@ -262,11 +275,20 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
         const int gm = m0 + row < M ? m0 + row : M - 1;
         asrc[i] = A + (int64_t)gm * K + c * 16;
     }
+    const int KG = K / 64;  // 64-byte k-groups per packed row block
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-        const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
-        const int gn = n0 + row < N ? n0 + row : N - 1;
-        bsrc[i] = B + (int64_t)gn * K + c * 16;
+        if constexpr (PACKED_B) {
+            // one contiguous 1 KB block per wave load: row block q / 2, k-group q % 2
+            const int q = i * NW + wave;
+            const int nb = (N + 15) / 16;
+            const int rb = n0 / 16 + q / 2 < nb ? n0 / 16 + q / 2 : nb - 1;
+            bsrc[i] = B + ((int64_t)rb * KG + (q & 1)) * 1024 + lane * 16;
+        } else {
+            const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
+            const int gn = n0 + row < N ? n0 + row : N - 1;
+            bsrc[i] = B + (int64_t)gn * K + c * 16;
+        }
     }
     auto issue = [&](int buf, int k0) {
         int8_t* sA = smem + buf * STAGE;
@@ -279,7 +301,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(bsrc[i] + k0),
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + (PACKED_B ? k0 * 16 : k0)),
                 (__attribute__((address_space(3))) void*)(sB + (i * NW + wave) * 1024), 16, 0, 0);
     };
 
@@ -306,7 +328,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
             af[0][i] = *reinterpret_cast<const v4i*>(sA + off(wm0 + i * 32 + (lane & 31), lane >> 5));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            bf[0][j] = *reinterpret_cast<const v4i*>(sB + off(wn0 + j * 32 + (lane & 31), lane >> 5));
+            bf[0][j] = *reinterpret_cast<const v4i*>(sB + boff(wn0 + j * 32 + (lane & 31), lane >> 5));
         if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -318,7 +340,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
                     af[nb][i] = *reinterpret_cast<const v4i*>(sA + off(wm0 + i * 32 + (lane & 31), ch));
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    bf[nb][j] = *reinterpret_cast<const v4i*>(sB + off(wn0 + j * 32 + (lane & 31), ch));
+                    bf[nb][j] = *reinterpret_cast<const v4i*>(sB + boff(wn0 + j * 32 + (lane & 31), ch));
             }
             // D = W_tile * X_tile^T: D's rows are output channels, its columns tokens.
 #pragma unroll
@@ -476,6 +498,131 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fragment-packed weights.  Row block b (16 output channels) and 64-byte
+// k-group c form one 1 KB block at ((b * KG) + c) * 1024 whose 16-byte piece l
+// holds channel b*16 + l%16, bytes c*64 + (l/16)*16 .. +16 -- exactly the
+// 16 x 64 operand of v_mfma_i32_16x16x64_i8, so a wave reads one fragment as
+// one contiguous kilobyte.  KG = K / 64; rows past N are zero.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const int8_t* __restrict__ wq, int N, int K,
+                                                          int8_t* __restrict__ wp) {
+    const int KG = K / 64, NB = (N + 15) / 16;
+    const int64_t pieces = (int64_t)NB * KG * 64;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < pieces;
+         i += (int64_t)gridDim.x * 256) {
+        const int l = (int)(i & 63);
+        const int64_t blk = i >> 6;
+        const int c = (int)(blk % KG), b = (int)(blk / KG);
+        const int n = b * 16 + (l & 15);
+        v4i v = {0, 0, 0, 0};
+        if (n < N) v = *reinterpret_cast<const v4i*>(wq + (int64_t)n * K + c * 64 + (l >> 4) * 16);
+        *reinterpret_cast<v4i*>(wp + i * 16) = v;
+    }
+}
+
+// Skinny kernel on packed weights (K % 64 == 0): as gemm_skinny_kernel, with
+// each weight fragment one contiguous, non-temporal 1 KB wave load.
+template <int TB, int NW, Out O>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    constexpr int U = 2;
+    __shared__ v4i red[NW][TB][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b0 = blockIdx.x;  // row block
+    const int n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64;
+    const int nsteps = (KG + 3) >> 2;  // 256-byte steps
+    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+
+    v4i acc[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
+    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
+        v4i wf[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st0 + u * NW) * 4 + t;
+                wf[u][t] = c < KG ? __builtin_nontemporal_load(
+                                        reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024))
+                                  : v4i{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int c = (st0 + u * NW) * 4 + t;
+                    const int tok = b * 16 + r;
+                    const v4i xf = (c < KG && tok < M)
+                                       ? *reinterpret_cast<const v4i*>(X + (int64_t)tok * K + c * 64 + g * 16)
+                                       : v4i{0, 0, 0, 0};
+                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc[b], 0, 0, 0);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
+    __syncthreads();
+    if (threadIdx.x < TB * 64) {
+        const int b = wave;
+        v4i tot = red[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tot += red[w][b][lane];
+        const int tok = b * 16 + (lane & 15);
+        if (tok < M) {
+            const float sxm = (O != Out::I32) ? sx[tok] : 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + 4 * g + qq;
+                if (n < N) {
+                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
+                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
+                }
+            }
+        }
+    }
+}
+
+template <Out O>
+hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t* wp,
+                                const float* sw, int M, int N, int K, void* y, hipStream_t s) {
+    if (M <= 64) {
+        constexpr int NW = 8;
+        const dim3 grid((unsigned)((N + 15) / 16)), block(NW * 64);
+        if (M <= 16)
+            hipLaunchKernelGGL((gemm_skinny_packed_kernel<1, NW, O>), grid, block, 0, s, xq, wp, sx,
+                               sw, y, M, N, K);
+        else if (M <= 32)
+            hipLaunchKernelGGL((gemm_skinny_packed_kernel<2, NW, O>), grid, block, 0, s, xq, wp, sx,
+                               sw, y, M, N, K);
+        else if (M <= 48)
+            hipLaunchKernelGGL((gemm_skinny_packed_kernel<3, NW, O>), grid, block, 0, s, xq, wp, sx,
+                               sw, y, M, N, K);
+        else
+            hipLaunchKernelGGL((gemm_skinny_packed_kernel<4, NW, O>), grid, block, 0, s, xq, wp, sx,
+                               sw, y, M, N, K);
+    } else {
+        const int t256 = ((M + 255) / 256) * ((N + 255) / 256);
+        if (t256 >= 384) {
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O, true>), dim3(t256), dim3(512),
+                               0, s, xq, wp, sx, sw, y, M, N, K);
+        } else {
+            const int t128 = ((M + 127) / 128) * ((N + 127) / 128);
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O, true>), dim3(t128), dim3(256),
+                               0, s, xq, wp, sx, sw, y, M, N, K);
+        }
+    }
+    return hipGetLastError();
+}
+
 template <Out O, bool KVEC>
 hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                          int M, int N, int K, void* y, hipStream_t s) {
@@ -499,11 +646,11 @@ hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, co
         // one and a half times; otherwise 128 x 128 (two workgroups per CU).
         const int t256 = ((M + 255) / 256) * ((N + 255) / 256);
         if (t256 >= 384) {
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O>), dim3(t256), dim3(512), 0, s,
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O, false>), dim3(t256), dim3(512), 0, s,
                                xq, wq, sx, sw, y, M, N, K);
         } else {
             const int t128 = ((M + 127) / 128) * ((N + 127) / 128);
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O>), dim3(t128), dim3(256), 0, s,
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O, false>), dim3(t128), dim3(256), 0, s,
                                xq, wq, sx, sw, y, M, N, K);
         }
     } else {
@@ -523,6 +670,30 @@ hipError_t gemm_out(const int8_t* xq, const float* sx, const int8_t* wq, const f
 }
 
 }  // namespace
+
+int64_t packed_weight_bytes(int64_t N, int64_t K) { return ((N + 15) / 16) * (K / 64) * 1024; }
+
+hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp, hipStream_t s) {
+    const int64_t pieces = packed_weight_bytes(N, K) / 16;
+    int64_t blocks = (pieces + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wq, (int)N,
+                       (int)K, wp);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8_t* wp,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                              Out out, hipStream_t s) {
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (out) {
+        case Out::I32: return gemm_packed_dispatch<Out::I32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
+        case Out::F16: return gemm_packed_dispatch<Out::F16>(xq, x_scale, wp, w_scale, m, n, k, y, s);
+        case Out::BF16: return gemm_packed_dispatch<Out::BF16>(xq, x_scale, wp, w_scale, m, n, k, y, s);
+        case Out::F32: return gemm_packed_dispatch<Out::F32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
