@@ -35,19 +35,19 @@ __device__ inline void load_smoothed(const typename D::T* p, const float* smooth
     }
 }
 
-template <int V>
-__device__ inline void store_codes(int8_t* dst, const float (&v)[V], float step) {
+template <bool FAST, int V>
+__device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowStep& step) {
     if constexpr (V == 8) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= (uint32_t)(uint8_t)quant_code(v[e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) lo |= (uint32_t)(uint8_t)quant_code<FAST>(v[e], step) << (8 * e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code(v[4 + e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code<FAST>(v[4 + e], step) << (8 * e);
         *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     } else {
         uint32_t w = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code(v[e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code<FAST>(v[e], step) << (8 * e);
         *reinterpret_cast<uint32_t*>(dst) = w;
     }
 }
@@ -91,13 +91,21 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
         for (int w = 0; w < WPR; ++w) amax = __builtin_fmaxf(amax, red[w0 + w]);
     }
     if (!live) return;
-    const float step = quant_step(amax);
-    if (part == 0 && lane == 0) sx[m] = step;
+    const RowStep step = row_step(amax);
+    if (part == 0 && lane == 0) sx[m] = step.step;
     int8_t* qrow = xq + m * K;
+    if (step.fast) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
-        if (ci < nch) store_codes<V>(qrow + ci * V, v[c], step);
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            if (ci < nch) store_codes<true, V>(qrow + ci * V, v[c], step);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            if (ci < nch) store_codes<false, V>(qrow + ci * V, v[c], step);
+        }
     }
 }
 
@@ -117,13 +125,13 @@ __global__ __launch_bounds__(NT) void act_quant_2pass_kernel(const typename D::T
         amax = __builtin_fmaxf(amax, __builtin_fabsf(v));
     }
     amax = block_max<NT>(amax, red);
-    const float step = quant_step(amax);
-    if (threadIdx.x == 0) sx[m] = step;
+    const RowStep step = row_step(amax);
+    if (threadIdx.x == 0) sx[m] = step.step;
     int8_t* qrow = xq + m * K;
     for (int64_t k = threadIdx.x; k < K; k += NT) {
         float v = D::to_f32(row[k]);
         if constexpr (SMOOTH) v = v / smooth[k];
-        qrow[k] = (int8_t)quant_code(v, step);
+        qrow[k] = (int8_t)(step.fast ? quant_code<true>(v, step) : quant_code<false>(v, step));
     }
 }
 

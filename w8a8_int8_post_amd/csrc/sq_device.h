@@ -54,11 +54,53 @@ __device__ inline void load_vec(const typename D::T* p, float (&out)[D::VEC]) {
 // from zero (v / step), -127, 127); a zero step gives code 0.
 __device__ inline float quant_step(float absmax) { return absmax / 127.0f; }
 
-__device__ inline int quant_code(float v, float step) {
-    if (step == 0.0f) return 0;
-    float r = __builtin_roundf(v / step);
+__device__ inline int code_from_quotient(float t) {
+    float r = __builtin_roundf(t);  // halves away from zero
     r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
     return (int)r;
+}
+
+__device__ inline int quant_code(float v, float step) {
+    if (step == 0.0f) return 0;
+    return code_from_quotient(v / step);
+}
+
+// One step shared by a whole row: the quotient v / step is needed for every
+// element, so the correctly rounded reciprocal y = 1 / step is computed once
+// and each quotient is formed by Markstein's correction
+//   q0 = RN(v * y),  r = v - q0 * step (exact, one FMA),  q = RN(q0 + r * y),
+// which equals the IEEE quotient RN(v / step) when y = RN(1 / step) and no
+// intermediate leaves the normal range (P. Markstein, "Computation of
+// elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+// Dev. 34(1), 1990; correctness proofs by Cornea-Hasegan, Golliver and
+// Markstein, ARITH-14, 1999).  Steps outside [2^-96, 2^96] use the plain
+// IEEE division instead.
+struct RowStep {
+    float step, rcp;
+    bool fast;
+};
+
+__device__ inline RowStep row_step(float absmax) {
+    RowStep q;
+    q.step = quant_step(absmax);
+    q.fast = q.step >= 0x1p-96f && q.step <= 0x1p96f;
+    q.rcp = q.fast ? 1.0f / q.step : 0.0f;
+    return q;
+}
+
+// FAST: the caller has checked q.fast (a row-uniform branch taken once).
+template <bool FAST>
+__device__ inline int quant_code(float v, const RowStep& q) {
+    if (q.step == 0.0f) return 0;
+    float t;
+    if constexpr (FAST) {
+        const float q0 = v * q.rcp;
+        const float r = __builtin_fmaf(-q0, q.step, v);
+        t = __builtin_fmaf(r, q.rcp, q0);
+    } else {
+        t = v / q.step;
+    }
+    return code_from_quotient(t);
 }
 
 // ------------------------------------------------------------ reductions
