@@ -172,6 +172,23 @@ def time_graphs(graphs, iters, warmup):
     return e0.elapsed_time(e1) / iters  # ms per replay
 
 
+def profiled_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 summary, if it
+    was taken on the current GEMM source (else None)."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "gemm_prefill_opt6.7b.md")
+    src = os.path.join(ROOT, "w8a8_int8_post_amd", "csrc", "sq_gemm.hip")
+    try:
+        fields = dict(ln.split(": ", 1) for ln in open(prof).read().splitlines()
+                      if ln.startswith(("traffic_bytes_per_launch:", "gemm_source_sha256:")))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if fields.get("gemm_source_sha256", "").strip() != digest:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def n_sets(footprint_bytes):
     return max(2, math.ceil((1 << 30) / footprint_bytes))
 
@@ -298,7 +315,9 @@ def main():
             "peak": PEAK_I8_TOPS,
             "unit": "TOP/s",
             "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic() if packed_best else None,
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
+                            "profiles/gemm_prefill_opt6.7b.md)",
             "avg_launch_us": round(gemm_ms * 1e3, 2),
             "per_launch_ops": ops_step / len(layers),
         },
