@@ -133,8 +133,11 @@ class Bufs:
 
     def step(self):
         for (x_hat, w, sw, xq, sx, y, N) in self.items:
-            sq.sq_quant_act_pertoken(x_hat, xq, sx)
-            self._gemm(xq, sx, w, sw, y, N)
+            if self.packed:  # one call per layer; one kernel for M <= 4
+                sq.sq_w8a8_linear_packed(x_hat, w, sw, xq, sx, y)
+            else:
+                sq.sq_quant_act_pertoken(x_hat, xq, sx)
+                self._gemm(xq, sx, w, sw, y, N)
 
     def gemm_only(self):
         for (x_hat, w, sw, xq, sx, y, N) in self.items:

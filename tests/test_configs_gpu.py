@@ -94,6 +94,8 @@ def test_config_layer(ref, dev, cid, layer):
             y_p = torch.empty(M, N, dtype=ydt, device=dev)
             sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y_p)
             acc_p = sq.w8a8_gemm_i32_packed(xq, wp, N)
+            # the one-call layer (a single fused kernel at M <= 4)
+            y_f, xq_f, sx_f = sq.linear_w8a8_packed(x_hat, wp, sw, ydt)
             torch.cuda.synchronize()
             rows = _sample(M, NSAMPLE, 3000 * cid + M)
             rows_d = torch.from_numpy(rows).to(dev)
@@ -110,7 +112,10 @@ def test_config_layer(ref, dev, cid, layer):
             y_r = ref.dequant(acc_r, sx_r, sw_r)
             same = assert_y_close(y[rows_d][:, cols_d], y_r, "y")
             assert_y_close(y_p[rows_d][:, cols_d], y_r, "y, packed weights")
+            assert_equal(xq_f[rows_d], xq_r, "Xq (one-call layer)")
+            assert_equal(sx_f[rows_d], sx_r, "x_scale (one-call layer)")
+            assert_y_close(y_f[rows_d][:, cols_d], y_r, "y (one-call layer)")
             log("  alpha %.2f M %5d: ok (y bit-equal to RNE(oracle) %.4f)" % (alpha, M, same))
-            del x_hat, xq, sx, y, acc, y_p, acc_p
+            del x_hat, xq, sx, y, acc, y_p, acc_p, y_f, xq_f, sx_f
         del s, w_hat, wq, sw, wp
         torch.cuda.empty_cache()

@@ -151,7 +151,8 @@ GEMM_SHAPES = [
     (65, 300, 1040), (300, 513, 2064), (70, 100, 100),
     (1000, 1000, 1008), (129, 255, 48),                          # register-staged tiles
     (512, 2048, 4096), (257, 256, 4096), (300, 130, 128),        # 128 x 128 DMA tiles
-    (2048, 12288, 256), (2000, 12300, 128),                      # 256 x 256 DMA tiles
+    (2048, 12288, 256), (2000, 12300, 128), (1999, 4100, 384),   # 256 x 256 DMA tiles
+    (2048, 4096, 256),                                           # 128 x 128 DMA tiles
 ]
 
 
@@ -243,6 +244,59 @@ def test_gemm_packed(ref, dev, M, N, K):
     acc_r = ref.gemm_i32(xq, wq)
     assert_equal(acc, acc_r, "acc (packed)")
     assert_y_close(y, ref.dequant(acc_r, sx, sw), "y (packed)")
+
+
+# ------------------------------------------- whole run-time layer (packed)
+
+LINEAR_CASES = [
+    # M <= 4 and M * K <= 65536: one fused kernel
+    (1, 37, 128, "f16", "f16"), (2, 4099, 4096, "bf16", "bf16"), (3, 300, 1024, "f32", "f32"),
+    (4, 12288, 4096, "f16", "f16"), (4, 1000, 16384, "f16", "f32"),
+    (1, 512, 28672, "bf16", "f16"),
+    # two launches: quantiser then the packed GEMM
+    (4, 200, 16512, "f16", "f16"), (5, 300, 1024, "f16", "f16"), (64, 600, 2048, "f16", "bf16"),
+    (300, 513, 2048, "bf16", "f16"),
+]
+
+
+def _linear_check(ref, dev, x, wq, ydt):
+    """sq_w8a8_linear_packed against the oracle and against the two-call path."""
+    M, K = x.shape
+    N = wq.shape[0]
+    sw = (np.random.default_rng([M, N, K, 2]).uniform(1e-4, 0.05, N) / 127).astype(np.float32)
+    x_d = _gpu(x, dev)
+    wp = sq.pack_weight(_gpu(torch.from_numpy(wq), dev))
+    sw_d = _gpu(torch.from_numpy(sw), dev)
+    y, xq, sx = sq.linear_w8a8_packed(x_d, wp, sw_d, DT[ydt])
+    xq2, sx2 = sq.quant_act_pertoken(x_d)
+    y2 = sq.w8a8_gemm_dequant_packed(xq2, sx2, wp, sw_d, DT[ydt])
+    torch.cuda.synchronize()
+    xq_r, sx_r = ref.quant_act_pertoken(x if x.dtype != torch.float32 else x.numpy())
+    assert_equal(xq, xq_r, "xq")
+    assert_equal(sx, sx_r, "x_scale")
+    acc_r = ref.gemm_i32(xq_r, wq)
+    assert_y_close(y, ref.dequant(acc_r, sx_r, sw), "y")
+    assert_equal(y.cpu().view(torch.int16 if ydt != "f32" else torch.int32),
+                 y2.cpu().view(torch.int16 if ydt != "f32" else torch.int32).numpy(),
+                 "y vs two-call path")
+
+
+@pytest.mark.parametrize("M,N,K,xdt,ydt", LINEAR_CASES)
+def test_linear_packed(ref, dev, M, N, K, xdt, ydt):
+    log("linear_packed", M, N, K, xdt, ydt)
+    x = synth.random_matrix(7 * M + K + N, M, K, xdt, outlier_cols=[1, K - 3], factor=30.0)
+    _, wq = _codes(M, N, K, M * 5 + N * 7 + K)
+    _linear_check(ref, dev, x, wq, ydt)
+
+
+def test_linear_packed_special_rows(ref, dev):
+    # a zero row (step 0), a subnormal step, a step above 2^96 (IEEE division
+    # path) and an ordinary row, through the fused kernel
+    K = 256
+    x = torch.from_numpy((np.random.default_rng(6).standard_normal((4, K)) *
+                          np.array([[0.0], [1e-40], [1e35], [1.0]])).astype(np.float32))
+    _, wq = _codes(4, 100, K, 11)
+    _linear_check(ref, dev, x, wq, "f32")
 
 
 # --------------------------------------------------------------- whole chain

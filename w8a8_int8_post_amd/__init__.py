@@ -26,6 +26,7 @@ __all__ = [
     "sq_smooth_activation", "sq_packed_weight_bytes", "sq_pack_weight",
     "sq_w8a8_gemm_dequant_packed", "sq_w8a8_gemm_i32_packed", "pack_weight",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_i32_packed", "linear_w8a8_packed",
+    "sq_w8a8_linear_packed",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -67,6 +68,7 @@ def load_library() -> ctypes.CDLL:
             "sq_pack_weight": [P, I64, I64, P, P],
             "sq_w8a8_gemm_dequant_packed": [P, P, P, P, I64, I64, I64, P, E, P],
             "sq_w8a8_gemm_i32_packed": [P, P, I64, I64, I64, P, P],
+            "sq_w8a8_linear_packed": [P, E, I64, I64, P, P, I64, P, P, P, E, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -205,6 +207,18 @@ def sq_w8a8_gemm_i32_packed(xq, wq_packed, N, acc, stream=None):
           _stream(xq, stream))
 
 
+def sq_w8a8_linear_packed(x, wq_packed, w_scale, xq, x_scale, y, stream=None):
+    M, K = x.shape
+    N = w_scale.shape[0]
+    if tuple(xq.shape) != (M, K) or tuple(y.shape) != (M, N) or x_scale.shape[0] != M:
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_linear_packed", _dev(x, "x"), _DT[x.dtype], M, K,
+          _dev(wq_packed, "wq_packed", torch.int8), _dev(w_scale, "w_scale", torch.float32), N,
+          _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32), _dev(y, "y"),
+          _DT[y.dtype], _stream(x, stream))
+
+
 # --------------------------------------------------------------------------
 # Allocating conveniences (outputs from torch.empty on the input's device)
 
@@ -285,9 +299,14 @@ def w8a8_gemm_i32_packed(xq, wq_packed, N, stream=None):
 
 
 def linear_w8a8_packed(x_hat, wq_packed, w_scale, out_dtype=torch.float16, stream=None):
-    """Run-time layer on packed weights: per-token quantisation then GEMM."""
-    xq, sx = quant_act_pertoken(x_hat, None, stream)
-    return w8a8_gemm_dequant_packed(xq, sx, wq_packed, w_scale, out_dtype, stream)
+    """Run-time layer on packed weights (sq_w8a8_linear_packed): (y, xq, sx)."""
+    M, K = x_hat.shape
+    N = w_scale.shape[0]
+    xq = torch.empty(M, K, dtype=torch.int8, device=x_hat.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x_hat.device)
+    y = torch.empty(M, N, dtype=out_dtype, device=x_hat.device)
+    sq_w8a8_linear_packed(x_hat, wq_packed, w_scale, xq, sx, y, stream)
+    return y, xq, sx
 
 
 def linear_w8a8(x_hat, wq, w_scale, out_dtype=torch.float16, stream=None):

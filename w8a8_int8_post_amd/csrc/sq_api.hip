@@ -142,4 +142,19 @@ sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int
                                              sq::Out::I32, as_stream(stream)));
 }
 
+sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                const int8_t* wq_packed, const float* w_scale, int64_t N,
+                                int8_t* xq, float* x_scale, void* y, sq_dtype ydt, void* stream) {
+    if (!x || !wq_packed || !w_scale || !xq || !x_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || !dims_ok(K, 1) || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(xdt) || !dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(wq_packed) || !aligned16(w_scale) || !aligned16(xq) ||
+        !aligned16(x_scale) || !aligned16(y))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_linear_packed(x, to_dt(xdt), M, K, wq_packed, w_scale, N, xq,
+                                               x_scale, y, out, as_stream(stream)));
+}
+
 }  // extern "C"

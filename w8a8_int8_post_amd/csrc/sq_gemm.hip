@@ -228,11 +228,13 @@ template <> struct Half<Out::BF16> {
     __device__ static T cvt(float f) { return BF16::from_f32(f); }
 };
 
-template <int BM, int BN, int WM, int WN, Out O, bool PACKED_B>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel(
+template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
-    constexpr int BK = 128, SWS = 1, GM = 8;
+    constexpr int SWS = 1, GM = 8;
+    constexpr int KGT = BK / 64;  // packed k-groups per K tile
+    static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
     constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NT = NW * 64;
     constexpr int TM = WM / 32, TN = WN / 32, CPR = BK / 16, S = BK / 32;
     constexpr int A_INS = BM * CPR / NT, B_INS = BN * CPR / NT;  // 1 KB wave loads per thread
@@ -261,7 +263,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
     // 16-byte piece of row r, k-subgroup g sits at (g * 16 + r) * 16.
     auto boff = [&](int row, int chunk) {
         if constexpr (PACKED_B)
-            return ((row >> 4) * 2 + (chunk >> 2)) * 1024 + (((chunk & 3) << 4) + (row & 15)) * 16;
+            return ((row >> 4) * KGT + (chunk >> 2)) * 1024 + (((chunk & 3) << 4) + (row & 15)) * 16;
         else
             return off(row, chunk);
     };
@@ -279,11 +281,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dma_kernel
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
         if constexpr (PACKED_B) {
-            // one contiguous 1 KB block per wave load: row block q / 2, k-group q % 2
+            // one contiguous 1 KB block per wave load: row block q / KGT, k-group q % KGT
             const int q = i * NW + wave;
             const int nb = (N + 15) / 16;
-            const int rb = n0 / 16 + q / 2 < nb ? n0 / 16 + q / 2 : nb - 1;
-            bsrc[i] = B + ((int64_t)rb * KG + (q & 1)) * 1024 + lane * 16;
+            const int rb = n0 / 16 + q / KGT < nb ? n0 / 16 + q / KGT : nb - 1;
+            bsrc[i] = B + ((int64_t)rb * KG + (q % KGT)) * 1024 + lane * 16;
         } else {
             const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
             const int gn = n0 + row < N ? n0 + row : N - 1;
@@ -499,6 +501,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
 }
 
 
+
+// Tile shape for the DMA kernel: 256x256 tiles (one workgroup per CU) when
+// there are enough of them to fill the GPU about one and a half times, else
+// 128x128 tiles (two workgroups per CU).  Larger tiles re-read fewer operand
+// bytes, which decides once the weights no longer fit the Infinity Cache.
+template <Out O, bool PACKED>
+hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
+                      int N, int K, void* y, hipStream_t s) {
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (tiles(256, 256) >= 384) {
+        hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 64, O, PACKED>), dim3(tiles(256, 256)),
+                           dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
+    } else {
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2>),
+                           dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
+    }
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Fragment-packed weights.  Row block b (16 output channels) and 64-byte
 // k-group c form one 1 KB block at ((b * KG) + c) * 1024 whose 16-byte piece l
@@ -591,6 +612,159 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Whole decode layer in one launch (M <= 4 tokens, packed weights): every
+// workgroup first issues its first weight loads, then -- while they are in
+// flight -- computes each token's absmax over K from x (the same reduction
+// and quantiser as the standalone per-token kernel, so the codes and steps are
+// identical), writes the codes into LDS, and streams its 16 output channels
+// as gemm_skinny_packed_kernel does, reading the activation fragments from
+// LDS.  Workgroup 0 also stores xq and x_scale.  LDS: M * K bytes.
+constexpr int kFusedMaxM = 4;
+constexpr int kFusedMaxLds = 64 * 1024;
+
+template <class D, int NW, Out O>
+__global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
+    const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,
+    const float* __restrict__ sw, int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
+    void* __restrict__ Y, int M, int N, int K) {
+    constexpr int U = 2, NT = NW * 64, V = D::VEC;
+    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
+    __shared__ v4i red[NW][64];
+    __shared__ float rmax[NW][kFusedMaxM];
+    __shared__ float steps[kFusedMaxM];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b0 = blockIdx.x, n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64;
+    const int nsteps = (KG + 3) >> 2;
+    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+
+    // 1) first weight loads in flight
+    v4i wf[U][4];
+    auto load_w = [&](int st0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st0 + u * NW) * 4 + t;
+                wf[u][t] = c < KG ? __builtin_nontemporal_load(
+                                        reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024))
+                                  : v4i{0, 0, 0, 0};
+            }
+    };
+    load_w(wave);
+
+    // 2) per-token absmax and codes
+    const int nch = K / V;
+    float amax[kFusedMaxM];
+#pragma unroll
+    for (int m = 0; m < kFusedMaxM; ++m) {
+        amax[m] = 0.0f;
+        if (m < M)
+            for (int ci = threadIdx.x; ci < nch; ci += NT) {
+                float v[V];
+                load_vec<D>(X + (int64_t)m * K + (int64_t)ci * V, v);
+#pragma unroll
+                for (int e = 0; e < V; ++e) amax[m] = __builtin_fmaxf(amax[m], __builtin_fabsf(v[e]));
+            }
+        amax[m] = wave_max(amax[m]);
+        if (lane == 0) rmax[wave][m] = amax[m];
+    }
+    __syncthreads();
+    if (threadIdx.x < kFusedMaxM) {
+        float a = rmax[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a = __builtin_fmaxf(a, rmax[w][threadIdx.x]);
+        steps[threadIdx.x] = a;
+    }
+    __syncthreads();
+    for (int m = 0; m < M; ++m) {
+        const RowStep st = row_step(steps[m]);
+        if (b0 == 0 && threadIdx.x == 0) sx_out[m] = st.step;
+        for (int ci = threadIdx.x; ci < nch; ci += NT) {
+            float v[V];
+            load_vec<D>(X + (int64_t)m * K + (int64_t)ci * V, v);
+            int8_t q[V];
+            if (st.fast) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) q[e] = (int8_t)quant_code<true>(v[e], st);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) q[e] = (int8_t)quant_code<false>(v[e], st);
+            }
+            int8_t* dst = xs + (int64_t)m * K + (int64_t)ci * V;
+            if constexpr (V == 8) {
+                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(q);
+                if (b0 == 0) *reinterpret_cast<uint2*>(xq_out + (int64_t)m * K + (int64_t)ci * V) =
+                    *reinterpret_cast<const uint2*>(q);
+            } else {
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(q);
+                if (b0 == 0) *reinterpret_cast<uint32_t*>(xq_out + (int64_t)m * K + (int64_t)ci * V) =
+                    *reinterpret_cast<const uint32_t*>(q);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3) stream the weights
+    v4i acc = {0, 0, 0, 0};
+    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st0 + u * NW) * 4 + t;
+                const v4i xf = (c < KG && r < M)
+                                   ? *reinterpret_cast<const v4i*>(xs + r * K + c * 64 + g * 16)
+                                   : v4i{0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc, 0, 0, 0);
+            }
+        }
+        if (st0 + NW * U < nsteps) load_w(st0 + NW * U);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        v4i tot = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tot += red[w][lane];
+        const int tok = lane & 15;
+        if (tok < M) {
+            const float sxm = quant_step(steps[tok]);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + 4 * g + qq;
+                if (n < N) store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, sw[n]);
+            }
+        }
+    }
+}
+
+template <class D, Out O>
+hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
+                        void* y, int M, int N, int K, hipStream_t s) {
+    constexpr int NW = 8;
+    const size_t lds = (size_t)M * K;
+    hipLaunchKernelGGL((linear_decode_fused_kernel<D, NW, O>), dim3((unsigned)((N + 15) / 16)),
+                       dim3(NW * 64), lds, s, static_cast<const typename D::T*>(x), wp, sw, xq,
+                       sx, y, M, N, K);
+    return hipGetLastError();
+}
+
+template <class D>
+hipError_t fused_out(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
+                     void* y, Out out, int M, int N, int K, hipStream_t s) {
+    switch (out) {
+        case Out::F16: return launch_fused<D, Out::F16>(x, wp, sw, xq, sx, y, M, N, K, s);
+        case Out::BF16: return launch_fused<D, Out::BF16>(x, wp, sw, xq, sx, y, M, N, K, s);
+        case Out::F32: return launch_fused<D, Out::F32>(x, wp, sw, xq, sx, y, M, N, K, s);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
 template <Out O>
 hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t* wp,
                                 const float* sw, int M, int N, int K, void* y, hipStream_t s) {
@@ -610,15 +784,7 @@ hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t*
             hipLaunchKernelGGL((gemm_skinny_packed_kernel<4, NW, O>), grid, block, 0, s, xq, wp, sx,
                                sw, y, M, N, K);
     } else {
-        const int t256 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (t256 >= 384) {
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O, true>), dim3(t256), dim3(512),
-                               0, s, xq, wp, sx, sw, y, M, N, K);
-        } else {
-            const int t128 = ((M + 127) / 128) * ((N + 127) / 128);
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O, true>), dim3(t128), dim3(256),
-                               0, s, xq, wp, sx, sw, y, M, N, K);
-        }
+        return launch_dma<O, true>(xq, sx, wp, sw, M, N, K, y, s);
     }
     return hipGetLastError();
 }
@@ -642,17 +808,7 @@ hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, co
             hipLaunchKernelGGL((gemm_skinny_kernel<4, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
                                sw, y, M, N, K);
     } else if (KVEC && K % 128 == 0) {
-        // 256 x 256 tiles when there are enough of them to fill the GPU about
-        // one and a half times; otherwise 128 x 128 (two workgroups per CU).
-        const int t256 = ((M + 255) / 256) * ((N + 255) / 256);
-        if (t256 >= 384) {
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, O, false>), dim3(t256), dim3(512), 0, s,
-                               xq, wq, sx, sw, y, M, N, K);
-        } else {
-            const int t128 = ((M + 127) / 128) * ((N + 127) / 128);
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, O, false>), dim3(t128), dim3(256), 0, s,
-                               xq, wq, sx, sw, y, M, N, K);
-        }
+        return launch_dma<O, false>(xq, sx, wq, sw, M, N, K, y, s);
     } else {
         constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, SWS = 1;
         const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -693,6 +849,23 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
         case Out::F32: return gemm_packed_dispatch<Out::F32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
+                                const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
+                                void* y, Out out, hipStream_t s) {
+    if (M <= kFusedMaxM && M * K <= kFusedMaxLds) {
+        const int m = (int)M, n = (int)N, k = (int)K;
+        switch (xdt) {
+            case Dt::F32: return fused_out<F32>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+            case Dt::F16: return fused_out<F16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+            case Dt::BF16: return fused_out<BF16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,

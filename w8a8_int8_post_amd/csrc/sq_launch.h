@@ -32,4 +32,8 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                               Out out, hipStream_t s);
 
+hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
+                                const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
+                                void* y, Out out, hipStream_t s);
+
 }  // namespace sq
