@@ -180,11 +180,14 @@ def profiled_traffic():
     was taken on the current GEMM source (else None)."""
     import hashlib
     prof = os.path.join(ROOT, "profiles", "gemm_prefill_opt6.7b.md")
-    src = os.path.join(ROOT, "w8a8_int8_post_amd", "csrc", "sq_gemm.hip")
+    csrc = os.path.join(ROOT, "w8a8_int8_post_amd", "csrc")
     try:
         fields = dict(ln.split(": ", 1) for ln in open(prof).read().splitlines()
                       if ln.startswith(("traffic_bytes_per_launch:", "gemm_source_sha256:")))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in ("sq_gemm.hip", "sq_gemm_common.h", "sq_device.h"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+        digest = h.hexdigest()
         if fields.get("gemm_source_sha256", "").strip() != digest:
             return None
         return int(fields["traffic_bytes_per_launch"])

@@ -1,0 +1,458 @@
+// sq_decode.hip -- the few-token (decode) regime of the W8A8 linear layer, gfx950.
+//
+// P1 = abeam.tech explainer of "SmoothQuant: Accurate and Efficient
+// Post-Training Quantization for Large Language Models": 推論方法 (per-token
+// activation quantisation, then the INT8 GEMM); P4 = blogs.itmedia.co.jp
+// 量子化 blog, section 3 (multiply the scale factor back at inference).
+//
+// With at most 64 tokens the layer is bound by streaming the weight matrix
+// from HBM once.  The weights go from global memory straight into MFMA
+// fragments (no LDS staging): one workgroup per 16 output channels; its
+// waves interleave over K in 256-byte steps (4 k-groups of 64 bytes), each
+// wave keeping two steps of weight loads in flight (the next is issued before
+// the MFMAs of the current); v_mfma_i32_16x16x64_i8 takes the weights as the
+// 16-row operand and up to four 16-token blocks of activations as the other;
+// the waves' partial sums are added in LDS before the epilogue.
+//
+// Loads in the stream are straight-line code from clamped addresses (a
+// fragment past K meets a zero activation fragment; a row past N is never
+// stored), the wave index is made wave-uniform, and activation fragments
+// are read before the next weight loads are issued: loads complete in order,
+// so the MFMAs then wait only for their own operands, not for the loads in
+// flight behind them.
+//
+// Row-major weights of a multiple-of-16 KB row length put the 16 rows of one
+// fragment on one HBM channel; the fragment-packed layout (one contiguous
+// kilobyte per fragment) avoids that.
+#include "sq_gemm_common.h"
+
+namespace sq {
+namespace {
+
+constexpr int kNW = 8;  // waves per workgroup
+constexpr int kU = 1;   // 256-byte K steps per stage
+
+// A stage: this wave's k-groups c = (st + u * NW) * 4 + t, u < U, t < 4.
+template <int NW, int U, class WF>
+__device__ inline void load_stage(v4i (&w)[U][4], int st, int KG, const WF& wfrag) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = (st + u * NW) * 4 + t;
+            w[u][t] = wfrag(c < KG ? c : KG - 1);
+        }
+}
+
+template <int TB, int NW, int U, class XF>
+__device__ inline void load_x(v4i (&x)[U][TB][4], int st, const XF& xfrag) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[u][b][t] = xfrag(b, (st + u * NW) * 4 + t);
+}
+
+template <int TB, int U>
+__device__ inline void mfma_stage(v4i (&acc)[TB], const v4i (&w)[U][4], const v4i (&x)[U][TB][4]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u][t], x[u][b][t], acc[b], 0, 0, 0);
+}
+
+// The wave's steps st = wave, wave + S, ... (S = NW * U), double-buffered.
+// w0 must hold the stage at st = wave on entry (if wave < nsteps).
+// wfrag(c): weight fragment of k-group c < KG.  xfrag(b, c): activation
+// fragment of token block b, k-group c (zero past K or past the tokens).
+template <int TB, int NW, int U, class WF, class XF>
+__device__ inline void stream_k(v4i (&acc)[TB], v4i (&w0)[U][4], v4i (&w1)[U][4], int wave,
+                                int nsteps, int KG, const WF& wfrag, const XF& xfrag) {
+    constexpr int S = NW * U;
+    int st = wave;
+    if (st >= nsteps) return;
+    while (true) {
+        v4i x[U][TB][4];
+        load_x<TB, NW, U>(x, st, xfrag);
+        if (st + S >= nsteps) {
+            mfma_stage<TB, U>(acc, w0, x);
+            return;
+        }
+        load_stage<NW, U>(w1, st + S, KG, wfrag);
+        mfma_stage<TB, U>(acc, w0, x);
+        st += S;
+        load_x<TB, NW, U>(x, st, xfrag);
+        if (st + S >= nsteps) {
+            mfma_stage<TB, U>(acc, w1, x);
+            return;
+        }
+        load_stage<NW, U>(w0, st + S, KG, wfrag);
+        mfma_stage<TB, U>(acc, w1, x);
+        st += S;
+    }
+}
+
+// Cross-wave sum of the accumulators and the scaled store.  16 x 16
+// accumulator layout: lane l, element q holds row 4*(l/16) + q (output
+// channel) and column l%16 (token).  sxf(tok) gives the token's step.
+template <int TB, int NW, Out O, class SX>
+__device__ inline void reduce_store(v4i (*red)[TB][64], const v4i (&acc)[TB], int wave, int lane,
+                                    int n0, int M, int N, const float* __restrict__ sw, void* Y,
+                                    const SX& sxf) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
+    __syncthreads();
+    if (wave < TB) {
+        const int b = wave;
+        v4i tot = red[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tot += red[w][b][lane];
+        const int g = lane >> 4;
+        const int tok = b * 16 + (lane & 15);
+        if (tok < M) {
+            const float sxm = (O != Out::I32) ? sxf(tok) : 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + 4 * g + qq;
+                if (n < N) {
+                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
+                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row-major weights [N x K] (M <= 16 * TB).  KVEC: K % 16 == 0, so each
+// 16-byte chunk is wholly inside or outside a row and loads from a clamped
+// address; otherwise chunks are assembled byte by byte with masking.
+template <int TB, int NW, int U, Out O, bool KVEC>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    __shared__ v4i red[NW][TB][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = (K + 63) / 64, nsteps = (KG + 3) / 4;
+    const int wrow = n0 + r < N ? n0 + r : N - 1;
+
+    auto wfrag = [&](int c) -> v4i {
+        const int k = c * 64 + g * 16;
+        if constexpr (KVEC) {
+            const v4i v = *reinterpret_cast<const v4i*>(W + (int64_t)wrow * K + (k < K ? k : K - 16));
+            return k < K ? v : v4i{0, 0, 0, 0};
+        } else {
+            return load_chunk<false>(W, wrow, N, k, K);
+        }
+    };
+    auto xfrag = [&](int b, int c) -> v4i {
+        const int tok = b * 16 + r, k = c * 64 + g * 16;
+        if constexpr (KVEC) {
+            const int t = tok < M ? tok : M - 1;
+            const v4i v = *reinterpret_cast<const v4i*>(X + (int64_t)t * K + (k < K ? k : K - 16));
+            return (tok < M && k < K) ? v : v4i{0, 0, 0, 0};
+        } else {
+            return load_chunk<false>(X, tok, M, k, K);
+        }
+    };
+
+    v4i acc[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
+    v4i w0[U][4], w1[U][4];
+    load_stage<NW, U>(w0, wave, KG, wfrag);  // clamped: valid for any wave
+    stream_k<TB, NW, U>(acc, w0, w1, wave, nsteps, KG, wfrag, xfrag);
+    reduce_store<TB, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
+                            [&](int tok) { return sx[tok]; });
+}
+
+// Fragment-packed weights (K % 64 == 0): each weight fragment is one
+// contiguous, non-temporal 1 KB wave load.
+template <int TB, int NW, int U, Out O>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    __shared__ v4i red[NW][TB][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b0 = blockIdx.x, n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64, nsteps = (KG + 3) / 4;
+    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+
+    auto wfrag = [&](int c) -> v4i {
+        return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024));
+    };
+    auto xfrag = [&](int b, int c) -> v4i {
+        const int tok = b * 16 + r;
+        const int t = tok < M ? tok : M - 1, cc = c < KG ? c : KG - 1;
+        const v4i v = *reinterpret_cast<const v4i*>(X + (int64_t)t * K + cc * 64 + g * 16);
+        return (tok < M && c < KG) ? v : v4i{0, 0, 0, 0};
+    };
+
+    v4i acc[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
+    v4i w0[U][4], w1[U][4];
+    load_stage<NW, U>(w0, wave, KG, wfrag);  // clamped: valid for any wave
+    stream_k<TB, NW, U>(acc, w0, w1, wave, nsteps, KG, wfrag, xfrag);
+    reduce_store<TB, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
+                            [&](int tok) { return sx[tok]; });
+}
+
+// ---------------------------------------------------------------------------
+// Whole decode layer in one launch (M <= 4 tokens, packed weights).  Every
+// workgroup
+//  1) loads the activations (CPT 16-byte chunks per thread, into registers),
+//     then issues its first weight stage, so that waiting for the
+//     activations does not wait for the weights;
+//  2) takes each token's absmax (DPP row reduction, then across waves in
+//     LDS) -- the same maximum and the same quantiser as the standalone
+//     per-token kernel, so codes and steps are identical;
+//  3) writes the codes into LDS (workgroup 0 also stores xq and x_scale);
+//  4) streams its 16 output channels with the activation fragments read
+//     from LDS, one stage of two 256-byte steps per wave in flight.
+// LDS: M * K bytes of codes.
+constexpr int kFusedMaxM = 4;
+constexpr int kFusedMaxLds = 64 * 1024;
+constexpr int kFusedMaxCpt = 16;
+constexpr int kFusedU = 2;  // 256-byte K steps per stage in the one-call layer
+
+// Max over the 64 lanes (non-negative values): DPP rotations within each row
+// of 16 lanes, then the four row results through scalar registers.
+__device__ inline float wave_max_dpp(float v) {
+    int x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(x, 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(x, 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(x, 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(x, 48));
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
+}
+
+template <class D, int NW, int U, Out O, int CPT>
+__global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
+    const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,
+    const float* __restrict__ sw, int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
+    void* __restrict__ Y, int M, int N, int K) {
+    constexpr int NT = NW * 64, V = D::VEC, MM = kFusedMaxM;
+    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
+    __shared__ v4i red[NW][1][64];
+    __shared__ float rmax[MM][NW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b0 = blockIdx.x, n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64, nsteps = (KG + 3) / 4;
+    const int nch = K / V, TC = M * nch;  // 16-byte chunks of x
+    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+
+    // 1) activations first, then the first weight stage
+    uint4 xr[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int j = i * NT + tid;
+        xr[i] = j < TC ? *reinterpret_cast<const uint4*>(X + (int64_t)j * V) : make_uint4(0, 0, 0, 0);
+    }
+    auto wfrag = [&](int c) -> v4i {
+        return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024));
+    };
+    // unconditional (clamped) so that the wait for x below counts only x
+    v4i w[U][4];
+    load_stage<NW, U>(w, wave, KG, wfrag);
+
+    // 2) per-token absmax (x rows are contiguous: chunk j belongs to token j / nch)
+    float am[MM] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int j = i * NT + tid;
+        const int m = j < TC ? j / nch : MM;
+        const typename D::T* e = reinterpret_cast<const typename D::T*>(&xr[i]);
+        float a = 0.0f;
+#pragma unroll
+        for (int q = 0; q < V; ++q) a = __builtin_fmaxf(a, __builtin_fabsf(D::to_f32(e[q])));
+#pragma unroll
+        for (int mm = 0; mm < MM; ++mm)
+            if (m == mm) am[mm] = __builtin_fmaxf(am[mm], a);
+    }
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+        const float w = wave_max_dpp(am[mm]);
+        if (lane == 0) rmax[mm][wave] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+        float a = rmax[mm][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a = __builtin_fmaxf(a, rmax[mm][w]);
+        am[mm] = a;
+    }
+    // a token's absmax by selects (no dynamic register-array index, which
+    // would put am[] in scratch memory)
+    const float am0 = am[0], am1 = am[1], am2 = am[2], am3 = am[3];
+    auto absmax_of = [am0, am1, am2, am3](int m) {
+        return m == 0 ? am0 : (m == 1 ? am1 : (m == 2 ? am2 : am3));
+    };
+
+    // 3) codes into LDS (and xq, x_scale from workgroup 0)
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int j = i * NT + tid;
+        if (j < TC) {
+            const RowStep st = row_step(absmax_of(j / nch));
+            const typename D::T* e = reinterpret_cast<const typename D::T*>(&xr[i]);
+            int8_t q[V];
+            if (st.fast) {
+#pragma unroll
+                for (int k = 0; k < V; ++k) q[k] = (int8_t)quant_code<true>(D::to_f32(e[k]), st);
+            } else {
+#pragma unroll
+                for (int k = 0; k < V; ++k) q[k] = (int8_t)quant_code<false>(D::to_f32(e[k]), st);
+            }
+            if constexpr (V == 8) {
+                const uint2 p = *reinterpret_cast<const uint2*>(q);
+                *reinterpret_cast<uint2*>(xs + (int64_t)j * V) = p;
+                if (b0 == 0) *reinterpret_cast<uint2*>(xq_out + (int64_t)j * V) = p;
+            } else {
+                const uint32_t p = *reinterpret_cast<const uint32_t*>(q);
+                *reinterpret_cast<uint32_t*>(xs + (int64_t)j * V) = p;
+                if (b0 == 0) *reinterpret_cast<uint32_t*>(xq_out + (int64_t)j * V) = p;
+            }
+        }
+    }
+    if (b0 == 0 && tid < M) sx_out[tid] = quant_step(absmax_of(tid));
+    __syncthreads();
+
+    // 4) the weight stream
+    auto xfrag = [&](int, int c) -> v4i {
+        const int t = r < M ? r : M - 1, cc = c < KG ? c : KG - 1;
+        const v4i v = *reinterpret_cast<const v4i*>(xs + t * K + cc * 64 + g * 16);
+        return (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
+    };
+    // One stage of U steps in flight per wave, the next issued after the
+    // MFMAs of the current one: the first stage (all of a short K) was in
+    // flight during the quantisation, and the stage registers stay few.
+    v4i acc[1] = {v4i{0, 0, 0, 0}};
+    constexpr int S = NW * U;
+    for (int st = wave; st < nsteps; st += S) {
+        v4i x[U][1][4];
+        load_x<1, NW, U>(x, st, xfrag);
+        mfma_stage<1, U>(acc, w, x);
+        if (st + S < nsteps) load_stage<NW, U>(w, st + S, KG, wfrag);
+    }
+    const float sx_lane = quant_step(absmax_of(lane & 15));  // this lane's token
+    reduce_store<1, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
+                           [sx_lane](int) { return sx_lane; });
+}
+
+template <class D, Out O, int CPT>
+hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, int8_t* xq,
+                            float* sx, void* y, int M, int N, int K, hipStream_t s) {
+    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT>),
+                       dim3((unsigned)((N + 15) / 16)), dim3(kNW * 64), (size_t)M * K, s,
+                       static_cast<const typename D::T*>(x), wp, sw, xq, sx, y, M, N, K);
+    return hipGetLastError();
+}
+
+template <class D, Out O>
+hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
+                        void* y, int M, int N, int K, hipStream_t s) {
+    const int cpt = (M * (K / D::VEC) + kNW * 64 - 1) / (kNW * 64);
+    if (cpt <= 1) return launch_fused_cpt<D, O, 1>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 2) return launch_fused_cpt<D, O, 2>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 4) return launch_fused_cpt<D, O, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 8) return launch_fused_cpt<D, O, 8>(x, wp, sw, xq, sx, y, M, N, K, s);
+    return launch_fused_cpt<D, O, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+}
+
+// The one-kernel path applies: few tokens, codes fit the LDS budget, x fits
+// the per-thread register budget.
+bool fused_fits(Dt xdt, int64_t M, int64_t K) {
+    const int64_t vec = xdt == Dt::F32 ? 4 : 8;
+    return M <= kFusedMaxM && M * K <= kFusedMaxLds &&
+           M * (K / vec) <= (int64_t)kFusedMaxCpt * kNW * 64;
+}
+
+template <class D>
+hipError_t fused_out(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
+                     void* y, Out out, int M, int N, int K, hipStream_t s) {
+    switch (out) {
+        case Out::F16: return launch_fused<D, Out::F16>(x, wp, sw, xq, sx, y, M, N, K, s);
+        case Out::BF16: return launch_fused<D, Out::BF16>(x, wp, sw, xq, sx, y, M, N, K, s);
+        case Out::F32: return launch_fused<D, Out::F32>(x, wp, sw, xq, sx, y, M, N, K, s);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int TB, Out O>
+hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
+                     int N, int K, void* y, bool packed, hipStream_t s) {
+    const dim3 grid((unsigned)((N + 15) / 16)), block(kNW * 64);
+    if (packed)
+        hipLaunchKernelGGL((gemm_skinny_packed_kernel<TB, kNW, kU, O>), grid, block, 0, s, xq, w,
+                           sx, sw, y, M, N, K);
+    else if (K % 16 == 0)
+        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, true>), grid, block, 0, s, xq, w, sx,
+                           sw, y, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, false>), grid, block, 0, s, xq, w,
+                           sx, sw, y, M, N, K);
+    return hipGetLastError();
+}
+
+template <Out O>
+hipError_t skinny_out(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
+                      int N, int K, void* y, bool packed, hipStream_t s) {
+    if (M <= 16) return skinny_tb<1, O>(xq, sx, w, sw, M, N, K, y, packed, s);
+    if (M <= 32) return skinny_tb<2, O>(xq, sx, w, sw, M, N, K, y, packed, s);
+    if (M <= 48) return skinny_tb<3, O>(xq, sx, w, sw, M, N, K, y, packed, s);
+    return skinny_tb<4, O>(xq, sx, w, sw, M, N, K, y, packed, s);
+}
+
+}  // namespace
+
+hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s) {
+    switch (out) {
+        case Out::I32: return skinny_out<Out::I32>(xq, sx, w, sw, M, N, K, y, packed, s);
+        case Out::F16: return skinny_out<Out::F16>(xq, sx, w, sw, M, N, K, y, packed, s);
+        case Out::BF16: return skinny_out<Out::BF16>(xq, sx, w, sw, M, N, K, y, packed, s);
+        case Out::F32: return skinny_out<Out::F32>(xq, sx, w, sw, M, N, K, y, packed, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
+                                const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
+                                void* y, Out out, hipStream_t s) {
+    if (fused_fits(xdt, M, K)) {
+        const int m = (int)M, n = (int)N, k = (int)K;
+        switch (xdt) {
+            case Dt::F32: return fused_out<F32>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+            case Dt::F16: return fused_out<F16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+            case Dt::BF16: return fused_out<BF16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
+}
+
+}  // namespace sq

@@ -12,7 +12,8 @@
 // Both operands are K-contiguous ("TN"), the natural feed of the MFMA
 // matrix cores: every lane's 16-byte fragment is one contiguous load.
 //
-// Three kernels, chosen by the shape:
+// Kernels, chosen by the shape (M <= 64 tokens go to the few-token kernels of
+// sq_decode.hip):
 //  * dma (M > 64, K % 128 == 0): workgroup tile BM x BN; 128-byte K slices go
 //    from global memory straight into LDS (global_load_lds_dwordx4, no
 //    register staging), double-buffered, as XOR-swizzled 16-byte chunks
@@ -23,65 +24,17 @@
 //    that tiles sharing operand panels run on the same XCD's L2.
 //  * tiled (M > 64, other K): the same tiling with register-staged loads and
 //    byte-granular masking of the K tail.
-//  * packed variants of dma and skinny read the weights in a fragment-packed
-//    layout (see pack_weight_kernel) where every wave load of weights is one
-//    contiguous kilobyte, independent of K: with the row-major layout the 16
-//    rows of one skinny-kernel fragment lie K bytes apart, which for K a
-//    multiple of 16 KB puts them all on the same HBM channel.
-//  * skinny (M <= 64, the decode regime): the weight matrix is streamed once
-//    from HBM straight into MFMA fragments (no LDS staging); one workgroup
-//    per 16 output channels, its waves interleave over K in 256-byte steps,
-//    v_mfma_i32_16x16x64_i8 with the weights as the 16-row operand and up to
-//    four 16-token blocks of activations as the other; the waves' partial
-//    sums are added in LDS before the epilogue.
+//  * the packed variant of dma reads the weights in the fragment-packed
+//    layout (see pack_weight_kernel), which the few-token kernels need: there
+//    every wave load of weights is one contiguous kilobyte, independent of K.
 //
 // The MFMA sums over K inside one instruction in whatever order the hardware
 // takes; the A and B fragments give each lane the same K positions, so any
 // order yields the same integer sum.
-#include "sq_device.h"
-#include "sq_launch.h"
+#include "sq_gemm_common.h"
 
 namespace sq {
 namespace {
-
-__device__ inline float dequant(int acc, float sxm, float swn) {
-    float f = (float)acc;  // round to nearest even
-    f = f * sxm;
-    f = f * swn;
-    return f;
-}
-
-template <Out O>
-__device__ inline void store_out(void* y, int64_t idx, int acc, float sxm, float swn) {
-    if constexpr (O == Out::I32) {
-        static_cast<int*>(y)[idx] = acc;
-    } else if constexpr (O == Out::F32) {
-        static_cast<float*>(y)[idx] = dequant(acc, sxm, swn);
-    } else if constexpr (O == Out::F16) {
-        static_cast<_Float16*>(y)[idx] = (_Float16)dequant(acc, sxm, swn);
-    } else {
-        static_cast<uint16_t*>(y)[idx] = BF16::from_f32(dequant(acc, sxm, swn));
-    }
-}
-
-// 16 bytes of row r starting at column k of a row-major [R x K] int8 matrix;
-// zero outside the matrix.  KVEC: K % 16 == 0, so a chunk is wholly inside or
-// wholly outside and is one aligned 16-byte load.
-template <bool KVEC>
-__device__ inline v4i load_chunk(const int8_t* __restrict__ base, int r, int R, int k, int K) {
-    v4i z = {0, 0, 0, 0};
-    if (r >= R || k >= K) return z;
-    const int8_t* p = base + (int64_t)r * K + k;
-    if constexpr (KVEC) {
-        return *reinterpret_cast<const v4i*>(p);
-    } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (int b = 0; b < 16; ++b)
-            if (k + b < K) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
-        v4i v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-        return v;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Tiled kernel.
@@ -435,73 +388,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     }
 }
 
-// ---------------------------------------------------------------------------
-// Skinny kernel (M <= 16 * TB).
-template <int TB, int NW, Out O, bool KVEC>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
-    const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
-    constexpr int U = 2;  // 256-byte K steps in flight per wave
-    __shared__ v4i red[NW][TB][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 16;
-    const int r = lane & 15, g = lane >> 4;
-    const int nsteps = (K + 255) >> 8;
-
-    v4i acc[TB];
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
-
-    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
-        v4i wf[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kb = (st0 + u * NW) * 256;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                wf[u][t] = load_chunk<KVEC>(W, n0 + r, N, kb + t * 64 + g * 16, K);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kb = (st0 + u * NW) * 256;
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const v4i xf = load_chunk<KVEC>(X, b * 16 + r, M, kb + t * 64 + g * 16, K);
-                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc[b], 0, 0, 0);
-                }
-            }
-        }
-    }
-
-#pragma unroll
-    for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
-    __syncthreads();
-    if (threadIdx.x < TB * 64) {
-        const int b = wave;
-        v4i tot = red[0][b][lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) tot += red[w][b][lane];
-        // 16 x 16 accumulator layout: lane l, element q holds row 4*(l/16) + q
-        // (output channel) and column l%16 (token).
-        const int tok = b * 16 + (lane & 15);
-        if (tok < M) {
-            const float sxm = (O != Out::I32) ? sx[tok] : 0.0f;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int n = n0 + 4 * g + qq;
-                if (n < N) {
-                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
-                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
-                }
-            }
-        }
-    }
-}
-
-
-
 // Tile shape for the DMA kernel: 256x256 tiles (one workgroup per CU) when
 // there are enough of them to fill the GPU about one and a half times, else
 // 128x128 tiles (two workgroups per CU).  Larger tiles re-read fewer operand
@@ -542,271 +428,18 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const int8_t* __restri
     }
 }
 
-// Skinny kernel on packed weights (K % 64 == 0): as gemm_skinny_kernel, with
-// each weight fragment one contiguous, non-temporal 1 KB wave load.
-template <int TB, int NW, Out O>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
-    const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
-    constexpr int U = 2;
-    __shared__ v4i red[NW][TB][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int b0 = blockIdx.x;  // row block
-    const int n0 = b0 * 16;
-    const int r = lane & 15, g = lane >> 4;
-    const int KG = K / 64;
-    const int nsteps = (KG + 3) >> 2;  // 256-byte steps
-    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
-
-    v4i acc[TB];
-#pragma unroll
-    for (int b = 0; b < TB; ++b) acc[b] = v4i{0, 0, 0, 0};
-    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
-        v4i wf[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int c = (st0 + u * NW) * 4 + t;
-                wf[u][t] = c < KG ? __builtin_nontemporal_load(
-                                        reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024))
-                                  : v4i{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int b = 0; b < TB; ++b) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int c = (st0 + u * NW) * 4 + t;
-                    const int tok = b * 16 + r;
-                    const v4i xf = (c < KG && tok < M)
-                                       ? *reinterpret_cast<const v4i*>(X + (int64_t)tok * K + c * 64 + g * 16)
-                                       : v4i{0, 0, 0, 0};
-                    acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc[b], 0, 0, 0);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
-    __syncthreads();
-    if (threadIdx.x < TB * 64) {
-        const int b = wave;
-        v4i tot = red[0][b][lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) tot += red[w][b][lane];
-        const int tok = b * 16 + (lane & 15);
-        if (tok < M) {
-            const float sxm = (O != Out::I32) ? sx[tok] : 0.0f;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int n = n0 + 4 * g + qq;
-                if (n < N) {
-                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
-                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
-                }
-            }
-        }
-    }
-}
-
-
-// ---------------------------------------------------------------------------
-// Whole decode layer in one launch (M <= 4 tokens, packed weights): every
-// workgroup first issues its first weight loads, then -- while they are in
-// flight -- computes each token's absmax over K from x (the same reduction
-// and quantiser as the standalone per-token kernel, so the codes and steps are
-// identical), writes the codes into LDS, and streams its 16 output channels
-// as gemm_skinny_packed_kernel does, reading the activation fragments from
-// LDS.  Workgroup 0 also stores xq and x_scale.  LDS: M * K bytes.
-constexpr int kFusedMaxM = 4;
-constexpr int kFusedMaxLds = 64 * 1024;
-
-template <class D, int NW, Out O>
-__global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
-    const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,
-    const float* __restrict__ sw, int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
-    void* __restrict__ Y, int M, int N, int K) {
-    constexpr int U = 2, NT = NW * 64, V = D::VEC;
-    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
-    __shared__ v4i red[NW][64];
-    __shared__ float rmax[NW][kFusedMaxM];
-    __shared__ float steps[kFusedMaxM];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int b0 = blockIdx.x, n0 = b0 * 16;
-    const int r = lane & 15, g = lane >> 4;
-    const int KG = K / 64;
-    const int nsteps = (KG + 3) >> 2;
-    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
-
-    // 1) first weight loads in flight
-    v4i wf[U][4];
-    auto load_w = [&](int st0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int c = (st0 + u * NW) * 4 + t;
-                wf[u][t] = c < KG ? __builtin_nontemporal_load(
-                                        reinterpret_cast<const v4i*>(wblk + (int64_t)c * 1024))
-                                  : v4i{0, 0, 0, 0};
-            }
-    };
-    load_w(wave);
-
-    // 2) per-token absmax and codes
-    const int nch = K / V;
-    float amax[kFusedMaxM];
-#pragma unroll
-    for (int m = 0; m < kFusedMaxM; ++m) {
-        amax[m] = 0.0f;
-        if (m < M)
-            for (int ci = threadIdx.x; ci < nch; ci += NT) {
-                float v[V];
-                load_vec<D>(X + (int64_t)m * K + (int64_t)ci * V, v);
-#pragma unroll
-                for (int e = 0; e < V; ++e) amax[m] = __builtin_fmaxf(amax[m], __builtin_fabsf(v[e]));
-            }
-        amax[m] = wave_max(amax[m]);
-        if (lane == 0) rmax[wave][m] = amax[m];
-    }
-    __syncthreads();
-    if (threadIdx.x < kFusedMaxM) {
-        float a = rmax[0][threadIdx.x];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) a = __builtin_fmaxf(a, rmax[w][threadIdx.x]);
-        steps[threadIdx.x] = a;
-    }
-    __syncthreads();
-    for (int m = 0; m < M; ++m) {
-        const RowStep st = row_step(steps[m]);
-        if (b0 == 0 && threadIdx.x == 0) sx_out[m] = st.step;
-        for (int ci = threadIdx.x; ci < nch; ci += NT) {
-            float v[V];
-            load_vec<D>(X + (int64_t)m * K + (int64_t)ci * V, v);
-            int8_t q[V];
-            if (st.fast) {
-#pragma unroll
-                for (int e = 0; e < V; ++e) q[e] = (int8_t)quant_code<true>(v[e], st);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) q[e] = (int8_t)quant_code<false>(v[e], st);
-            }
-            int8_t* dst = xs + (int64_t)m * K + (int64_t)ci * V;
-            if constexpr (V == 8) {
-                *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(q);
-                if (b0 == 0) *reinterpret_cast<uint2*>(xq_out + (int64_t)m * K + (int64_t)ci * V) =
-                    *reinterpret_cast<const uint2*>(q);
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(q);
-                if (b0 == 0) *reinterpret_cast<uint32_t*>(xq_out + (int64_t)m * K + (int64_t)ci * V) =
-                    *reinterpret_cast<const uint32_t*>(q);
-            }
-        }
-    }
-    __syncthreads();
-
-    // 3) stream the weights
-    v4i acc = {0, 0, 0, 0};
-    for (int st0 = wave; st0 < nsteps; st0 += NW * U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int c = (st0 + u * NW) * 4 + t;
-                const v4i xf = (c < KG && r < M)
-                                   ? *reinterpret_cast<const v4i*>(xs + r * K + c * 64 + g * 16)
-                                   : v4i{0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[u][t], xf, acc, 0, 0, 0);
-            }
-        }
-        if (st0 + NW * U < nsteps) load_w(st0 + NW * U);
-    }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        v4i tot = red[0][lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) tot += red[w][lane];
-        const int tok = lane & 15;
-        if (tok < M) {
-            const float sxm = quant_step(steps[tok]);
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int n = n0 + 4 * g + qq;
-                if (n < N) store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, sw[n]);
-            }
-        }
-    }
-}
-
-template <class D, Out O>
-hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
-                        void* y, int M, int N, int K, hipStream_t s) {
-    constexpr int NW = 8;
-    const size_t lds = (size_t)M * K;
-    hipLaunchKernelGGL((linear_decode_fused_kernel<D, NW, O>), dim3((unsigned)((N + 15) / 16)),
-                       dim3(NW * 64), lds, s, static_cast<const typename D::T*>(x), wp, sw, xq,
-                       sx, y, M, N, K);
-    return hipGetLastError();
-}
-
-template <class D>
-hipError_t fused_out(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
-                     void* y, Out out, int M, int N, int K, hipStream_t s) {
-    switch (out) {
-        case Out::F16: return launch_fused<D, Out::F16>(x, wp, sw, xq, sx, y, M, N, K, s);
-        case Out::BF16: return launch_fused<D, Out::BF16>(x, wp, sw, xq, sx, y, M, N, K, s);
-        case Out::F32: return launch_fused<D, Out::F32>(x, wp, sw, xq, sx, y, M, N, K, s);
-        default: break;
-    }
-    return hipErrorInvalidValue;
-}
-
 template <Out O>
 hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t* wp,
                                 const float* sw, int M, int N, int K, void* y, hipStream_t s) {
-    if (M <= 64) {
-        constexpr int NW = 8;
-        const dim3 grid((unsigned)((N + 15) / 16)), block(NW * 64);
-        if (M <= 16)
-            hipLaunchKernelGGL((gemm_skinny_packed_kernel<1, NW, O>), grid, block, 0, s, xq, wp, sx,
-                               sw, y, M, N, K);
-        else if (M <= 32)
-            hipLaunchKernelGGL((gemm_skinny_packed_kernel<2, NW, O>), grid, block, 0, s, xq, wp, sx,
-                               sw, y, M, N, K);
-        else if (M <= 48)
-            hipLaunchKernelGGL((gemm_skinny_packed_kernel<3, NW, O>), grid, block, 0, s, xq, wp, sx,
-                               sw, y, M, N, K);
-        else
-            hipLaunchKernelGGL((gemm_skinny_packed_kernel<4, NW, O>), grid, block, 0, s, xq, wp, sx,
-                               sw, y, M, N, K);
-    } else {
-        return launch_dma<O, true>(xq, sx, wp, sw, M, N, K, y, s);
-    }
-    return hipGetLastError();
+    if (M <= 64) return launch_skinny(xq, sx, wp, sw, M, N, K, y, O, true, s);
+    return launch_dma<O, true>(xq, sx, wp, sw, M, N, K, y, s);
 }
 
 template <Out O, bool KVEC>
 hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                          int M, int N, int K, void* y, hipStream_t s) {
     if (M <= 64) {
-        constexpr int NW = 8;
-        const dim3 grid((unsigned)((N + 15) / 16)), block(NW * 64);
-        if (M <= 16)
-            hipLaunchKernelGGL((gemm_skinny_kernel<1, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
-                               sw, y, M, N, K);
-        else if (M <= 32)
-            hipLaunchKernelGGL((gemm_skinny_kernel<2, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
-                               sw, y, M, N, K);
-        else if (M <= 48)
-            hipLaunchKernelGGL((gemm_skinny_kernel<3, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
-                               sw, y, M, N, K);
-        else
-            hipLaunchKernelGGL((gemm_skinny_kernel<4, NW, O, KVEC>), grid, block, 0, s, xq, wq, sx,
-                               sw, y, M, N, K);
+        return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s);
     } else if (KVEC && K % 128 == 0) {
         return launch_dma<O, false>(xq, sx, wq, sw, M, N, K, y, s);
     } else {
@@ -849,23 +482,6 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
         case Out::F32: return gemm_packed_dispatch<Out::F32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
     }
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
-                                const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
-                                void* y, Out out, hipStream_t s) {
-    if (M <= kFusedMaxM && M * K <= kFusedMaxLds) {
-        const int m = (int)M, n = (int)N, k = (int)K;
-        switch (xdt) {
-            case Dt::F32: return fused_out<F32>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-            case Dt::F16: return fused_out<F16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-            case Dt::BF16: return fused_out<BF16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-        }
-        return hipErrorInvalidValue;
-    }
-    hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s);
-    if (e != hipSuccess) return e;
-    return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,

@@ -1,0 +1,49 @@
+// sq_gemm_common.h -- device helpers shared by the GEMM kernels (internal):
+// the scale-back epilogue and masked 16-byte operand loads.
+#pragma once
+
+#include "sq_device.h"
+#include "sq_launch.h"
+
+namespace sq {
+
+__device__ inline float dequant(int acc, float sxm, float swn) {
+    float f = (float)acc;  // round to nearest even
+    f = f * sxm;
+    f = f * swn;
+    return f;
+}
+
+template <Out O>
+__device__ inline void store_out(void* y, int64_t idx, int acc, float sxm, float swn) {
+    if constexpr (O == Out::I32) {
+        static_cast<int*>(y)[idx] = acc;
+    } else if constexpr (O == Out::F32) {
+        static_cast<float*>(y)[idx] = dequant(acc, sxm, swn);
+    } else if constexpr (O == Out::F16) {
+        static_cast<_Float16*>(y)[idx] = (_Float16)dequant(acc, sxm, swn);
+    } else {
+        static_cast<uint16_t*>(y)[idx] = BF16::from_f32(dequant(acc, sxm, swn));
+    }
+}
+
+// 16 bytes of row r starting at column k of a row-major [R x K] int8 matrix;
+// zero outside the matrix.  KVEC: K % 16 == 0, so a chunk is wholly inside or
+// wholly outside and is one aligned 16-byte load.
+template <bool KVEC>
+__device__ inline v4i load_chunk(const int8_t* __restrict__ base, int r, int R, int k, int K) {
+    v4i z = {0, 0, 0, 0};
+    if (r >= R || k >= K) return z;
+    const int8_t* p = base + (int64_t)r * K + k;
+    if constexpr (KVEC) {
+        return *reinterpret_cast<const v4i*>(p);
+    } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int b = 0; b < 16; ++b)
+            if (k + b < K) w[b >> 2] |= (uint32_t)(uint8_t)p[b] << (8 * (b & 3));
+        v4i v = {(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        return v;
+    }
+}
+
+}  // namespace sq

@@ -32,6 +32,10 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                               Out out, hipStream_t s);
 
+// Few-token GEMM (M <= 64): row-major or fragment-packed weights.
+hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
+                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s);
+
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
                                 void* y, Out out, hipStream_t s);
