@@ -181,7 +181,14 @@ template <> struct Half<Out::BF16> {
     __device__ static T cvt(float f) { return BF16::from_f32(f); }
 };
 
-template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1>
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ inline void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1,
+          int NSTAGE = 2>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
@@ -196,7 +203,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     constexpr bool HALF_OUT = (O == Out::F16 || O == Out::BF16);
     constexpr int EPI_LD = BN * 2 + 16;  // staged output row pitch (bytes): padded, 16-byte aligned
     constexpr int EPI = HALF_OUT ? BM * EPI_LD : 0;
-    constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+    constexpr int SMEM = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 operand stages");
     __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -268,14 +277,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][i][r] = 0;
 
+    // NSTAGE operand stages in a ring: tiles kt+1 .. kt+NSTAGE-2 stay in
+    // flight while tile kt is multiplied, and tile kt+NSTAGE-1 is issued into
+    // the stage that tile kt-1 used.
     const int nk = K / BK;
-    issue(0, 0);
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+        if (p < nk) issue(p, p * BK);
+    int cur = 0;  // stage of tile kt
     for (int kt = 0; kt < nk; ++kt) {
-        // This wave's loads of tile kt have landed; after the barrier every
-        // wave's have, and every wave is done reading the other stage.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // This wave's loads of tile kt have landed (loads complete in order,
+        // so only the later tiles' may be outstanding); after the barrier
+        // every wave's have, and every wave is done reading tile kt-1.
+        const int ahead = nk - 1 - kt;  // tiles issued after tile kt, capped below
+        if (NSTAGE >= 4 && ahead >= 2)
+            wait_vm<2 * INS>();
+        else if (NSTAGE >= 3 && ahead >= 1)
+            wait_vm<INS>();
+        else
+            wait_vm<0>();
         asm volatile("s_barrier" ::: "memory");
-        const int8_t* sA = smem + (kt & 1) * STAGE;
+        const int8_t* sA = smem + cur * STAGE;
         const int8_t* sB = sA + BM * BK;
         v4i af[2][TM], bf[2][TN];
 #pragma unroll
@@ -284,7 +306,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             bf[0][j] = *reinterpret_cast<const v4i*>(sB + boff(wn0 + j * 32 + (lane & 31), lane >> 5));
-        if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * BK);
+        {
+            const int nxt = kt + NSTAGE - 1;
+            int nbuf = cur + NSTAGE - 1;
+            nbuf = nbuf >= NSTAGE ? nbuf - NSTAGE : nbuf;
+            if (nxt < nk) issue(nbuf, nxt * BK);
+        }
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             const int cb = s & 1, nb = cb ^ 1;
@@ -305,6 +332,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                     acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
         }
         __builtin_amdgcn_iglp_opt(0);  // interleave the LDS reads with the MFMAs
+        cur = cur + 1 == NSTAGE ? 0 : cur + 1;
     }
 
     // Epilogue.  Sub-tile (j, i), lane l: token m = i*32 + l%32; elements
@@ -388,20 +416,70 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     }
 }
 
-// Tile shape for the DMA kernel: 256x256 tiles (one workgroup per CU) when
-// there are enough of them to fill the GPU about one and a half times, else
-// 128x128 tiles (two workgroups per CU).  Larger tiles re-read fewer operand
-// bytes, which decides once the weights no longer fit the Infinity Cache.
+// Tile shape for the DMA kernel.  A launch runs in rounds of (CUs x
+// workgroups per CU) tiles; a partial last round leaves CUs idle, so the
+// shape is chosen to minimise
+//     rounds * (tile area * workgroups per CU) / efficiency,
+// the time of the rounds in units of one CU's work on a 256 x 256 tile.
+// Candidates: 256 x 256 (BK 64, four operand stages), 256 x 192 (BK 128,
+// two stages; 512 tiles make exactly two rounds of the 2048 x 12288 QKV
+// shape that 256 x 256 covers in one and a half), 128 x 128 (two per CU).
+// The efficiencies are measured relative throughputs per unit of tile area
+// on whole rounds.
+struct TileCfg {
+    int bm, bn, per_cu;
+    double eff;
+};
+constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.95}, {128, 128, 2, 0.90}};
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int pick_tile(int M, int N) {
+    const int cus = cu_count();
+    int best = 0;
+    double best_cost = 0.0;
+    for (int c = 0; c < 3; ++c) {
+        const TileCfg& t = kTiles[c];
+        const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        const int64_t slots = (int64_t)cus * t.per_cu;
+        const int64_t rounds = (tiles + slots - 1) / slots;
+        const double cost = (double)rounds * t.bm * t.bn * t.per_cu / t.eff;
+        if (c == 0 || cost < best_cost) {
+            best = c;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <Out O, bool PACKED>
 hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
                       int N, int K, void* y, hipStream_t s) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (tiles(256, 256) >= 384) {
-        hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 64, O, PACKED>), dim3(tiles(256, 256)),
-                           dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
-    } else {
-        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2>),
-                           dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
+    switch (pick_tile(M, N)) {
+        case 0:
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 64, 128, 64, O, PACKED, 1, 4>),
+                               dim3(tiles(256, 256)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
+            break;
+        case 1:
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 192, 128, 64, 96, O, PACKED, 1, 2>),
+                               dim3(tiles(256, 192)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2>),
+                               dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
+            break;
     }
     return hipGetLastError();
 }
