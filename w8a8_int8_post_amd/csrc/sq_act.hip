@@ -71,15 +71,44 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
     const bool live = m < M;
     const typename D::T* row = x + (live ? m : 0) * K;
     const int64_t nch = K / V;
+    // All of the lane's loads are issued before any is used, as straight-line
+    // code from clamped addresses (a conditional load would make the compiler
+    // wait for each load before the next is issued); pieces past the row end
+    // are left out of the maximum and are not stored.
+    uint4 raw[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+        raw[c] = *reinterpret_cast<const uint4*>(row + (ci < nch ? ci : nch - 1) * V);
+    }
+    float4 sm[NCH][V / 4];
+    if constexpr (SMOOTH) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            const float* sp = smooth + (ci < nch ? ci : nch - 1) * V;
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q) sm[c][q] = *reinterpret_cast<const float4*>(sp + 4 * q);
+        }
+    }
     float v[NCH][V];
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
-        if (live && ci < nch) {
-            load_smoothed<D, SMOOTH>(row + ci * V, smooth, ci * V, v[c]);
+        const typename D::T* e = reinterpret_cast<const typename D::T*>(&raw[c]);
 #pragma unroll
-            for (int e = 0; e < V; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][e]));
+        for (int q = 0; q < V; ++q) {
+            v[c][q] = D::to_f32(e[q]);
+            if constexpr (SMOOTH) {
+                const float4 s4 = sm[c][q / 4];
+                const float sq = (q & 3) == 0 ? s4.x : (q & 3) == 1 ? s4.y : (q & 3) == 2 ? s4.z : s4.w;
+                v[c][q] = v[c][q] / sq;
+            }
+        }
+        if (ci < nch) {
+#pragma unroll
+            for (int q = 0; q < V; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][q]));
         }
     }
     amax = wave_max(amax);
