@@ -364,28 +364,28 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             const int m = m0 + wm0 + i * 32 + (lane & 31);
             sxv[i] = m < M ? sx[m] : 0.0f;
         }
-        float4 swv[TN][4];
+        asm volatile("s_barrier" ::: "memory");  // all waves are done with the operand stages
+        // One 32-channel column block at a time, so that only its scales
+        // (four float4) are live next to the accumulators.
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
+            float4 swv[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
                 if (n + 3 < N)
-                    swv[j][g] = *reinterpret_cast<const float4*>(sw + n);  // n % 4 == 0
+                    swv[g] = *reinterpret_cast<const float4*>(sw + n);  // n % 4 == 0
                 else
-                    swv[j][g] = make_float4(n < N ? sw[n] : 0.f, n + 1 < N ? sw[n + 1] : 0.f,
-                                            n + 2 < N ? sw[n + 2] : 0.f, 0.f);
+                    swv[g] = make_float4(n < N ? sw[n] : 0.f, n + 1 < N ? sw[n + 1] : 0.f,
+                                         n + 2 < N ? sw[n + 2] : 0.f, 0.f);
             }
-        asm volatile("s_barrier" ::: "memory");  // all waves are done with the operand stages
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int ml = wm0 + i * 32 + (lane & 31);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int i = 0; i < TM; ++i) {
+                const int ml = wm0 + i * 32 + (lane & 31);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int nl = wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
-                    const float4 w4 = swv[j][g];
+                    const float4 w4 = swv[g];
                     T o[4];
                     o[0] = Half<O>::cvt(dequant(acc[j][i][4 * g + 0], sxv[i], w4.x));
                     o[1] = Half<O>::cvt(dequant(acc[j][i][4 * g + 1], sxv[i], w4.y));
@@ -394,6 +394,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                     *reinterpret_cast<uint2*>(smem + ml * EPI_LD + nl * 2) =
                         *reinterpret_cast<const uint2*>(o);
                 }
+            }
         }
         __syncthreads();
         // Write-out: 16 bytes (8 outputs) of one row per thread per step.
@@ -421,16 +422,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 // shape is chosen to minimise
 //     rounds * (tile area * workgroups per CU) / efficiency,
 // the time of the rounds in units of one CU's work on a 256 x 256 tile.
-// Candidates: 256 x 256 (BK 64, four operand stages), 256 x 192 (BK 128,
-// two stages; 512 tiles make exactly two rounds of the 2048 x 12288 QKV
-// shape that 256 x 256 covers in one and a half), 128 x 128 (two per CU).
+// Candidates: 256 x 256 (four waves, one per SIMD, each a 128 x 128
+// register tile: a third fewer LDS fragment bytes per MFMA than eight waves
+// of 128 x 64), 256 x 192 (eight waves of 64 x 96; 512 tiles make exactly
+// two rounds of the 2048 x 12288 QKV shape that 256 x 256 covers in one and
+// a half), 128 x 128 (two per CU).  All use BK 128 and two operand stages.
 // The efficiencies are measured relative throughputs per unit of tile area
 // on whole rounds.
 struct TileCfg {
     int bm, bn, per_cu;
     double eff;
 };
-constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.95}, {128, 128, 2, 0.90}};
+constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.85}, {128, 128, 2, 0.82}};
 
 int cu_count() {
     static int cached[64] = {0};
@@ -469,8 +472,8 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     switch (pick_tile(M, N)) {
         case 0:
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 64, 128, 64, O, PACKED, 1, 4>),
-                               dim3(tiles(256, 256)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2>),
+                               dim3(tiles(256, 256)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
             break;
         case 1:
             hipLaunchKernelGGL((gemm_dma_kernel<256, 192, 128, 64, 96, O, PACKED, 1, 2>),
