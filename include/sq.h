@@ -167,10 +167,10 @@ sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int
 
 /* The whole run-time layer on packed weights: per-token quantisation of x
  * (exactly sq_quant_act_pertoken with smooth = NULL, writing xq and x_scale)
- * followed by sq_w8a8_gemm_dequant_packed, in one call.  For M <= 4,
- * M * K <= 65536 and M * K * (element size of x) <= 131072 the two steps run
- * as one kernel (every workgroup quantises the few tokens itself while its
- * first weight loads are in flight); other shapes take two launches.  x: [M x K] of dtype xdt; xq: int8 [M x K];
+ * followed by sq_w8a8_gemm_dequant_packed, in one call.  For M <= 16 and
+ * M * K <= 32768 the two steps run as one kernel (every workgroup quantises
+ * the few tokens itself while its first weight loads are in flight); other
+ * shapes take two launches.  x: [M x K] of dtype xdt; xq: int8 [M x K];
  * x_scale: fp32 [M]; wq_packed as above; w_scale: fp32 [N]; y: [M x N] of
  * ydt.  K % 128 == 0.  xq and x_scale are written in both cases. */
 sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t K,

@@ -250,13 +250,15 @@ def test_gemm_packed(ref, dev, M, N, K):
 # ------------------------------------------- whole run-time layer (packed)
 
 LINEAR_CASES = [
-    # M <= 4 and M * K <= 65536: one fused kernel
+    # M <= 16 and M * K <= 32768: one fused kernel (4 token slots up to M = 4, else 16)
     (1, 37, 128, "f16", "f16"), (2, 4099, 4096, "bf16", "bf16"), (3, 300, 1024, "f32", "f32"),
-    (4, 12288, 4096, "f16", "f16"), (4, 1000, 16384, "f16", "f32"),
+    (4, 12288, 4096, "f16", "f16"), (2, 700, 16384, "f16", "f32"),
     (1, 512, 28672, "bf16", "f16"),
+    (5, 300, 1024, "f16", "f16"), (8, 300, 2048, "bf16", "f32"), (16, 4099, 2048, "f16", "f16"),
+    (13, 1000, 2048, "f32", "bf16"),
     # two launches: quantiser then the packed GEMM
-    (4, 200, 16512, "f16", "f16"), (5, 300, 1024, "f16", "f16"), (64, 600, 2048, "f16", "bf16"),
-    (300, 513, 2048, "bf16", "f16"),
+    (4, 1000, 16384, "f16", "f32"), (4, 200, 16512, "f16", "f16"), (16, 200, 4096, "f16", "f16"),
+    (17, 300, 1024, "f16", "f16"), (64, 600, 2048, "f16", "bf16"), (300, 513, 2048, "bf16", "f16"),
 ]
 
 
@@ -290,13 +292,17 @@ def test_linear_packed(ref, dev, M, N, K, xdt, ydt):
     _linear_check(ref, dev, x, wq, ydt)
 
 
-def test_linear_packed_special_rows(ref, dev):
-    # a zero row (step 0), a subnormal step, a step above 2^96 (IEEE division
-    # path) and an ordinary row, through the fused kernel
+@pytest.mark.parametrize("M", [4, 12])
+def test_linear_packed_special_rows(ref, dev, M):
+    # zero rows (step 0), subnormal steps, steps above 2^96 (IEEE division
+    # path) and ordinary rows, through the fused kernel (4 and 16 token slots).
+    # 1e31 puts the step above 2^96 while fp32(acc) * step stays finite (the
+    # scale-back multiplies in fp32, the oracle in double).
     K = 256
-    x = torch.from_numpy((np.random.default_rng(6).standard_normal((4, K)) *
-                          np.array([[0.0], [1e-40], [1e35], [1.0]])).astype(np.float32))
-    _, wq = _codes(4, 100, K, 11)
+    scale = np.array([0.0, 1e-40, 1e31, 1.0] * (M // 4))[:, None]
+    x = torch.from_numpy((np.random.default_rng(6 + M).standard_normal((M, K)) * scale)
+                         .astype(np.float32))
+    _, wq = _codes(M, 100, K, 11)
     _linear_check(ref, dev, x, wq, "f32")
 
 

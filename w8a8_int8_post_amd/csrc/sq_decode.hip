@@ -208,20 +208,25 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Whole decode layer in one launch (M <= 4 tokens, packed weights).  Every
+// Whole decode layer in one launch (M <= 16 tokens, packed weights).  Every
 // workgroup
 //  1) loads the activations (CPT 16-byte chunks per thread, into registers),
 //     then issues its first weight stage, so that waiting for the
 //     activations does not wait for the weights;
 //  2) takes each token's absmax (DPP row reduction, then across waves in
-//     LDS) -- the same maximum and the same quantiser as the standalone
-//     per-token kernel, so codes and steps are identical;
+//     LDS; MM = 4 or 16 token slots) -- the same maximum and the same
+//     quantiser as the standalone per-token kernel, so codes and steps are
+//     identical;
 //  3) writes the codes into LDS (workgroup 0 also stores xq and x_scale);
 //  4) streams its 16 output channels with the activation fragments read
 //     from LDS, one stage of two 256-byte steps per wave in flight.
 // LDS: M * K bytes of codes.
-constexpr int kFusedMaxM = 4;
-constexpr int kFusedMaxLds = 64 * 1024;
+constexpr int kFusedMaxM = 16;
+// Every workgroup quantises all M x K activations itself, which pays off
+// only while that work is small next to streaming the workgroup's weights
+// (measured: 16 x 4096 tokens x channels took 4x longer fused than as two
+// launches; 1 x 28672 and 4 x 8192 are faster fused).
+constexpr int kFusedMaxLds = 32 * 1024;
 constexpr int kFusedMaxCpt = 16;
 constexpr int kFusedU = 2;  // 256-byte K steps per stage in the one-call layer
 
@@ -244,15 +249,16 @@ __device__ inline float wave_max_dpp(float v) {
     return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
-template <class D, int NW, int U, Out O, int CPT>
+template <class D, int NW, int U, Out O, int CPT, int MM>
 __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,
     const float* __restrict__ sw, int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
     void* __restrict__ Y, int M, int N, int K) {
-    constexpr int NT = NW * 64, V = D::VEC, MM = kFusedMaxM;
+    constexpr int NT = NW * 64, V = D::VEC;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
     __shared__ v4i red[NW][1][64];
     __shared__ float rmax[MM][NW];
+    __shared__ float smax[MM];  // per-token absmax
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b0 = blockIdx.x, n0 = b0 * 16;
@@ -276,7 +282,9 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     load_stage<NW, U>(w, wave, KG, wfrag);
 
     // 2) per-token absmax (x rows are contiguous: chunk j belongs to token j / nch)
-    float am[MM] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float am[MM];
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) am[mm] = 0.0f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int j = i * NT + tid;
@@ -295,19 +303,16 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
         if (lane == 0) rmax[mm][wave] = w;
     }
     __syncthreads();
+    if (tid < MM) {
+        float a = rmax[tid][0];
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-        float a = rmax[mm][0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) a = __builtin_fmaxf(a, rmax[mm][w]);
-        am[mm] = a;
+        for (int w = 1; w < NW; ++w) a = __builtin_fmaxf(a, rmax[tid][w]);
+        smax[tid] = a;
     }
-    // a token's absmax by selects (no dynamic register-array index, which
-    // would put am[] in scratch memory)
-    const float am0 = am[0], am1 = am[1], am2 = am[2], am3 = am[3];
-    auto absmax_of = [am0, am1, am2, am3](int m) {
-        return m == 0 ? am0 : (m == 1 ? am1 : (m == 2 ? am2 : am3));
-    };
+    __syncthreads();
+    // a token's absmax from LDS (a runtime index into a register array would
+    // put the array in scratch memory)
+    auto absmax_of = [&](int m) { return smax[m]; };
 
     // 3) codes into LDS (and xq, x_scale from workgroup 0)
 #pragma unroll
@@ -355,15 +360,16 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
         mfma_stage<1, U>(acc, w, x);
         if (st + S < nsteps) load_stage<NW, U>(w, st + S, KG, wfrag);
     }
-    const float sx_lane = quant_step(absmax_of(lane & 15));  // this lane's token
+    const int tok = lane & 15;  // this lane's token (stored only if < M)
+    const float sx_lane = quant_step(tok < MM ? absmax_of(tok) : 0.0f);
     reduce_store<1, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
                            [sx_lane](int) { return sx_lane; });
 }
 
-template <class D, Out O, int CPT>
+template <class D, Out O, int CPT, int MM>
 hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, int8_t* xq,
                             float* sx, void* y, int M, int N, int K, hipStream_t s) {
-    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT>),
+    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT, MM>),
                        dim3((unsigned)((N + 15) / 16)), dim3(kNW * 64), (size_t)M * K, s,
                        static_cast<const typename D::T*>(x), wp, sw, xq, sx, y, M, N, K);
     return hipGetLastError();
@@ -373,15 +379,21 @@ template <class D, Out O>
 hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
                         void* y, int M, int N, int K, hipStream_t s) {
     const int cpt = (M * (K / D::VEC) + kNW * 64 - 1) / (kNW * 64);
-    if (cpt <= 1) return launch_fused_cpt<D, O, 1>(x, wp, sw, xq, sx, y, M, N, K, s);
-    if (cpt <= 2) return launch_fused_cpt<D, O, 2>(x, wp, sw, xq, sx, y, M, N, K, s);
-    if (cpt <= 4) return launch_fused_cpt<D, O, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
-    if (cpt <= 8) return launch_fused_cpt<D, O, 8>(x, wp, sw, xq, sx, y, M, N, K, s);
-    return launch_fused_cpt<D, O, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (M <= 4) {
+        if (cpt <= 1) return launch_fused_cpt<D, O, 1, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+        if (cpt <= 2) return launch_fused_cpt<D, O, 2, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+        if (cpt <= 4) return launch_fused_cpt<D, O, 4, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+        if (cpt <= 8) return launch_fused_cpt<D, O, 8, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+        return launch_fused_cpt<D, O, 16, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+    }
+    if (cpt <= 2) return launch_fused_cpt<D, O, 2, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 4) return launch_fused_cpt<D, O, 4, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 8) return launch_fused_cpt<D, O, 8, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+    return launch_fused_cpt<D, O, 16, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
 }
 
-// The one-kernel path applies: few tokens, codes fit the LDS budget, x fits
-// the per-thread register budget.
+// The one-kernel path applies: few tokens, M * K within the redundant-work
+// (and LDS) budget, x within the per-thread register budget.
 bool fused_fits(Dt xdt, int64_t M, int64_t K) {
     const int64_t vec = xdt == Dt::F32 ? 4 : 8;
     return M <= kFusedMaxM && M * K <= kFusedMaxLds &&
