@@ -68,6 +68,10 @@ def _load():
         lib.sqref_quantize_vector.restype = ctypes.c_float
         lib.sqref_quant_act_pertoken.argtypes = [P, I, I, P, P]
         lib.sqref_quant_weight_perchannel.argtypes = [P, I, I, P, P]
+        lib.sqref_quant_act_pertensor.argtypes = [P, I, I, P, P, P]
+        lib.sqref_static_act_step.argtypes = [P, P, I]
+        lib.sqref_static_act_step.restype = ctypes.c_float
+        lib.sqref_quant_weight_pertensor.argtypes = [P, I, I, P, P]
         lib.sqref_gemm_i32.argtypes = [P, P, I, I, I, P]
         lib.sqref_gemm_i32.restype = ctypes.c_int
         lib.sqref_gemm_i32_sampled.argtypes = [P, P, I, P, I, P, I, P]
@@ -182,6 +186,36 @@ def quant_act_pertoken(x_hat):
     sx = np.empty(M, np.float32)
     _load().sqref_quant_act_pertoken(_ptr(x), M, K, _ptr(xq), _ptr(sx))
     return xq, sx
+
+
+def quant_act_pertensor(x_hat, step_in=None):
+    """(Xq int8 [M x K], sx float32 [M]) with one step for the whole tensor:
+    dynamic (absmax / 127) when step_in is None, else the given static step."""
+    x = _f32(x_hat)
+    M, K = x.shape
+    xq = np.empty((M, K), np.int8)
+    sx = np.empty(M, np.float32)
+    st = None if step_in is None else np.array([step_in], np.float32)
+    _load().sqref_quant_act_pertensor(_ptr(x), M, K, None if st is None else _ptr(st),
+                                     _ptr(xq), _ptr(sx))
+    return xq, sx
+
+
+def static_act_step(a, s) -> np.float32:
+    """O3 step from the calibration maxima a and the smoothing factors s."""
+    a = _f32(a)
+    s = _f32(s)
+    return np.float32(_load().sqref_static_act_step(_ptr(a), _ptr(s), a.shape[0]))
+
+
+def quant_weight_pertensor(w_hat):
+    """(Wq int8 [N x K], sw float32 [N]) from W_hat [K x N], one step."""
+    w = _f32(w_hat)
+    K, N = w.shape
+    wq = np.empty((N, K), np.int8)
+    sw = np.empty(N, np.float32)
+    _load().sqref_quant_weight_pertensor(_ptr(w), K, N, _ptr(wq), _ptr(sw))
+    return wq, sw
 
 
 def quant_weight_perchannel(w_hat):

@@ -7,7 +7,9 @@ oracle in ``sqref.c``:
   integer arithmetic, so no int8 wrap-around);
 * the symmetric quantiser with fp32 division done by numpy float32 scalars
   and the half-away-from-zero rounding done exactly in Python's double
-  (``floor(|t| + 0.5)`` is exact in double for an fp32 ``t``).
+  (``floor(|t| + 0.5)`` is exact in double for an fp32 ``t``), with the step
+  either taken from the values' own range or given (a static step, where the
+  clamp to +-127 becomes active).
 
 P1 = abeam.tech SmoothQuant explainer (用語解説 "INT8 GEMM"; 推論方法 O1);
 P4 = blogs.itmedia.co.jp 量子化 blog, section 3 (range -> scale -> round).
@@ -47,3 +49,15 @@ def quantize_vector(values):
         q = round_half_away(t)
         codes.append(max(-127, min(127, q)))
     return codes, step
+
+
+def quantize_with_step(values, step):
+    """Codes for a given fp32 step: round half away from zero, clamp +-127."""
+    step = np.float32(step)
+    if step == 0:
+        return [0] * len(values)
+    codes = []
+    for v in values:
+        t = float(np.float32(np.float32(v) / step))
+        codes.append(max(-127, min(127, round_half_away(t))))
+    return codes

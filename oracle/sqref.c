@@ -15,7 +15,9 @@
  *        and the offline fold), なぜ活性値が量子化しづらいのか (range set by
  *        the max absolute value), smoothing factor はどう決めるのか (equation
  *        for s_j and alpha), 学習方法 (calibrate -> s -> quantize),
- *        推論方法 (O1: per-token activations, dynamic).
+ *        推論方法 (O1: per-token activations, dynamic; O2: per-tensor,
+ *        dynamic; O3: per-tensor, static), 課題 (static scales come from
+ *        calibration data).
  *   [P4] blogs.itmedia.co.jp, 「LLMのダイエット術、『量子化（Quantization）』」,
  *        section 3 「レイヤーごとのマッピング」 (range -> scale -> round to the
  *        nearest representable value; scale back at inference; worked
@@ -173,6 +175,67 @@ void sqref_quant_weight_perchannel(const float* w_hat, int64_t K, int64_t N, int
 {
     for (int64_t n = 0; n < N; ++n)
         sw[n] = sqref_quantize_vector(w_hat + n, K, N, wq + n * K, 1);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Per-tensor activation quantisation [P1 推論方法: O2 quantises activations
+ * per tensor, dynamically; O3 per tensor, statically].  One step for the
+ * whole X_hat[M x K]:
+ *   step_in == NULL (O2): step = max over all |x_hat| / 127, as for a token
+ *                          but over the whole tensor;
+ *   step_in != NULL (O3): step = *step_in, fixed offline from calibration
+ *                          data, so values beyond the calibrated range reach
+ *                          the clamp at +-127.
+ * The codes follow the same quantiser; sx[m] = step for every row, the form
+ * the scale-back takes. */
+void sqref_quant_act_pertensor(const float* x_hat, int64_t M, int64_t K, const float* step_in,
+                               int8_t* xq, float* sx)
+{
+    float step;
+    if (step_in) {
+        step = *step_in;
+    } else {
+        float m = 0.0f;
+        for (int64_t i = 0; i < M * K; ++i) {
+            float a = fabsf(x_hat[i]);
+            if (a > m) m = a;
+        }
+        step = sqref_step(m);
+    }
+    for (int64_t i = 0; i < M * K; ++i) xq[i] = sqref_quantize_value(x_hat[i], step);
+    for (int64_t m = 0; m < M; ++m) sx[m] = step;
+}
+
+/* The static per-tensor step of O3 [P1 推論方法; 課題 (activation scales are
+ * estimated from calibration data)]: the largest |x_hat| the calibration set
+ * produces, over 127.  x_hat = x / s_j per channel and the fp32 division is
+ * monotone, so the largest calibration |x_hat| in channel j is a_j / s_j:
+ *   step = max_j (a_j / s_j) / 127. */
+float sqref_static_act_step(const float* a, const float* s, int64_t K)
+{
+    float m = 0.0f;
+    for (int64_t j = 0; j < K; ++j) {
+        float v = a[j] / s[j];
+        if (v > m) m = v;
+    }
+    return sqref_step(m);
+}
+
+/* Per-tensor weight quantisation [P1 推論方法: O1-O3 quantise the weights
+ * per tensor]: one step = max over all |W_hat| / 127; codes stored as
+ * Wq[N x K] like the per-channel case, sw[n] = step for every channel. */
+void sqref_quant_weight_pertensor(const float* w_hat, int64_t K, int64_t N, int8_t* wq, float* sw)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < K * N; ++i) {
+        float a = fabsf(w_hat[i]);
+        if (a > m) m = a;
+    }
+    float step = sqref_step(m);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) wq[n * K + k] = sqref_quantize_value(w_hat[k * N + n], step);
+        sw[n] = step;
+    }
 }
 
 /* ---------------------------------------------------------------------- */

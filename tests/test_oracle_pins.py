@@ -323,3 +323,81 @@ def test_synth_outliers_persist():
         col = np.abs(x).max(axis=0)
         assert set(np.argsort(col)[-5:]) == set(idx.tolist())
     assert not np.array_equal(xc[:16], xe)
+
+
+# --------------------------------------------------------------------------
+# Per-tensor variants (P1 推論方法: O2 per-tensor dynamic, O3 per-tensor static)
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pertensor_dynamic_is_one_range_for_the_tensor(ref, seed):
+    r = np.random.default_rng([11, seed])
+    x = (r.standard_normal((5, 37)) * np.array([[0.1], [1.0], [3.0], [0.01], [7.0]])).astype(np.float32)
+    xq, sx = ref.quant_act_pertensor(x)
+    qb, stb = brute.quantize_vector(x.ravel())
+    assert (sx == stb).all()
+    assert xq.ravel().tolist() == qb
+
+
+def test_pertensor_dynamic_single_row_is_pertoken(ref):
+    x = np.random.default_rng(12).standard_normal((1, 300)).astype(np.float32)
+    xq, sx = ref.quant_act_pertensor(x)
+    xq_t, sx_t = ref.quant_act_pertoken(x)
+    assert (xq == xq_t).all() and (sx == sx_t).all()
+
+
+def test_pertensor_static_step_clamps(ref):
+    # step 1: the code is the value rounded half away from zero, clamped to +-127
+    v = np.array([[-200.0, -127.5, -126.5, -0.5, 0.49999997, 0.5, 126.49998, 126.5, 127.4, 300.0]],
+                 np.float32)
+    xq, sx = ref.quant_act_pertensor(v, 1.0)
+    assert xq.tolist() == [[-127, -127, -127, -1, 0, 1, 126, 127, 127, 127]]
+    assert sx.tolist() == [1.0]
+    # step 0.5: 63.25 -> 126.5 -> 127; 64 -> 128 -> clamped
+    xq, _ = ref.quant_act_pertensor(np.array([[63.25, 64.0, -64.0, 10.0]], np.float32), 0.5)
+    assert xq.tolist() == [[127, 127, -127, 20]]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pertensor_static_matches_bruteforce(ref, seed):
+    r = np.random.default_rng([13, seed])
+    x = (r.standard_normal((4, 29)) * 3).astype(np.float32)
+    step = np.float32(r.uniform(0.005, 0.05))
+    xq, sx = ref.quant_act_pertensor(x, step)
+    assert xq.ravel().tolist() == brute.quantize_with_step(x.ravel(), step)
+    assert (sx == step).all()
+
+
+def test_static_step_is_largest_smoothed_calibration_value(ref):
+    # O3's step: the largest |x_hat| over the calibration set (x_hat = x / s,
+    # one fp32 division per element, numpy here), over 127
+    cfg = synth.CONFIGS[1]
+    xc = synth.activations(cfg, "toy", cfg.T, calibration=True).float().numpy()
+    w = synth.weight(cfg, "toy").float().numpy()
+    a = np.abs(xc).max(axis=0)
+    s = ref.smoothing_factors(a, np.abs(w).max(axis=1), 0.5)
+    x_hat = xc / s[None, :]
+    assert x_hat.dtype == np.float32
+    assert ref.static_act_step(a, s) == np.float32(np.abs(x_hat).max()) / np.float32(127)
+
+
+def test_static_step_alpha_one_is_one_over_127(ref):
+    # alpha = 1: s_j = a_j, so every calibration channel is flattened to max 1
+    a = np.abs(np.random.default_rng(14).standard_normal(64)).astype(np.float32) + 0.1
+    s = ref.smoothing_factors(a, np.ones(64, np.float32), 1.0)
+    assert ref.static_act_step(a, s) == np.float32(1) / np.float32(127)
+
+
+def test_pertensor_weight_is_one_range_transposed(ref):
+    w = (np.random.default_rng(15).standard_normal((23, 5)) * 0.02).astype(np.float32)
+    w[3, 2] = 0.9  # one large weight sets the tensor's range
+    wq, sw = ref.quant_weight_pertensor(w)
+    codes, st = brute.quantize_vector(w.ravel())
+    assert (sw == st).all()
+    assert wq.tolist() == np.array(codes).reshape(23, 5).T.tolist()
+
+
+def test_pertensor_weight_single_column_is_perchannel(ref):
+    w = np.random.default_rng(16).standard_normal((40, 1)).astype(np.float32)
+    assert all((p == q).all() for p, q in zip(ref.quant_weight_pertensor(w),
+                                                ref.quant_weight_perchannel(w)))
+
