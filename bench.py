@@ -63,6 +63,11 @@ class Layer:
         self.s, w_hat = sq.smooth_fold(a, w, ALPHA)
         self.wq, self.sw = sq.quant_weight_perchannel(w_hat)
         self.wp = sq.pack_weight(self.wq)  # fragment-packed copy (offline re-layout)
+        # O2/O3: per-tensor weights; O3's static activation step from calibration
+        wq_t, self.sw_t = sq.quant_weight_pertensor(w_hat)
+        self.wp_t = sq.pack_weight(wq_t)
+        self.step = sq.static_act_step(a, self.s)
+        del wq_t
         x = self.x_eval_host.to(dev)
         self.x_hat = sq.smooth_activation(x, self.s)   # what a folded LayerNorm emits
         torch.cuda.synchronize()
@@ -113,13 +118,20 @@ class Bufs:
     """One rotating set of run-time buffers for every layer at M tokens, with
     the weights either row-major (canonical) or fragment-packed."""
 
-    def __init__(self, layers, M, dev, packed):
+    def __init__(self, layers, M, dev, packed, mode="o1"):
         self.items = []
         self.packed = packed
+        self.mode = mode
+        self.steps = []
         for ly in layers:
             x_hat = ly.x_hat[:M].clone()
-            w = (ly.wp if packed else ly.wq).clone()
-            sw = ly.sw.clone()
+            if mode == "o1":
+                w = (ly.wp if packed else ly.wq).clone()
+                sw = ly.sw.clone()
+            else:  # per-tensor weights
+                assert packed
+                w, sw = ly.wp_t.clone(), ly.sw_t.clone()
+            self.steps.append(ly.step.clone())
             xq = torch.empty(M, ly.K, dtype=torch.int8, device=dev)
             sx = torch.empty(M, dtype=torch.float32, device=dev)
             y = torch.empty(M, ly.N, dtype=torch.float16, device=dev)
@@ -132,8 +144,13 @@ class Bufs:
             sq.sq_w8a8_gemm_dequant(xq, sx, w, sw, y)
 
     def step(self):
-        for (x_hat, w, sw, xq, sx, y, N) in self.items:
-            if self.packed:  # one call per layer; one kernel for M <= 4
+        for (x_hat, w, sw, xq, sx, y, N), st in zip(self.items, self.steps):
+            if self.mode == "o3":  # one call per layer, static per-tensor step
+                sq.sq_w8a8_linear_packed_static(x_hat, w, sw, st, xq, sx, y)
+            elif self.mode == "o2":
+                sq.sq_quant_act_pertensor(x_hat, xq, sx)
+                self._gemm(xq, sx, w, sw, y, N)
+            elif self.packed:  # one call per layer; one kernel for few tokens
                 sq.sq_w8a8_linear_packed(x_hat, w, sw, xq, sx, y)
             else:
                 sq.sq_quant_act_pertoken(x_hat, xq, sx)
@@ -144,8 +161,13 @@ class Bufs:
             self._gemm(xq, sx, w, sw, y, N)
 
     def quant_only(self):
-        for (x_hat, w, sw, xq, sx, y, N) in self.items:
-            sq.sq_quant_act_pertoken(x_hat, xq, sx)
+        for (x_hat, w, sw, xq, sx, y, N), st in zip(self.items, self.steps):
+            if self.mode == "o3":
+                sq.sq_quant_act_pertensor(x_hat, xq, sx, None, st)
+            elif self.mode == "o2":
+                sq.sq_quant_act_pertensor(x_hat, xq, sx)
+            else:
+                sq.sq_quant_act_pertoken(x_hat, xq, sx)
 
 
 def capture(fn):
@@ -238,6 +260,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offline", action="store_true")
+    ap.add_argument("--no-levels", action="store_true", help="skip the O2/O3 measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -360,6 +383,45 @@ def main():
                 torch.cuda.synchronize()
             dec["M=%d" % Md] = entry
         out["decode"] = dec
+
+    # ---- O2 (per-tensor dynamic) and O3 (per-tensor static) activations with
+    # per-tensor weights, packed layout
+    if not args.no_levels:
+        lv = {}
+        for mode in ("o2", "o3"):
+            sets = [Bufs(layers, M, dev, True, mode) for _ in range(2)]
+            ms_l = time_graphs([capture(b.step) for b in sets], args.steps, args.warmup)
+            q_l = time_graphs([capture(b.quant_only) for b in sets], args.steps,
+                              args.warmup) / len(layers)
+            ent = {"prefill_ms_per_step": round(ms_l, 4),
+                   "prefill_tops": round(ops_step / (ms_l * 1e-3) / 1e12, 2),
+                   "act_quant_avg_us": round(q_l * 1e3, 2)}
+            log("%s prefill: step %.3f ms (%.1f TOPS); act quant avg %.2f us"
+                % (mode, ms_l, ops_step / ms_l / 1e9, q_l * 1e3))
+            del sets
+            torch.cuda.synchronize()
+            if mode == "o3" and not args.no_decode:
+                for Md in DECODE_M:
+                    foot = sum(ly.N * ly.K + Md * ly.K * 3 + Md * ly.N * 2 for ly in layers)
+                    R = n_sets(foot)
+                    nbytes = sum(ly.N * ly.K + 4 * ly.N + 2 * Md * ly.K + 2 * Md * ly.N + 4 * Md
+                                 for ly in layers)
+                    sets = [Bufs(layers, Md, dev, True, mode) for _ in range(R)]
+                    ms_d = time_graphs([capture(b.step) for b in sets], max(args.steps, 4 * R),
+                                       args.warmup)
+                    gbs = nbytes / (ms_d * 1e-3) / 1e9
+                    ent["decode_M=%d" % Md] = {"us_per_step": round(ms_d * 1e3, 2),
+                                               "gbs": round(gbs, 1),
+                                               "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+                    log("o3 decode M=%d: %.2f us/step, %.0f GB/s (%.1f%% HBM)"
+                        % (Md, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS))
+                    del sets
+                    torch.cuda.synchronize()
+            lv[mode] = ent
+        lv["step"] = ("o2: sq_quant_act_pertensor (dynamic) + sq_w8a8_gemm_dequant_packed; "
+                      "o3: sq_w8a8_linear_packed_static (static step from calibration); "
+                      "per-tensor weights; 3 layers")
+        out["per_tensor_levels"] = lv
 
     if not args.no_offline:
         out["offline"] = offline_time(dev)

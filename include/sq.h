@@ -55,7 +55,8 @@ typedef enum {
     SQ_ERR_K_OVERFLOW = 4,  /* K > SQ_MAX_K: int32 accumulators could overflow */
     SQ_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
     SQ_ERR_ALPHA = 6,       /* alpha outside [0, 1] or not finite */
-    SQ_ERR_HIP = 7          /* the HIP runtime reported a launch error */
+    SQ_ERR_HIP = 7,         /* the HIP runtime reported a launch error */
+    SQ_ERR_ALIAS = 8        /* two buffers overlap where the entry point forbids it */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
@@ -105,6 +106,14 @@ sq_status sq_smooth_fold(const float* a, const void* w, sq_dtype wdt, int64_t K,
 sq_status sq_quant_weight_perchannel(const void* w, sq_dtype wdt, int64_t K, int64_t N,
                                      int8_t* wq, float* w_scale, void* stream);
 
+/* Per-tensor weight quantisation [P1 推論方法, O1-O3: weights per tensor]:
+ * one step for the whole matrix,
+ *   step = max_{j,n} |w[j, n]| / 127;   wq[n, j] = code(w[j, n], step)
+ * and every w_scale[n] = step, so the GEMM entry points take it unchanged.
+ * Shapes, layouts and dtypes as sq_quant_weight_perchannel. */
+sq_status sq_quant_weight_pertensor(const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                                    int8_t* wq, float* w_scale, void* stream);
+
 /* ---------------------------------------------------------------- runtime */
 
 /* Per-token dynamic activation quantisation [P1 推論方法, O1: activations per
@@ -116,6 +125,34 @@ sq_status sq_quant_weight_perchannel(const void* w, sq_dtype wdt, int64_t K, int
  * smoothed).  xq: int8 [M x K].  x_scale: fp32 [M]. */
 sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
                                 const float* smooth, int8_t* xq, float* x_scale, void* stream);
+
+/* Per-tensor activation quantisation [P1 推論方法, O2: activations per
+ * tensor, dynamic; O3: per tensor, static, the step fixed offline from
+ * calibration]:
+ *   v[m, k] = smooth ? fp32(x[m, k]) / smooth[k] : fp32(x[m, k])
+ *   step    = step_in ? *step_in                      (O3, static)
+ *                     : max_{m,k} |v[m, k]| / 127      (O2, dynamic)
+ *   xq[m, k] = code(v[m, k], step)  (clamped to +-127: under a static step
+ *              values beyond 127 * step saturate);   x_scale[m] = step
+ * Every x_scale entry holds the same step, so sq_w8a8_gemm_dequant and the
+ * packed GEMM consume the result unchanged.  step_in: device pointer to one
+ * fp32 (the output of sq_static_act_step) or NULL; it must not overlap
+ * x_scale.  In the dynamic case x_scale[0] serves as the reduction's
+ * accumulator until the last launch overwrites it.  Other arguments as
+ * sq_quant_act_pertoken.  Dynamic: four launches (clear, max, codes, fill);
+ * static: one. */
+sq_status sq_quant_act_pertensor(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                 const float* smooth, const float* step_in, int8_t* xq,
+                                 float* x_scale, void* stream);
+
+/* The O3 static activation step from calibration statistics [P1 推論方法, O3;
+ * smoothing factor はどう決めるのか]: the calibration maxima a_j of X's
+ * channels become a_j / s_j after smoothing, so
+ *   *step_out = max_j (a[j] / s[j]) / 127      (fp32 divisions)
+ * a, s: fp32 [K] (sq_calibrate_absmax's and sq_smooth_fold's outputs).
+ * step_out: device pointer to one fp32.  One workgroup. */
+sq_status sq_static_act_step(const float* a, const float* s, int64_t K, float* step_out,
+                             void* stream);
 
 /* INT8 GEMM with fused scale back [P1 用語解説 "INT8 GEMM", 推論方法;
  * P4 section 3: multiply the scale factor back]:
@@ -176,6 +213,19 @@ sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int
 sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t K,
                                 const int8_t* wq_packed, const float* w_scale, int64_t N,
                                 int8_t* xq, float* x_scale, void* y, sq_dtype ydt, void* stream);
+
+/* The same one-call layer with O3's static per-tensor step [P1 推論方法, O3]:
+ * quantisation is exactly sq_quant_act_pertensor with smooth = NULL and
+ * step_in given (no run-time maximum: every token uses *step_in, values
+ * beyond 127 steps saturate), followed by sq_w8a8_gemm_dequant_packed.  One
+ * kernel for M <= 16 and M * K <= 32768, else two launches.  step_in: device
+ * pointer to one fp32 (sq_static_act_step's output), not inside x_scale
+ * (SQ_ERR_ALIAS).  Other arguments and outputs as sq_w8a8_linear_packed;
+ * every x_scale entry is *step_in. */
+sq_status sq_w8a8_linear_packed_static(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                       const int8_t* wq_packed, const float* w_scale, int64_t N,
+                                       const float* step_in, int8_t* xq, float* x_scale, void* y,
+                                       sq_dtype ydt, void* stream);
 
 /* Library version string (static storage). */
 const char* sq_version(void);

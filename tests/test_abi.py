@@ -91,3 +91,19 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(4, 4, dtype=torch.float16)
     with pytest.raises(TypeError):
         sq.quant_act_pertoken(x)
+
+
+def test_pertensor_entry_points_validate(lib):
+    # argument order: x, xdt, M, K, smooth, step_in, xq, x_scale, stream
+    assert lib.sq_quant_act_pertensor(None, 1, 4, 4, None, None, A, A, None) == 1
+    assert lib.sq_quant_act_pertensor(A, 1, 0, 4, None, None, A, A, None) == 2
+    assert lib.sq_quant_act_pertensor(A, 5, 4, 4, None, None, A, A, None) == 3
+    assert lib.sq_quant_act_pertensor(A, 1, 4, 4, A + 4, None, A, A, None) == 5
+    # a static step inside x_scale (x_scale = 8192, M = 4 floats) is refused
+    assert lib.sq_quant_act_pertensor(A, 1, 4, 4, None, 8192 + 12, A, 8192, None) == 8
+    assert lib.sq_static_act_step(A, None, 4, A, None) == 1
+    assert lib.sq_static_act_step(A, A, 0, A, None) == 2
+    assert lib.sq_quant_weight_pertensor(A, 1, 4, 4, None, A, None) == 1
+    assert lib.sq_quant_weight_pertensor(A, 1, 4, -3, A, A, None) == 2
+    assert lib.sq_quant_weight_pertensor(A, 9, 4, 4, A, A, None) == 3
+    assert lib.sq_quant_weight_pertensor(A, 1, 4, 4, A, A + 2, None) == 5

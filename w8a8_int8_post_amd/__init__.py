@@ -26,7 +26,9 @@ __all__ = [
     "sq_smooth_activation", "sq_packed_weight_bytes", "sq_pack_weight",
     "sq_w8a8_gemm_dequant_packed", "sq_w8a8_gemm_i32_packed", "pack_weight",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_i32_packed", "linear_w8a8_packed",
-    "sq_w8a8_linear_packed",
+    "sq_w8a8_linear_packed", "sq_w8a8_linear_packed_static", "sq_quant_act_pertensor", "sq_static_act_step",
+    "sq_quant_weight_pertensor", "quant_act_pertensor", "static_act_step",
+    "quant_weight_pertensor", "linear_w8a8_packed_static",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -34,7 +36,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE",
-          4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP"}
+          4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP",
+          8: "SQ_ERR_ALIAS"}
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
 MAX_K = 133144
@@ -69,6 +72,10 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_gemm_dequant_packed": [P, P, P, P, I64, I64, I64, P, E, P],
             "sq_w8a8_gemm_i32_packed": [P, P, I64, I64, I64, P, P],
             "sq_w8a8_linear_packed": [P, E, I64, I64, P, P, I64, P, P, P, E, P],
+            "sq_w8a8_linear_packed_static": [P, E, I64, I64, P, P, I64, P, P, P, P, E, P],
+            "sq_quant_act_pertensor": [P, E, I64, I64, P, P, P, P, P],
+            "sq_static_act_step": [P, P, I64, P, P],
+            "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -140,6 +147,41 @@ def sq_quant_act_pertoken(x, xq, x_scale, smooth=None, stream=None):
     _call("sq_quant_act_pertoken", _dev(x, "x"), _DT[x.dtype], M, K,
           _opt(smooth, "smooth", torch.float32), _dev(xq, "xq", torch.int8),
           _dev(x_scale, "x_scale", torch.float32), _stream(x, stream))
+
+
+def sq_w8a8_linear_packed_static(x, wq_packed, w_scale, step_in, xq, x_scale, y, stream=None):
+    M, K = x.shape
+    N = w_scale.shape[0]
+    if tuple(xq.shape) != (M, K) or tuple(y.shape) != (M, N) or x_scale.shape[0] != M:
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_linear_packed_static", _dev(x, "x"), _DT[x.dtype], M, K,
+          _dev(wq_packed, "wq_packed", torch.int8), _dev(w_scale, "w_scale", torch.float32), N,
+          _dev(step_in, "step_in", torch.float32), _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(y, "y"), _DT[y.dtype], _stream(x, stream))
+
+
+def sq_quant_act_pertensor(x, xq, x_scale, smooth=None, step_in=None, stream=None):
+    M, K = x.shape
+    if tuple(xq.shape) != (M, K) or x_scale.shape[0] != M:
+        raise ValueError("shape mismatch")
+    _call("sq_quant_act_pertensor", _dev(x, "x"), _DT[x.dtype], M, K,
+          _opt(smooth, "smooth", torch.float32), _opt(step_in, "step_in", torch.float32),
+          _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32), _stream(x, stream))
+
+
+def sq_static_act_step(a, s, step_out, stream=None):
+    K = a.shape[0]
+    if s.shape[0] != K or step_out.numel() < 1:
+        raise ValueError("shape mismatch")
+    _call("sq_static_act_step", _dev(a, "a", torch.float32), _dev(s, "s", torch.float32), K,
+          _dev(step_out, "step_out", torch.float32), _stream(a, stream))
+
+
+def sq_quant_weight_pertensor(w, wq, w_scale, stream=None):
+    K, N = w.shape
+    _call("sq_quant_weight_pertensor", _dev(w, "w"), _DT[w.dtype], K, N,
+          _dev(wq, "wq", torch.int8), _dev(w_scale, "w_scale", torch.float32), _stream(w, stream))
 
 
 def sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream=None):
@@ -255,6 +297,29 @@ def quant_act_pertoken(x, smooth=None, stream=None):
     return xq, sx
 
 
+def quant_act_pertensor(x, smooth=None, step_in=None, stream=None):
+    """O2 (step_in None: dynamic) or O3 (step_in: a 1-element device step)."""
+    M, K = x.shape
+    xq = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    sq_quant_act_pertensor(x, xq, sx, smooth, step_in, stream)
+    return xq, sx
+
+
+def static_act_step(a, s, stream=None):
+    out = torch.empty(1, dtype=torch.float32, device=a.device)
+    sq_static_act_step(a, s, out, stream)
+    return out
+
+
+def quant_weight_pertensor(w, stream=None):
+    K, N = w.shape
+    wq = torch.empty(N, K, dtype=torch.int8, device=w.device)
+    sw = torch.empty(N, dtype=torch.float32, device=w.device)
+    sq_quant_weight_pertensor(w, wq, sw, stream)
+    return wq, sw
+
+
 def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, out_dtype=torch.float16, stream=None):
     y = torch.empty(xq.shape[0], wq.shape[0], dtype=out_dtype, device=xq.device)
     sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream)
@@ -306,6 +371,18 @@ def linear_w8a8_packed(x_hat, wq_packed, w_scale, out_dtype=torch.float16, strea
     sx = torch.empty(M, dtype=torch.float32, device=x_hat.device)
     y = torch.empty(M, N, dtype=out_dtype, device=x_hat.device)
     sq_w8a8_linear_packed(x_hat, wq_packed, w_scale, xq, sx, y, stream)
+    return y, xq, sx
+
+
+def linear_w8a8_packed_static(x_hat, wq_packed, w_scale, step_in, out_dtype=torch.float16,
+                              stream=None):
+    """O3 run-time layer on packed weights (sq_w8a8_linear_packed_static): (y, xq, sx)."""
+    M, K = x_hat.shape
+    N = w_scale.shape[0]
+    xq = torch.empty(M, K, dtype=torch.int8, device=x_hat.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x_hat.device)
+    y = torch.empty(M, N, dtype=out_dtype, device=x_hat.device)
+    sq_w8a8_linear_packed_static(x_hat, wq_packed, w_scale, step_in, xq, sx, y, stream)
     return y, xq, sx
 
 

@@ -243,7 +243,182 @@ hipError_t smooth_act_typed(const void* xv, int64_t M, int64_t K, const float* s
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor activation quantisation [P1 推論方法: O2 per tensor, dynamic;
+// O3 per tensor, static].  The tensor is treated as M * K contiguous values
+// (rows are contiguous), in 16-byte chunks when K is a multiple of the
+// vector width (a chunk then never crosses a row), else element by element.
+
+constexpr int kTensorThreads = 256;
+constexpr int kTensorUnroll = 4;  // chunks in flight per thread
+
+// Chunk c of the flat tensor (V values), widened to fp32 and optionally
+// divided by the smoothing factors of its channels.
+template <class D, bool SMOOTH, int V>
+__device__ inline void load_chunk_f32(const typename D::T* x, const float* smooth, int64_t c,
+                                      int64_t K, float (&v)[V]) {
+    if constexpr (V == D::VEC) {
+        load_vec<D>(x + c * V, v);
+    } else {
+        v[0] = D::to_f32(x[c]);
+    }
+    if constexpr (SMOOTH) {
+        const int64_t k0 = (c * V) % K;
+        if constexpr (V % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < V; e += 4) {
+                const float4 s4 = *reinterpret_cast<const float4*>(smooth + k0 + e);
+                v[e] = v[e] / s4.x;
+                v[e + 1] = v[e + 1] / s4.y;
+                v[e + 2] = v[e + 2] / s4.z;
+                v[e + 3] = v[e + 3] / s4.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[e] = v[e] / smooth[k0 + e];
+        }
+    }
+}
+
+// Largest |x_hat| over the tensor, folded into *acc (zeroed beforehand) with
+// an unsigned atomic max (exact and order-free for non-negative floats).
+template <class D, bool SMOOTH, int V>
+__global__ __launch_bounds__(kTensorThreads) void tensor_absmax_kernel(
+    const typename D::T* __restrict__ x, const float* __restrict__ smooth, int64_t M, int64_t K,
+    float* __restrict__ acc) {
+    __shared__ float red[kTensorThreads / 64];
+    const int64_t total = M * K / V;
+    const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
+    float m = 0.0f;
+    for (int64_t i0 = (int64_t)blockIdx.x * kTensorThreads + threadIdx.x; i0 < total;
+         i0 += stride * kTensorUnroll) {
+        float v[kTensorUnroll][V];
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u) {
+            const int64_t i = i0 + u * stride;
+            load_chunk_f32<D, SMOOTH, V>(x, smooth, i < total ? i : total - 1, K, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u)
+            if (i0 + u * stride < total) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[u][e]));
+            }
+    }
+    m = block_max<kTensorThreads>(m, red);
+    if (threadIdx.x == 0) atomic_max_nonneg(acc, m);
+}
+
+// Codes with one step: STATIC -> src[0] is the step, and workgroup 0 also
+// writes it to x_scale[0..M); else src[0] is the tensor's absmax, the step
+// is absmax / 127 and x_scale is written afterwards by fill_scale_kernel.
+template <class D, bool SMOOTH, int V, bool STATIC>
+__global__ __launch_bounds__(kTensorThreads) void tensor_quant_kernel(
+    const typename D::T* __restrict__ x, const float* __restrict__ smooth, int64_t M, int64_t K,
+    const float* __restrict__ src, int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    const RowStep q = given_step(STATIC ? src[0] : quant_step(src[0]));
+    if (STATIC && blockIdx.x == 0)
+        for (int64_t m = threadIdx.x; m < M; m += kTensorThreads) x_scale[m] = q.step;
+    const int64_t total = M * K / V;
+    const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
+    for (int64_t i0 = (int64_t)blockIdx.x * kTensorThreads + threadIdx.x; i0 < total;
+         i0 += stride * kTensorUnroll) {
+        float v[kTensorUnroll][V];
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u) {
+            const int64_t i = i0 + u * stride;
+            load_chunk_f32<D, SMOOTH, V>(x, smooth, i < total ? i : total - 1, K, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kTensorUnroll; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i >= total) continue;
+            if constexpr (V == 1) {
+                xq[i] = (int8_t)(q.fast ? quant_code<true>(v[u][0], q) : quant_code<false>(v[u][0], q));
+            } else if (q.fast) {
+                store_codes<true, V>(xq + i * V, v[u], q);
+            } else {
+                store_codes<false, V>(xq + i * V, v[u], q);
+            }
+        }
+    }
+}
+
+// x_scale[0] holds the tensor's absmax; every x_scale[m] becomes the step.
+// One workgroup: every thread reads x_scale[0] before any thread writes.
+__global__ __launch_bounds__(1024) void fill_scale_kernel(float* x_scale, int64_t M) {
+    const float v = quant_step(x_scale[0]);
+    __syncthreads();
+    for (int64_t m = threadIdx.x; m < M; m += 1024) x_scale[m] = v;
+}
+
+__global__ void zero_one_kernel(float* p) { *p = 0.0f; }
+
+template <class D, bool SMOOTH, int V>
+hipError_t pertensor_typed(const void* xv, int64_t M, int64_t K, const float* smooth,
+                           const float* step, int8_t* xq, float* x_scale, hipStream_t s) {
+    const typename D::T* x = static_cast<const typename D::T*>(xv);
+    const int64_t total = M * K / V;
+    int64_t blocks = (total + kTensorThreads * kTensorUnroll - 1) / (kTensorThreads * kTensorUnroll);
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    const float* src = step;
+    if (!step) {
+        hipLaunchKernelGGL(zero_one_kernel, dim3(1), dim3(1), 0, s, x_scale);
+        hipLaunchKernelGGL((tensor_absmax_kernel<D, SMOOTH, V>), dim3((unsigned)blocks),
+                           dim3(kTensorThreads), 0, s, x, smooth, M, K, x_scale);
+        src = x_scale;
+        hipLaunchKernelGGL((tensor_quant_kernel<D, SMOOTH, V, false>), dim3((unsigned)blocks),
+                           dim3(kTensorThreads), 0, s, x, smooth, M, K, src, xq, nullptr);
+        hipLaunchKernelGGL(fill_scale_kernel, dim3(1), dim3(1024), 0, s, x_scale, M);
+    } else {
+        hipLaunchKernelGGL((tensor_quant_kernel<D, SMOOTH, V, true>), dim3((unsigned)blocks),
+                           dim3(kTensorThreads), 0, s, x, smooth, M, K, src, xq, x_scale);
+    }
+    return hipGetLastError();
+}
+
+template <class D>
+hipError_t pertensor_dispatch(const void* x, int64_t M, int64_t K, const float* smooth,
+                              const float* step, int8_t* xq, float* x_scale, hipStream_t s) {
+    const bool vect = K % D::VEC == 0;
+    if (smooth) {
+        return vect ? pertensor_typed<D, true, D::VEC>(x, M, K, smooth, step, xq, x_scale, s)
+                    : pertensor_typed<D, true, 1>(x, M, K, smooth, step, xq, x_scale, s);
+    }
+    return vect ? pertensor_typed<D, false, D::VEC>(x, M, K, smooth, step, xq, x_scale, s)
+                : pertensor_typed<D, false, 1>(x, M, K, smooth, step, xq, x_scale, s);
+}
+
+// O3's step from calibration: the largest a_j / s_j (fp32 division), over
+// 127.  One workgroup.
+__global__ __launch_bounds__(1024) void static_step_kernel(const float* __restrict__ a,
+                                                           const float* __restrict__ sm, int64_t K,
+                                                           float* __restrict__ out) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int64_t j = threadIdx.x; j < K; j += 1024) m = __builtin_fmaxf(m, a[j] / sm[j]);
+    m = block_max<1024>(m, red);
+    if (threadIdx.x == 0) out[0] = quant_step(m);
+}
+
 }  // namespace
+
+hipError_t launch_act_quant_pertensor(const void* x, Dt dt, int64_t M, int64_t K,
+                                      const float* smooth, const float* step, int8_t* xq,
+                                      float* x_scale, hipStream_t s) {
+    switch (dt) {
+        case Dt::F32: return pertensor_dispatch<F32>(x, M, K, smooth, step, xq, x_scale, s);
+        case Dt::F16: return pertensor_dispatch<F16>(x, M, K, smooth, step, xq, x_scale, s);
+        case Dt::BF16: return pertensor_dispatch<BF16>(x, M, K, smooth, step, xq, x_scale, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_static_act_step(const float* a, const float* smooth, int64_t K, float* step_out,
+                                  hipStream_t s) {
+    hipLaunchKernelGGL(static_step_kernel, dim3(1), dim3(1024), 0, s, a, smooth, K, step_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                             int8_t* xq, float* x_scale, hipStream_t s) {

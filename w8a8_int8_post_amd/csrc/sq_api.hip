@@ -71,6 +71,36 @@ sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t 
         sq::launch_act_quant(x, to_dt(xdt), M, K, smooth, xq, x_scale, as_stream(stream)));
 }
 
+sq_status sq_quant_weight_pertensor(const void* w, sq_dtype wdt, int64_t K, int64_t N,
+                                    int8_t* wq, float* w_scale, void* stream) {
+    if (!w || !wq || !w_scale) return SQ_ERR_NULL;
+    if (!dims_ok(K, N)) return SQ_ERR_SHAPE;
+    if (!dt_ok(wdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)) return SQ_ERR_ALIGN;
+    return hip_status(
+        sq::launch_quant_weight_pertensor(w, to_dt(wdt), K, N, wq, w_scale, as_stream(stream)));
+}
+
+sq_status sq_quant_act_pertensor(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                 const float* smooth, const float* step_in, int8_t* xq,
+                                 float* x_scale, void* stream) {
+    if (!x || !xq || !x_scale) return SQ_ERR_NULL;
+    if (!dims_ok(M, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(xdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || (smooth && !aligned16(smooth)))
+        return SQ_ERR_ALIGN;
+    if (step_in && step_in >= x_scale && step_in < x_scale + M) return SQ_ERR_ALIAS;
+    return hip_status(sq::launch_act_quant_pertensor(x, to_dt(xdt), M, K, smooth, step_in, xq,
+                                                     x_scale, as_stream(stream)));
+}
+
+sq_status sq_static_act_step(const float* a, const float* s, int64_t K, float* step_out,
+                             void* stream) {
+    if (!a || !s || !step_out) return SQ_ERR_NULL;
+    if (!dims_ok(1, K)) return SQ_ERR_SHAPE;
+    return hip_status(sq::launch_static_act_step(a, s, K, step_out, as_stream(stream)));
+}
+
 sq_status sq_w8a8_gemm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                                sq_dtype ydt, void* stream) {
@@ -155,6 +185,24 @@ sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t 
     sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
     return hip_status(sq::launch_linear_packed(x, to_dt(xdt), M, K, wq_packed, w_scale, N, xq,
                                                x_scale, y, out, as_stream(stream)));
+}
+
+sq_status sq_w8a8_linear_packed_static(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                       const int8_t* wq_packed, const float* w_scale, int64_t N,
+                                       const float* step_in, int8_t* xq, float* x_scale, void* y,
+                                       sq_dtype ydt, void* stream) {
+    if (!x || !wq_packed || !w_scale || !step_in || !xq || !x_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || !dims_ok(K, 1) || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(xdt) || !dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(wq_packed) || !aligned16(w_scale) || !aligned16(xq) ||
+        !aligned16(x_scale) || !aligned16(y))
+        return SQ_ERR_ALIGN;
+    if (step_in >= x_scale && step_in < x_scale + M) return SQ_ERR_ALIAS;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_linear_packed_static(x, to_dt(xdt), M, K, wq_packed, w_scale, N,
+                                                      step_in, xq, x_scale, y, out,
+                                                      as_stream(stream)));
 }
 
 }  // extern "C"

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
 //  3) writes the codes into LDS (workgroup 0 also stores xq and x_scale);
 //  4) streams its 16 output channels with the activation fragments read
 //     from LDS, one stage of two 256-byte steps per wave in flight.
-// LDS: M * K bytes of codes.
+// LDS: M * K bytes of codes.  STATIC (O3, one step for the whole tensor,
+// given in step_in[0]): step 2 disappears and every token takes that step.
 constexpr int kFusedMaxM = 16;
 // Every workgroup quantises all M x K activations itself, which pays off
 // only while that work is small next to streaming the workgroup's weights
@@ -249,11 +250,11 @@ __device__ inline float wave_max_dpp(float v) {
     return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
 }
 
-template <class D, int NW, int U, Out O, int CPT, int MM>
+template <class D, int NW, int U, Out O, int CPT, int MM, bool STATIC>
 __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,
-    const float* __restrict__ sw, int8_t* __restrict__ xq_out, float* __restrict__ sx_out,
-    void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, const float* __restrict__ step_in, int8_t* __restrict__ xq_out,
+    float* __restrict__ sx_out, void* __restrict__ Y, int M, int N, int K) {
     constexpr int NT = NW * 64, V = D::VEC;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
     __shared__ v4i red[NW][1][64];
@@ -282,6 +283,16 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     load_stage<NW, U>(w, wave, KG, wfrag);
 
     // 2) per-token absmax (x rows are contiguous: chunk j belongs to token j / nch)
+    // a token's step (per-token maxima from LDS: a runtime index into a
+    // register array would put the array in scratch memory)
+    float sstep = 0.0f;
+    auto step_of = [&](int m) -> float {
+        if constexpr (STATIC) return sstep;
+        else return quant_step(smax[m]);
+    };
+    if constexpr (STATIC) {
+        sstep = step_in[0];
+    } else {
     float am[MM];
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) am[mm] = 0.0f;
@@ -310,16 +321,14 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
         smax[tid] = a;
     }
     __syncthreads();
-    // a token's absmax from LDS (a runtime index into a register array would
-    // put the array in scratch memory)
-    auto absmax_of = [&](int m) { return smax[m]; };
+    }  // !STATIC
 
     // 3) codes into LDS (and xq, x_scale from workgroup 0)
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
         const int j = i * NT + tid;
         if (j < TC) {
-            const RowStep st = row_step(absmax_of(j / nch));
+            const RowStep st = given_step(step_of(j / nch));
             const typename D::T* e = reinterpret_cast<const typename D::T*>(&xr[i]);
             int8_t q[V];
             if (st.fast) {
@@ -340,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
             }
         }
     }
-    if (b0 == 0 && tid < M) sx_out[tid] = quant_step(absmax_of(tid));
+    if (b0 == 0 && tid < M) sx_out[tid] = step_of(tid);
     __syncthreads();
 
     // 4) the weight stream
@@ -361,35 +370,42 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
         if (st + S < nsteps) load_stage<NW, U>(w, st + S, KG, wfrag);
     }
     const int tok = lane & 15;  // this lane's token (stored only if < M)
-    const float sx_lane = quant_step(tok < MM ? absmax_of(tok) : 0.0f);
+    const float sx_lane = step_of(tok < MM ? tok : 0);
     reduce_store<1, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
                            [sx_lane](int) { return sx_lane; });
 }
 
-template <class D, Out O, int CPT, int MM>
-hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, int8_t* xq,
-                            float* sx, void* y, int M, int N, int K, hipStream_t s) {
-    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT, MM>),
+template <class D, Out O, int CPT, int MM, bool STATIC>
+hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, const float* step,
+                            int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
+    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT, MM, STATIC>),
                        dim3((unsigned)((N + 15) / 16)), dim3(kNW * 64), (size_t)M * K, s,
-                       static_cast<const typename D::T*>(x), wp, sw, xq, sx, y, M, N, K);
+                       static_cast<const typename D::T*>(x), wp, sw, step, xq, sx, y, M, N, K);
     return hipGetLastError();
 }
 
-template <class D, Out O>
-hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
-                        void* y, int M, int N, int K, hipStream_t s) {
+// CPT: 16-byte chunks of x per thread; MM: token slots of the absmax (the
+// static variant has none and always takes MM = 4).
+template <class D, Out O, bool STATIC>
+hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const float* step,
+                        int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
     const int cpt = (M * (K / D::VEC) + kNW * 64 - 1) / (kNW * 64);
-    if (M <= 4) {
-        if (cpt <= 1) return launch_fused_cpt<D, O, 1, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
-        if (cpt <= 2) return launch_fused_cpt<D, O, 2, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
-        if (cpt <= 4) return launch_fused_cpt<D, O, 4, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
-        if (cpt <= 8) return launch_fused_cpt<D, O, 8, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
-        return launch_fused_cpt<D, O, 16, 4>(x, wp, sw, xq, sx, y, M, N, K, s);
+#define SQ_FUSED(C, MMV) \
+    return launch_fused_cpt<D, O, C, MMV, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s)
+    if constexpr (!STATIC) {
+        if (M > 4) {
+            if (cpt <= 2) SQ_FUSED(2, 16);
+            if (cpt <= 4) SQ_FUSED(4, 16);
+            if (cpt <= 8) SQ_FUSED(8, 16);
+            SQ_FUSED(16, 16);
+        }
     }
-    if (cpt <= 2) return launch_fused_cpt<D, O, 2, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
-    if (cpt <= 4) return launch_fused_cpt<D, O, 4, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
-    if (cpt <= 8) return launch_fused_cpt<D, O, 8, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
-    return launch_fused_cpt<D, O, 16, 16>(x, wp, sw, xq, sx, y, M, N, K, s);
+    if (cpt <= 1) SQ_FUSED(1, 4);
+    if (cpt <= 2) SQ_FUSED(2, 4);
+    if (cpt <= 4) SQ_FUSED(4, 4);
+    if (cpt <= 8) SQ_FUSED(8, 4);
+    SQ_FUSED(16, 4);
+#undef SQ_FUSED
 }
 
 // The one-kernel path applies: few tokens, M * K within the redundant-work
@@ -400,14 +416,28 @@ bool fused_fits(Dt xdt, int64_t M, int64_t K) {
            M * (K / vec) <= (int64_t)kFusedMaxCpt * kNW * 64;
 }
 
-template <class D>
-hipError_t fused_out(const void* x, const int8_t* wp, const float* sw, int8_t* xq, float* sx,
-                     void* y, Out out, int M, int N, int K, hipStream_t s) {
+template <class D, bool STATIC>
+hipError_t fused_out(const void* x, const int8_t* wp, const float* sw, const float* step,
+                     int8_t* xq, float* sx, void* y, Out out, int M, int N, int K, hipStream_t s) {
     switch (out) {
-        case Out::F16: return launch_fused<D, Out::F16>(x, wp, sw, xq, sx, y, M, N, K, s);
-        case Out::BF16: return launch_fused<D, Out::BF16>(x, wp, sw, xq, sx, y, M, N, K, s);
-        case Out::F32: return launch_fused<D, Out::F32>(x, wp, sw, xq, sx, y, M, N, K, s);
+        case Out::F16:
+            return launch_fused<D, Out::F16, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
+        case Out::BF16:
+            return launch_fused<D, Out::BF16, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
+        case Out::F32:
+            return launch_fused<D, Out::F32, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
         default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool STATIC>
+hipError_t fused_dt(const void* x, Dt xdt, const int8_t* wp, const float* sw, const float* step,
+                    int8_t* xq, float* sx, void* y, Out out, int M, int N, int K, hipStream_t s) {
+    switch (xdt) {
+        case Dt::F32: return fused_out<F32, STATIC>(x, wp, sw, step, xq, sx, y, out, M, N, K, s);
+        case Dt::F16: return fused_out<F16, STATIC>(x, wp, sw, step, xq, sx, y, out, M, N, K, s);
+        case Dt::BF16: return fused_out<BF16, STATIC>(x, wp, sw, step, xq, sx, y, out, M, N, K, s);
     }
     return hipErrorInvalidValue;
 }
@@ -453,16 +483,22 @@ hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, con
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
                                 void* y, Out out, hipStream_t s) {
-    if (fused_fits(xdt, M, K)) {
-        const int m = (int)M, n = (int)N, k = (int)K;
-        switch (xdt) {
-            case Dt::F32: return fused_out<F32>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-            case Dt::F16: return fused_out<F16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-            case Dt::BF16: return fused_out<BF16>(x, wp, w_scale, xq, x_scale, y, out, m, n, k, s);
-        }
-        return hipErrorInvalidValue;
-    }
+    if (fused_fits(xdt, M, K))
+        return fused_dt<false>(x, xdt, wp, w_scale, nullptr, xq, x_scale, y, out, (int)M, (int)N,
+                               (int)K, s);
     hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
+}
+
+hipError_t launch_linear_packed_static(const void* x, Dt xdt, int64_t M, int64_t K,
+                                       const int8_t* wp, const float* w_scale, int64_t N,
+                                       const float* step, int8_t* xq, float* x_scale, void* y,
+                                       Out out, hipStream_t s) {
+    if (fused_fits(xdt, M, K))
+        return fused_dt<true>(x, xdt, wp, w_scale, step, xq, x_scale, y, out, (int)M, (int)N,
+                              (int)K, s);
+    hipError_t e = launch_act_quant_pertensor(x, xdt, M, K, nullptr, step, xq, x_scale, s);
     if (e != hipSuccess) return e;
     return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
 }

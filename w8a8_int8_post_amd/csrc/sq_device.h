@@ -80,13 +80,17 @@ struct RowStep {
     bool fast;
 };
 
-__device__ inline RowStep row_step(float absmax) {
+// Quantiser parameters for a given step.
+__device__ inline RowStep given_step(float step) {
     RowStep q;
-    q.step = quant_step(absmax);
-    q.fast = q.step >= 0x1p-96f && q.step <= 0x1p96f;
-    q.rcp = q.fast ? 1.0f / q.step : 0.0f;
+    q.step = step;
+    q.fast = step >= 0x1p-96f && step <= 0x1p96f;
+    q.rcp = q.fast ? 1.0f / step : 0.0f;
     return q;
 }
+
+// ... and for the step absmax / 127 of a row's maximum.
+__device__ inline RowStep row_step(float absmax) { return given_step(quant_step(absmax)); }
 
 // FAST: the caller has checked q.fast (a row-uniform branch taken once).
 template <bool FAST>

@@ -20,6 +20,13 @@ hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_
                                float* w_scale, hipStream_t s);
 hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                             int8_t* xq, float* x_scale, hipStream_t s);
+hipError_t launch_act_quant_pertensor(const void* x, Dt dt, int64_t M, int64_t K,
+                                      const float* smooth, const float* step, int8_t* xq,
+                                      float* x_scale, hipStream_t s);
+hipError_t launch_static_act_step(const float* a, const float* smooth, int64_t K, float* step_out,
+                                  hipStream_t s);
+hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
+                                         float* w_scale, hipStream_t s);
 hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                              void* x_hat, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
@@ -39,5 +46,9 @@ hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, con
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
                                 void* y, Out out, hipStream_t s);
+hipError_t launch_linear_packed_static(const void* x, Dt xdt, int64_t M, int64_t K,
+                                       const int8_t* wp, const float* w_scale, int64_t N,
+                                       const float* step, int8_t* xq, float* x_scale, void* y,
+                                       Out out, hipStream_t s);
 
 }  // namespace sq

@@ -213,6 +213,16 @@ __global__ __launch_bounds__(kTileThreads) void quant_transpose_kernel(
     }
 }
 
+// p[0..n) <- max of p[0..n) (non-negative values).  One workgroup: every
+// read happens before the barriers in block_max, every write after them.
+__global__ __launch_bounds__(1024) void max_fill_kernel(float* p, int64_t n) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 1024) m = __builtin_fmaxf(m, p[i]);
+    m = block_max<1024>(m, red);
+    for (int64_t i = threadIdx.x; i < n; i += 1024) p[i] = m;
+}
+
 __global__ void absmax_to_step_kernel(float* p, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = quant_step(p[i]);
@@ -254,6 +264,27 @@ static hipError_t quant_transpose_typed(const void* wv, int64_t K, int64_t N, co
     dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile));
     hipLaunchKernelGGL((quant_transpose_kernel<D>), grid, dim3(kTileThreads), 0, s,
                        static_cast<const typename D::T*>(wv), K, N, absmax, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
+                                         float* w_scale, hipStream_t s) {
+    // per-column absmax, then every column takes the tensor's maximum; the
+    // per-channel steps and codes that follow are then those of one step
+    hipError_t e = launch_colmax(w, dt, K, N, w_scale, true, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(max_fill_kernel, dim3(1), dim3(1024), 0, s, w_scale, N);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (dt) {
+        case Dt::F32: e = quant_transpose_typed<F32>(w, K, N, w_scale, wq, s); break;
+        case Dt::F16: e = quant_transpose_typed<F16>(w, K, N, w_scale, wq, s); break;
+        case Dt::BF16: e = quant_transpose_typed<BF16>(w, K, N, w_scale, wq, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(absmax_to_step_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                       w_scale, N);
     return hipGetLastError();
 }
 
