@@ -137,10 +137,10 @@ sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t 
  * Every x_scale entry holds the same step, so sq_w8a8_gemm_dequant and the
  * packed GEMM consume the result unchanged.  step_in: device pointer to one
  * fp32 (the output of sq_static_act_step) or NULL; it must not overlap
- * x_scale.  In the dynamic case x_scale[0] serves as the reduction's
- * accumulator until the last launch overwrites it.  Other arguments as
- * sq_quant_act_pertoken.  Dynamic: four launches (clear, max, codes, fill);
- * static: one. */
+ * x_scale.  In the dynamic case x_scale first holds partial maxima (one per
+ * workgroup of the first launch) until the second launch replaces every
+ * entry with the step.  Other arguments as sq_quant_act_pertoken.  Dynamic:
+ * three launches (partial maxima, step, codes); static: one. */
 sq_status sq_quant_act_pertensor(const void* x, sq_dtype xdt, int64_t M, int64_t K,
                                  const float* smooth, const float* step_in, int8_t* xq,
                                  float* x_scale, void* stream);

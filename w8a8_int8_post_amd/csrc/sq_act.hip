@@ -280,12 +280,12 @@ __device__ inline void load_chunk_f32(const typename D::T* x, const float* smoot
     }
 }
 
-// Largest |x_hat| over the tensor, folded into *acc (zeroed beforehand) with
-// an unsigned atomic max (exact and order-free for non-negative floats).
+// Partial maxima of |x_hat|: workgroup b writes the largest value of its
+// grid-stride share to part[b] (the tensor's maximum is that of the parts).
 template <class D, bool SMOOTH, int V>
 __global__ __launch_bounds__(kTensorThreads) void tensor_absmax_kernel(
     const typename D::T* __restrict__ x, const float* __restrict__ smooth, int64_t M, int64_t K,
-    float* __restrict__ acc) {
+    float* __restrict__ part) {
     __shared__ float red[kTensorThreads / 64];
     const int64_t total = M * K / V;
     const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
@@ -306,18 +306,29 @@ __global__ __launch_bounds__(kTensorThreads) void tensor_absmax_kernel(
             }
     }
     m = block_max<kTensorThreads>(m, red);
-    if (threadIdx.x == 0) atomic_max_nonneg(acc, m);
+    if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-// Codes with one step: STATIC -> src[0] is the step, and workgroup 0 also
-// writes it to x_scale[0..M); else src[0] is the tensor's absmax, the step
-// is absmax / 127 and x_scale is written afterwards by fill_scale_kernel.
-template <class D, bool SMOOTH, int V, bool STATIC>
+// One workgroup: the tensor's absmax from the nb partial maxima held in
+// x_scale[0..nb), then x_scale[0..M) <- absmax / 127.  Every read happens
+// before the barriers inside block_max, every write after them.
+__global__ __launch_bounds__(1024) void reduce_fill_kernel(float* x_scale, int nb, int64_t M) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nb; i += 1024) m = __builtin_fmaxf(m, x_scale[i]);
+    m = block_max<1024>(m, red);
+    const float st = quant_step(m);
+    for (int64_t i = threadIdx.x; i < M; i += 1024) x_scale[i] = st;
+}
+
+// Codes with the step src[0]; with FILL, workgroup 0 also writes the step
+// to x_scale[0..M) (src must not lie in x_scale then).
+template <class D, bool SMOOTH, int V, bool FILL>
 __global__ __launch_bounds__(kTensorThreads) void tensor_quant_kernel(
     const typename D::T* __restrict__ x, const float* __restrict__ smooth, int64_t M, int64_t K,
-    const float* __restrict__ src, int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-    const RowStep q = given_step(STATIC ? src[0] : quant_step(src[0]));
-    if (STATIC && blockIdx.x == 0)
+    const float* src, int8_t* __restrict__ xq, float* x_scale) {
+    const RowStep q = given_step(src[0]);
+    if (FILL && blockIdx.x == 0)
         for (int64_t m = threadIdx.x; m < M; m += kTensorThreads) x_scale[m] = q.step;
     const int64_t total = M * K / V;
     const int64_t stride = (int64_t)gridDim.x * kTensorThreads;
@@ -344,35 +355,28 @@ __global__ __launch_bounds__(kTensorThreads) void tensor_quant_kernel(
     }
 }
 
-// x_scale[0] holds the tensor's absmax; every x_scale[m] becomes the step.
-// One workgroup: every thread reads x_scale[0] before any thread writes.
-__global__ __launch_bounds__(1024) void fill_scale_kernel(float* x_scale, int64_t M) {
-    const float v = quant_step(x_scale[0]);
-    __syncthreads();
-    for (int64_t m = threadIdx.x; m < M; m += 1024) x_scale[m] = v;
-}
-
-__global__ void zero_one_kernel(float* p) { *p = 0.0f; }
-
+// Dynamic: partial maxima (at most min(M, 1024) workgroups, into x_scale),
+// their maximum and the step (one workgroup, into every x_scale entry), the
+// codes.  Static: the codes, workgroup 0 writing x_scale.
 template <class D, bool SMOOTH, int V>
 hipError_t pertensor_typed(const void* xv, int64_t M, int64_t K, const float* smooth,
                            const float* step, int8_t* xq, float* x_scale, hipStream_t s) {
     const typename D::T* x = static_cast<const typename D::T*>(xv);
     const int64_t total = M * K / V;
-    int64_t blocks = (total + kTensorThreads * kTensorUnroll - 1) / (kTensorThreads * kTensorUnroll);
+    const int64_t per_block = kTensorThreads * kTensorUnroll;
+    int64_t blocks = (total + per_block - 1) / per_block;
     if (blocks > 256 * 16) blocks = 256 * 16;
-    const float* src = step;
     if (!step) {
-        hipLaunchKernelGGL(zero_one_kernel, dim3(1), dim3(1), 0, s, x_scale);
-        hipLaunchKernelGGL((tensor_absmax_kernel<D, SMOOTH, V>), dim3((unsigned)blocks),
+        int64_t nb = blocks < M ? blocks : M;
+        if (nb > 1024) nb = 1024;
+        hipLaunchKernelGGL((tensor_absmax_kernel<D, SMOOTH, V>), dim3((unsigned)nb),
                            dim3(kTensorThreads), 0, s, x, smooth, M, K, x_scale);
-        src = x_scale;
+        hipLaunchKernelGGL(reduce_fill_kernel, dim3(1), dim3(1024), 0, s, x_scale, (int)nb, M);
         hipLaunchKernelGGL((tensor_quant_kernel<D, SMOOTH, V, false>), dim3((unsigned)blocks),
-                           dim3(kTensorThreads), 0, s, x, smooth, M, K, src, xq, nullptr);
-        hipLaunchKernelGGL(fill_scale_kernel, dim3(1), dim3(1024), 0, s, x_scale, M);
+                           dim3(kTensorThreads), 0, s, x, smooth, M, K, x_scale, xq, x_scale);
     } else {
         hipLaunchKernelGGL((tensor_quant_kernel<D, SMOOTH, V, true>), dim3((unsigned)blocks),
-                           dim3(kTensorThreads), 0, s, x, smooth, M, K, src, xq, x_scale);
+                           dim3(kTensorThreads), 0, s, x, smooth, M, K, step, xq, x_scale);
     }
     return hipGetLastError();
 }
