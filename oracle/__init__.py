@@ -77,6 +77,8 @@ def _load():
         lib.sqref_gemm_i32_sampled.argtypes = [P, P, I, P, I, P, I, P]
         lib.sqref_gemm_i32_sampled.restype = ctypes.c_int
         lib.sqref_dequant.argtypes = [P, P, P, I, I, P]
+        lib.sqref_dequant_bias_act.argtypes = [P, P, P, P, ctypes.c_int, I, I, P]
+        lib.sqref_fold_prev_linear.argtypes = [P, P, I, I, P, P]
         lib.sqref_linear_w8a8.argtypes = [P, P, P, I, I, I, P]
         lib.sqref_linear_w8a8.restype = ctypes.c_int
         _lib = lib
@@ -149,6 +151,19 @@ def smooth_fold(a, w, alpha: float, gamma=None, beta=None):
     w_hat = fold_weight(w, s)
     g, bt = fold_norm(s, gamma, beta)
     return s, w_hat, g, bt
+
+
+def fold_prev_linear(s, w_prev, bias=None):
+    """(W_prev / s per output column [Kp x K] fp32, bias / s or None): the
+    smoothing of the next layer folded into the layer before it."""
+    s = _f32(s)
+    w = _f32(w_prev)
+    Kp, K = w.shape
+    assert s.shape[0] == K
+    out = np.empty((Kp, K), np.float32)
+    b = None if bias is None else _f32(bias).copy()
+    _load().sqref_fold_prev_linear(_ptr(s), _ptr(w), Kp, K, _ptr(out), None if b is None else _ptr(b))
+    return out, b
 
 
 def smooth_activation(x, s):
@@ -266,6 +281,19 @@ def dequant(acc, sx, sw):
     M, N = acc.shape
     y = np.empty((M, N), np.float64)
     _load().sqref_dequant(_ptr(acc), _ptr(sx), _ptr(sw), M, N, _ptr(y))
+    return y
+
+
+def dequant_bias_act(acc, sx, sw, bias=None, relu=False):
+    """acc*sx*sw + bias, then ReLU if asked (double [M x N])."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    sx = _f32(sx)
+    sw = _f32(sw)
+    M, N = acc.shape
+    b = None if bias is None else _f32(bias)
+    y = np.empty((M, N), np.float64)
+    _load().sqref_dequant_bias_act(_ptr(acc), _ptr(sx), _ptr(sw), None if b is None else _ptr(b),
+                                   1 if relu else 0, M, N, _ptr(y))
     return y
 
 

@@ -113,6 +113,24 @@ void sqref_fold_norm(const float* s, int64_t K, float* gamma, float* beta)
     }
 }
 
+/* Offline fold of diag(s)^-1 into a preceding linear layer [P1
+ * 数学的に何をしているのか: the scales may be absorbed by the preceding linear
+ * layer as well as by a LayerNorm].  That layer's output channel j feeds
+ * input channel j of this one, so column j of its weight W_prev [Kp x K]
+ * and its bias_j are divided by s_j (fp32 division); its output is then
+ * X diag(s)^-1 directly.  An elementwise activation f between the two layers
+ * commutes with the division only if f(z / s) = f(z) / s for s > 0 (ReLU and
+ * the identity do).  bias may be NULL; it is updated in place. */
+void sqref_fold_prev_linear(const float* s, const float* w_prev, int64_t Kp, int64_t K,
+                            float* w_out, float* bias)
+{
+    for (int64_t i = 0; i < Kp; ++i)
+        for (int64_t j = 0; j < K; ++j)
+            w_out[i * K + j] = w_prev[i * K + j] / s[j];
+    if (bias)
+        for (int64_t j = 0; j < K; ++j) bias[j] = bias[j] / s[j];
+}
+
 /* X diag(s)^-1 applied at run time instead of folded [P1
  * 数学的に何をしているのか]: x_hat[m,j] = x[m,j] / s_j (fp32 division). */
 void sqref_smooth_activation(const float* x, const float* s, int64_t M, int64_t K, float* x_hat)
@@ -282,6 +300,22 @@ void sqref_dequant(const int32_t* acc, const float* sx, const float* sw, int64_t
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             y[m * N + n] = (double)acc[m * N + n] * (double)sx[m] * (double)sw[n];
+}
+
+/* Scale back followed by the rest of a linear layer: y = acc*sx*sw + bias[n]
+ * (bias over output channels, may be NULL), then max(y, 0) when relu is set,
+ * in double.  The ReLU is the activation a smoothed layer may be folded
+ * through (see sqref_fold_prev_linear). */
+void sqref_dequant_bias_act(const int32_t* acc, const float* sx, const float* sw,
+                            const float* bias, int relu, int64_t M, int64_t N, double* y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)acc[m * N + n] * (double)sx[m] * (double)sw[n];
+            if (bias) v += (double)bias[n];
+            if (relu && !(v > 0.0)) v = 0.0;
+            y[m * N + n] = v;
+        }
 }
 
 /* Whole run-time linear layer for timing: per-token quantisation of X_hat,

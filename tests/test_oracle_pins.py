@@ -401,3 +401,65 @@ def test_pertensor_weight_single_column_is_perchannel(ref):
     assert all((p == q).all() for p, q in zip(ref.quant_weight_pertensor(w),
                                                 ref.quant_weight_perchannel(w)))
 
+
+
+# --------------------------------------------------------------------------
+# Bias / ReLU epilogue and the fold into a preceding linear layer
+
+def test_dequant_bias_relu_hand_example(ref):
+    # token 0: 100*0.5*0.25 - 20 = -7.5 and -40*0.5*2 + 10 = -30;
+    # token 1 (step 2): 100*2*0.25 - 20 = 30 and -40*2*2 + 10 = -150
+    acc = np.array([[100, -40], [100, -40]], np.int32)
+    sx = np.array([0.5, 2.0], np.float32)
+    sw = np.array([0.25, 2.0], np.float32)
+    bias = np.array([-20.0, 10.0], np.float32)
+    assert ref.dequant_bias_act(acc, sx, sw, bias).tolist() == [[-7.5, -30.0], [30.0, -150.0]]
+    assert ref.dequant_bias_act(acc, sx, sw, bias, relu=True).tolist() == [[0.0, 0.0], [30.0, 0.0]]
+    assert ref.dequant_bias_act(acc, sx, sw).tolist() == [[12.5, -40.0], [50.0, -160.0]]
+    assert ref.dequant_bias_act(acc, sx, sw, None, relu=True).tolist() == [[12.5, 0.0], [50.0, 0.0]]
+
+
+def test_dequant_bias_act_reduces_to_dequant(ref):
+    r = np.random.default_rng(21)
+    acc = r.integers(-2 ** 20, 2 ** 20, (5, 7)).astype(np.int32)
+    sx = r.random(5).astype(np.float32)
+    sw = r.random(7).astype(np.float32)
+    y0 = ref.dequant(acc, sx, sw)
+    assert np.array_equal(ref.dequant_bias_act(acc, sx, sw), y0)
+    assert np.array_equal(ref.dequant_bias_act(acc, sx, sw, relu=True), np.maximum(y0, 0.0))
+    b = r.standard_normal(7).astype(np.float32)
+    np.testing.assert_allclose(ref.dequant_bias_act(acc, sx, sw, b), y0 + b.astype(np.float64),
+                               rtol=1e-15, atol=1e-15)
+
+
+def test_fold_into_preceding_linear_through_relu(ref):
+    # relu(x W1' + b1') (diag(s) W2) = relu(x W1 + b1) W2 when W1', b1' are
+    # W1, b1 divided by s per output column (ReLU is positively homogeneous)
+    r = np.random.default_rng(23)
+    T, Kp, K, N = 6, 24, 40, 12
+    x = r.standard_normal((T, Kp))
+    w1 = (0.2 * r.standard_normal((Kp, K))).astype(np.float32)
+    b1 = (0.1 * r.standard_normal(K)).astype(np.float32)
+    w2 = (0.2 * r.standard_normal((K, N))).astype(np.float32)
+    s = np.exp(r.standard_normal(K)).astype(np.float32)
+    w1f, b1f = ref.fold_prev_linear(s, w1, b1)
+    w2f = ref.fold_weight(w2, s)
+    h = np.maximum(x @ w1f.astype(np.float64) + b1f.astype(np.float64), 0.0)
+    lhs = h @ w2f.astype(np.float64)
+    rhs = np.maximum(x @ w1.astype(np.float64) + b1.astype(np.float64), 0.0) @ w2.astype(np.float64)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-5, atol=1e-6)
+    # the folded layer's output is the smoothed activation X diag(s)^-1
+    h0 = np.maximum(x @ w1.astype(np.float64) + b1.astype(np.float64), 0.0)
+    np.testing.assert_allclose(h, h0 / s.astype(np.float64), rtol=1e-5, atol=1e-7)
+    # columns, not rows, are divided: the transposed fold breaks the identity
+    # (a planted mistake the test must be able to see)
+    assert not np.allclose(w1f, w1 / s[:Kp, None] if Kp <= K else w1, rtol=1e-3)
+
+
+def test_fold_prev_linear_without_bias_and_unit_factors(ref):
+    r = np.random.default_rng(24)
+    w = r.standard_normal((9, 5)).astype(np.float32)
+    out, b = ref.fold_prev_linear(np.ones(5, np.float32), w)
+    assert b is None and np.array_equal(out, w)
+    out, b = ref.fold_prev_linear(np.full(5, 2.0, np.float32), w, np.ones(5, np.float32))
+    assert np.array_equal(out, w * np.float32(0.5)) and np.array_equal(b, np.full(5, 0.5, np.float32))
