@@ -78,6 +78,7 @@ def _load():
         lib.sqref_gemm_i32_sampled.restype = ctypes.c_int
         lib.sqref_dequant.argtypes = [P, P, P, I, I, P]
         lib.sqref_dequant_bias_act.argtypes = [P, P, P, P, ctypes.c_int, I, I, P]
+        lib.sqref_dequant_bias_act_f32.argtypes = [P, P, P, P, ctypes.c_int, I, I, P]
         lib.sqref_fold_prev_linear.argtypes = [P, P, I, I, P, P]
         lib.sqref_linear_w8a8.argtypes = [P, P, P, I, I, I, P]
         lib.sqref_linear_w8a8.restype = ctypes.c_int
@@ -294,6 +295,22 @@ def dequant_bias_act(acc, sx, sw, bias=None, relu=False):
     y = np.empty((M, N), np.float64)
     _load().sqref_dequant_bias_act(_ptr(acc), _ptr(sx), _ptr(sw), None if b is None else _ptr(b),
                                    1 if relu else 0, M, N, _ptr(y))
+    return y
+
+
+def dequant_bias_act_f32(acc, sx, sw, bias=None, relu=False):
+    """The same in fp32: RN(RN(fp32(acc) * sx) * sw + bias) with one rounding
+    for the multiply-add, then ReLU (float32 [M x N]).  Used where the output
+    feeds a quantiser, so that the codes are decided in fp32."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    sx = _f32(sx)
+    sw = _f32(sw)
+    M, N = acc.shape
+    b = None if bias is None else _f32(bias)
+    y = np.empty((M, N), np.float32)
+    _load().sqref_dequant_bias_act_f32(_ptr(acc), _ptr(sx), _ptr(sw),
+                                       None if b is None else _ptr(b), 1 if relu else 0, M, N,
+                                       _ptr(y))
     return y
 
 

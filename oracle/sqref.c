@@ -318,6 +318,25 @@ void sqref_dequant_bias_act(const int32_t* acc, const float* sx, const float* sw
         }
 }
 
+/* The same scale back with bias and ReLU, evaluated in fp32 in a fixed order
+ * so that a quantised code taken from its output (the next layer's input)
+ * is decided in the precision the layer computes in: f = fp32(acc) * sx[m]
+ * (one fp32 rounding), v = f * sw[n] + bias[n] with a single rounding
+ * (C99 fmaf), then ReLU as v > 0 ? v : +0.  The pages fix no precision for
+ * this step; this is fp32 with one rounding per operation. */
+void sqref_dequant_bias_act_f32(const int32_t* acc, const float* sx, const float* sw,
+                                const float* bias, int relu, int64_t M, int64_t N, float* y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float f = (float)acc[m * N + n];
+            f = f * sx[m];
+            float v = fmaf(f, sw[n], bias ? bias[n] : 0.0f);
+            if (relu && !(v > 0.0f)) v = 0.0f;
+            y[m * N + n] = v;
+        }
+}
+
 /* Whole run-time linear layer for timing: per-token quantisation of X_hat,
  * INT8 GEMM and scale back, one token row at a time (rows are independent).
  * xq_row / acc_row are caller scratch of K and N entries per thread slot;

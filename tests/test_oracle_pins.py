@@ -463,3 +463,40 @@ def test_fold_prev_linear_without_bias_and_unit_factors(ref):
     assert b is None and np.array_equal(out, w)
     out, b = ref.fold_prev_linear(np.full(5, 2.0, np.float32), w, np.ones(5, np.float32))
     assert np.array_equal(out, w * np.float32(0.5)) and np.array_equal(b, np.full(5, 0.5, np.float32))
+
+
+def test_dequant_bias_act_f32_hand_and_single_rounding(ref):
+    acc = np.array([[100, -40], [100, -40]], np.int32)
+    sx = np.array([0.5, 2.0], np.float32)
+    sw = np.array([0.25, 2.0], np.float32)
+    bias = np.array([-20.0, 10.0], np.float32)
+    y = ref.dequant_bias_act_f32(acc, sx, sw, bias, relu=True)
+    assert y.dtype == np.float32 and y.tolist() == [[0.0, 0.0], [30.0, 0.0]]
+    assert ref.dequant_bias_act_f32(acc, sx, sw, bias).tolist() == [[-7.5, -30.0], [30.0, -150.0]]
+    # f = 1 + 2^-12, sw = 1 + 2^-12: f*sw = 1 + 2^-11 + 2^-24 exactly; with
+    # bias -1 one rounding keeps 2^-11 + 2^-24, while a rounded product (a tie,
+    # to even: 1 + 2^-11) minus 1 would give 2^-11
+    e = np.float32(1 + 2.0 ** -12)
+    y = ref.dequant_bias_act_f32(np.array([[1]], np.int32), np.array([e]), np.array([e]),
+                                 np.array([-1.0], np.float32))
+    assert float(y[0, 0]) == 2.0 ** -11 + 2.0 ** -24
+    # relu returns +0 for negative and zero values
+    y = ref.dequant_bias_act_f32(np.array([[-3, 0]], np.int32), np.array([1.0], np.float32),
+                                 np.array([1.0, 1.0], np.float32), None, relu=True)
+    assert y.tolist() == [[0.0, 0.0]] and not np.signbit(y).any()
+
+
+def test_dequant_bias_act_f32_within_fp32_bound_of_exact(ref):
+    # |y32 - y| <= 2^-24 (|acc sx sw| + |y|) (one rounding for acc*sx, one for
+    # the multiply-add; |acc| < 2^24 converts exactly), checked against the
+    # double version
+    r = np.random.default_rng(25)
+    acc = r.integers(-2 ** 23, 2 ** 23, (32, 48)).astype(np.int32)
+    sx = (r.random(32) * 1e-3).astype(np.float32)
+    sw = (r.random(48) * 1e-3).astype(np.float32)
+    b = (r.standard_normal(48) * 3).astype(np.float32)
+    for relu in (False, True):
+        y = ref.dequant_bias_act(acc, sx, sw, b, relu)
+        p = np.abs(ref.dequant(acc, sx, sw))
+        y32 = ref.dequant_bias_act_f32(acc, sx, sw, b, relu).astype(np.float64)
+        assert (np.abs(y32 - y) <= 2.0 ** -24 * (p + np.abs(y)) * (1 + 1e-9)).all()
