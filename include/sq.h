@@ -56,10 +56,14 @@ typedef enum {
     SQ_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned */
     SQ_ERR_ALPHA = 6,       /* alpha outside [0, 1] or not finite */
     SQ_ERR_HIP = 7,         /* the HIP runtime reported a launch error */
-    SQ_ERR_ALIAS = 8        /* two buffers overlap where the entry point forbids it */
+    SQ_ERR_ALIAS = 8,       /* two buffers overlap where the entry point forbids it */
+    SQ_ERR_ACT = 9          /* activation code not one of sq_act */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
+
+/* Elementwise activation applied after the bias (sq_w8a8_gemm_dequant_ex). */
+typedef enum { SQ_ACT_NONE = 0, SQ_ACT_RELU = 1 } sq_act;
 
 /* |sum_k xq*wq| <= K * 127 * 127 < 2^31 holds for K <= 133144. */
 #define SQ_MAX_K 133144
@@ -95,6 +99,20 @@ sq_status sq_calibrate_absmax(const void* x, sq_dtype xdt, int64_t T, int64_t K,
 sq_status sq_smooth_fold(const float* a, const void* w, sq_dtype wdt, int64_t K, int64_t N,
                          double alpha, float* s_out, float* w_out, float* gamma, float* beta,
                          void* stream);
+
+/* Offline fold of this layer's smoothing into a preceding linear layer [P1
+ * 数学的に何をしているのか: diag(s)^-1 may be absorbed by the preceding linear
+ * layer instead of a LayerNorm].  That layer's output channel j feeds input
+ * channel j here, so
+ *   w_out[i, j] = fp32(w_prev[i, j]) / s[j]      (fp32 division)
+ *   bias[j]     = bias[j] / s[j]                 (in place; bias may be NULL)
+ * and its output is X diag(s)^-1 directly.  An activation between the two
+ * layers must commute with the division (f(z / s) = f(z) / s for s > 0:
+ * ReLU does, GELU does not).  s: fp32 [K] (sq_smooth_fold's s_out of the
+ * next layer).  w_prev: [Kp x K] of dtype wdt (its input channels in rows,
+ * the convention of sq_smooth_fold).  w_out: fp32 [Kp x K]. */
+sq_status sq_fold_prev_linear(const float* s, const void* w_prev, sq_dtype wdt, int64_t Kp,
+                              int64_t K, float* w_out, float* bias, void* stream);
 
 /* Per-output-channel weight quantisation (each column n of w gets its own
  * step; P1 推論方法 names per-tensor weights for O1, the special case of a
@@ -165,6 +183,20 @@ sq_status sq_w8a8_gemm_dequant(const int8_t* xq, const float* x_scale, const int
                                const float* w_scale, int64_t M, int64_t N, int64_t K,
                                void* y, sq_dtype ydt, void* stream);
 
+/* The scale back extended by the rest of a linear layer [P1
+ * 数学的に何をしているのか: a smoothed layer whose factors are folded into the
+ * layer before it; SmoothQuant's target models put a bias and an activation
+ * between such layers]:
+ *   y[m, n] = ydt( act( fma(fp32(acc) * x_scale[m], w_scale[n], bias[n]) ) )
+ * i.e. RN(RN(acc * sx) * sw + bias) in one fp32 FMA, then act: SQ_ACT_NONE,
+ * or SQ_ACT_RELU (v > 0 ? v : +0), then round to nearest even to ydt.
+ * bias: fp32 [N], 16-byte aligned, or NULL (treated as zeros).  act other
+ * than sq_act's values: SQ_ERR_ACT.  Everything else as sq_w8a8_gemm_dequant
+ * (same kernels and tiling, the epilogue extended). */
+sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, const float* bias, int act, int64_t M,
+                                  int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream);
+
 /* ------------------------------------------------------------- auxiliary */
 
 /* The INT8 GEMM's raw accumulators, for exact checking of the GEMM kernels:
@@ -201,6 +233,13 @@ sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
                                       int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream);
 sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,
                                   int64_t K, int32_t* acc, void* stream);
+
+/* sq_w8a8_gemm_dequant_ex with the weights in the packed layout; identical
+ * results.  K % 128 == 0. */
+sq_status sq_w8a8_gemm_dequant_packed_ex(const int8_t* xq, const float* x_scale,
+                                         const int8_t* wq_packed, const float* w_scale,
+                                         const float* bias, int act, int64_t M, int64_t N,
+                                         int64_t K, void* y, sq_dtype ydt, void* stream);
 
 /* The whole run-time layer on packed weights: per-token quantisation of x
  * (exactly sq_quant_act_pertoken with smooth = NULL, writing xq and x_scale)

@@ -107,3 +107,19 @@ def test_pertensor_entry_points_validate(lib):
     assert lib.sq_quant_weight_pertensor(A, 1, 4, -3, A, A, None) == 2
     assert lib.sq_quant_weight_pertensor(A, 9, 4, 4, A, A, None) == 3
     assert lib.sq_quant_weight_pertensor(A, 1, 4, 4, A, A + 2, None) == 5
+
+
+def test_epilogue_entry_points_validate(lib):
+    # sq_w8a8_gemm_dequant_ex(xq, sx, wq, sw, bias, act, M, N, K, y, ydt, stream)
+    assert lib.sq_w8a8_gemm_dequant_ex(A, A, A, A, None, 2, 4, 4, 16, A, 1, None) == 9
+    assert lib.sq_w8a8_gemm_dequant_ex(A, A, A, A, None, -1, 4, 4, 16, A, 1, None) == 9
+    assert lib.sq_w8a8_gemm_dequant_ex(A, A, None, A, None, 0, 4, 4, 16, A, 1, None) == 1
+    assert lib.sq_w8a8_gemm_dequant_ex(A, A, A, A, A + 4, 1, 4, 4, 16, A, 1, None) == 5
+    assert lib.sq_w8a8_gemm_dequant_ex(A, A, A, A, None, 1, 4, 4, 16, A, 7, None) == 3
+    assert lib.sq_w8a8_gemm_dequant_packed_ex(A, A, A, A, None, 1, 4, 4, 64, A, 1, None) == 2
+    assert lib.sq_w8a8_gemm_dequant_packed_ex(A, A, A, A, None, 3, 4, 4, 128, A, 1, None) == 9
+    # sq_fold_prev_linear(s, w_prev, wdt, Kp, K, w_out, bias, stream)
+    assert lib.sq_fold_prev_linear(None, A, 0, 4, 4, A, None, None) == 1
+    assert lib.sq_fold_prev_linear(A, A, 0, 0, 4, A, None, None) == 2
+    assert lib.sq_fold_prev_linear(A, A, 4, 4, 4, A, None, None) == 3
+    assert lib.sq_fold_prev_linear(A, A, 0, 4, 4, A, A + 8, None) == 5

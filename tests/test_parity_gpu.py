@@ -200,8 +200,18 @@ def test_gemm_dequant(ref, dev, M, N, K, ydt):
                              _gpu(torch.from_numpy(wq), dev), _gpu(torch.from_numpy(sw), dev),
                              DT[ydt])
     torch.cuda.synchronize()
-    same = assert_y_close(y, ref.dequant(ref.gemm_i32(xq, wq), sx, sw))
+    acc_r = ref.gemm_i32(xq, wq)
+    same = assert_y_close(y, ref.dequant(acc_r, sx, sw))
     log("  bit-equal to RNE(oracle):", same)
+    _assert_fp32_order(y, ref, acc_r, sx, sw)
+
+
+def _assert_fp32_order(y, ref, acc, sx, sw):
+    """The scale back is RN(RN(fp32(acc) * sx) * sw) in fp32, then one rounding
+    to y's dtype: bit-equal to the oracle's fp32 evaluation of that order."""
+    y32 = torch.from_numpy(ref.dequant_bias_act_f32(acc, sx, sw)).to(y.dtype)
+    bits = torch.int16 if y.dtype != torch.float32 else torch.int32
+    assert_equal(y.cpu().view(bits), y32.view(bits).numpy(), "y (fp32 order, bits)")
 
 
 # --------------------------------------------------------------- packed weights
@@ -245,6 +255,7 @@ def test_gemm_packed(ref, dev, M, N, K):
     acc_r = ref.gemm_i32(xq, wq)
     assert_equal(acc, acc_r, "acc (packed)")
     assert_y_close(y, ref.dequant(acc_r, sx, sw), "y (packed)")
+    _assert_fp32_order(y, ref, acc_r, sx, sw)
 
 
 # ------------------------------------------- whole run-time layer (packed)

@@ -28,7 +28,9 @@ __all__ = [
     "w8a8_gemm_dequant_packed", "w8a8_gemm_i32_packed", "linear_w8a8_packed",
     "sq_w8a8_linear_packed", "sq_w8a8_linear_packed_static", "sq_quant_act_pertensor", "sq_static_act_step",
     "sq_quant_weight_pertensor", "quant_act_pertensor", "static_act_step",
-    "quant_weight_pertensor", "linear_w8a8_packed_static",
+    "quant_weight_pertensor", "linear_w8a8_packed_static", "sq_w8a8_gemm_dequant_ex",
+    "sq_w8a8_gemm_dequant_packed_ex", "sq_fold_prev_linear", "w8a8_gemm_dequant_ex",
+    "w8a8_gemm_dequant_packed_ex", "fold_prev_linear", "SQ_ACT_NONE", "SQ_ACT_RELU",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -37,8 +39,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE",
           4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP",
-          8: "SQ_ERR_ALIAS"}
+          8: "SQ_ERR_ALIAS", 9: "SQ_ERR_ACT"}
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
+SQ_ACT_NONE, SQ_ACT_RELU = 0, 1
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
 MAX_K = 133144
 
@@ -74,6 +77,9 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_linear_packed": [P, E, I64, I64, P, P, I64, P, P, P, E, P],
             "sq_w8a8_linear_packed_static": [P, E, I64, I64, P, P, I64, P, P, P, P, E, P],
             "sq_quant_act_pertensor": [P, E, I64, I64, P, P, P, P, P],
+            "sq_w8a8_gemm_dequant_ex": [P, P, P, P, P, E, I64, I64, I64, P, E, P],
+            "sq_w8a8_gemm_dequant_packed_ex": [P, P, P, P, P, E, I64, I64, I64, P, E, P],
+            "sq_fold_prev_linear": [P, P, E, I64, I64, P, P, P],
             "sq_static_act_step": [P, P, I64, P, P],
             "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
         }
@@ -194,6 +200,17 @@ def sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream=None):
           _dev(y, "y"), _DT[y.dtype], _stream(xq, stream))
 
 
+def sq_w8a8_gemm_dequant_ex(xq, x_scale, wq, w_scale, bias, act, y, stream=None):
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K or tuple(y.shape) != (M, N) or (bias is not None and bias.shape[0] != N):
+        raise ValueError("shape mismatch")
+    _call("sq_w8a8_gemm_dequant_ex", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq, "wq", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), _opt(bias, "bias", torch.float32), int(act),
+          M, N, K, _dev(y, "y"), _DT[y.dtype], _stream(xq, stream))
+
+
 def sq_w8a8_gemm_i32(xq, wq, acc, stream=None):
     M, K = xq.shape
     N = wq.shape[0]
@@ -237,6 +254,27 @@ def sq_w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, N, y, stream=No
           _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
           _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype],
           _stream(xq, stream))
+
+
+def sq_w8a8_gemm_dequant_packed_ex(xq, x_scale, wq_packed, w_scale, bias, act, N, y,
+                                   stream=None):
+    M, K = xq.shape
+    if tuple(y.shape) != (M, N) or (bias is not None and bias.shape[0] != N):
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_gemm_dequant_packed_ex", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), _opt(bias, "bias", torch.float32), int(act),
+          M, N, K, _dev(y, "y"), _DT[y.dtype], _stream(xq, stream))
+
+
+def sq_fold_prev_linear(s, w_prev, w_out, bias=None, stream=None):
+    Kp, K = w_prev.shape
+    if s.shape[0] != K or tuple(w_out.shape) != (Kp, K) or (bias is not None and bias.shape[0] != K):
+        raise ValueError("shape mismatch")
+    _call("sq_fold_prev_linear", _dev(s, "s", torch.float32), _dev(w_prev, "w_prev"),
+          _DT[w_prev.dtype], Kp, K, _dev(w_out, "w_out", torch.float32),
+          _opt(bias, "bias", torch.float32), _stream(w_prev, stream))
 
 
 def sq_w8a8_gemm_i32_packed(xq, wq_packed, N, acc, stream=None):
@@ -324,6 +362,28 @@ def w8a8_gemm_dequant(xq, x_scale, wq, w_scale, out_dtype=torch.float16, stream=
     y = torch.empty(xq.shape[0], wq.shape[0], dtype=out_dtype, device=xq.device)
     sq_w8a8_gemm_dequant(xq, x_scale, wq, w_scale, y, stream)
     return y
+
+
+def w8a8_gemm_dequant_ex(xq, x_scale, wq, w_scale, bias=None, act=SQ_ACT_NONE,
+                         out_dtype=torch.float16, stream=None):
+    y = torch.empty(xq.shape[0], wq.shape[0], dtype=out_dtype, device=xq.device)
+    sq_w8a8_gemm_dequant_ex(xq, x_scale, wq, w_scale, bias, act, y, stream)
+    return y
+
+
+def w8a8_gemm_dequant_packed_ex(xq, x_scale, wq_packed, w_scale, bias=None, act=SQ_ACT_NONE,
+                                out_dtype=torch.float16, stream=None):
+    N = w_scale.shape[0]
+    y = torch.empty(xq.shape[0], N, dtype=out_dtype, device=xq.device)
+    sq_w8a8_gemm_dequant_packed_ex(xq, x_scale, wq_packed, w_scale, bias, act, N, y, stream)
+    return y
+
+
+def fold_prev_linear(s, w_prev, bias=None, stream=None):
+    """(W_prev / s per output column, fp32; bias is divided in place)."""
+    out = torch.empty(w_prev.shape, dtype=torch.float32, device=w_prev.device)
+    sq_fold_prev_linear(s, w_prev, out, bias, stream)
+    return out
 
 
 def w8a8_gemm_i32(xq, wq, stream=None):

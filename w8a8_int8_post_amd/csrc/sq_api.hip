@@ -71,6 +71,17 @@ sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t 
         sq::launch_act_quant(x, to_dt(xdt), M, K, smooth, xq, x_scale, as_stream(stream)));
 }
 
+sq_status sq_fold_prev_linear(const float* s, const void* w_prev, sq_dtype wdt, int64_t Kp,
+                              int64_t K, float* w_out, float* bias, void* stream) {
+    if (!s || !w_prev || !w_out) return SQ_ERR_NULL;
+    if (!dims_ok(Kp, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(wdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(s) || !aligned16(w_prev) || !aligned16(w_out) || (bias && !aligned16(bias)))
+        return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_fold_prev_linear(s, w_prev, to_dt(wdt), Kp, K, w_out, bias,
+                                                  as_stream(stream)));
+}
+
 sq_status sq_quant_weight_pertensor(const void* w, sq_dtype wdt, int64_t K, int64_t N,
                                     int8_t* wq, float* w_scale, void* stream) {
     if (!w || !wq || !w_scale) return SQ_ERR_NULL;
@@ -160,6 +171,45 @@ sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
     sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
     return hip_status(sq::launch_gemm_packed(xq, x_scale, wq_packed, w_scale, M, N, K, y, out,
                                              as_stream(stream)));
+}
+
+sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, const float* bias, int act, int64_t M,
+                                  int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (act != SQ_ACT_NONE && act != SQ_ACT_RELU) return SQ_ERR_ACT;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) ||
+        !aligned16(y) || (bias && !aligned16(bias)))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    sq::Epi epi;
+    epi.bias = bias;
+    epi.relu = act == SQ_ACT_RELU;
+    return hip_status(
+        sq::launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y, out, as_stream(stream), epi));
+}
+
+sq_status sq_w8a8_gemm_dequant_packed_ex(const int8_t* xq, const float* x_scale,
+                                         const int8_t* wq_packed, const float* w_scale,
+                                         const float* bias, int act, int64_t M, int64_t N,
+                                         int64_t K, void* y, sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq_packed || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (act != SQ_ACT_NONE && act != SQ_ACT_RELU) return SQ_ERR_ACT;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq_packed) || !aligned16(w_scale) ||
+        !aligned16(y) || (bias && !aligned16(bias)))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    sq::Epi epi;
+    epi.bias = bias;
+    epi.relu = act == SQ_ACT_RELU;
+    return hip_status(sq::launch_gemm_packed(xq, x_scale, wq_packed, w_scale, M, N, K, y, out,
+                                             as_stream(stream), epi));
 }
 
 sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,

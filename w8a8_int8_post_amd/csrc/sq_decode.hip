@@ -99,10 +99,10 @@ __device__ inline void stream_k(v4i (&acc)[TB], v4i (&w0)[U][4], v4i (&w1)[U][4]
 // Cross-wave sum of the accumulators and the scaled store.  16 x 16
 // accumulator layout: lane l, element q holds row 4*(l/16) + q (output
 // channel) and column l%16 (token).  sxf(tok) gives the token's step.
-template <int TB, int NW, Out O, class SX>
+template <int TB, int NW, Out O, class SX, bool EXT = false>
 __device__ inline void reduce_store(v4i (*red)[TB][64], const v4i (&acc)[TB], int wave, int lane,
                                     int n0, int M, int N, const float* __restrict__ sw, void* Y,
-                                    const SX& sxf) {
+                                    const SX& sxf, const Epi& epi = Epi()) {
 #pragma unroll
     for (int b = 0; b < TB; ++b) red[wave][b][lane] = acc[b];
     __syncthreads();
@@ -120,7 +120,7 @@ __device__ inline void reduce_store(v4i (*red)[TB][64], const v4i (&acc)[TB], in
                 const int n = n0 + 4 * g + qq;
                 if (n < N) {
                     const float swn = (O != Out::I32) ? sw[n] : 0.0f;
-                    store_out<O>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn);
+                    store_out_ext<O, EXT>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn, epi, n);
                 }
             }
         }
@@ -131,10 +131,10 @@ __device__ inline void reduce_store(v4i (*red)[TB][64], const v4i (&acc)[TB], in
 // Row-major weights [N x K] (M <= 16 * TB).  KVEC: K % 16 == 0, so each
 // 16-byte chunk is wholly inside or outside a row and loads from a clamped
 // address; otherwise chunks are assembled byte by byte with masking.
-template <int TB, int NW, int U, Out O, bool KVEC>
+template <int TB, int NW, int U, Out O, bool KVEC, bool EXT>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     __shared__ v4i red[NW][TB][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -169,16 +169,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     v4i w0[U][4], w1[U][4];
     load_stage<NW, U>(w0, wave, KG, wfrag);  // clamped: valid for any wave
     stream_k<TB, NW, U>(acc, w0, w1, wave, nsteps, KG, wfrag, xfrag);
-    reduce_store<TB, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
-                            [&](int tok) { return sx[tok]; });
+    auto sxf = [&](int tok) { return sx[tok]; };
+    reduce_store<TB, NW, O, decltype(sxf), EXT>(red, acc, wave, lane, n0, M, N, sw, Y, sxf, epi);
 }
 
 // Fragment-packed weights (K % 64 == 0): each weight fragment is one
 // contiguous, non-temporal 1 KB wave load.
-template <int TB, int NW, int U, Out O>
+template <int TB, int NW, int U, Out O, bool EXT>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     __shared__ v4i red[NW][TB][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
     v4i w0[U][4], w1[U][4];
     load_stage<NW, U>(w0, wave, KG, wfrag);  // clamped: valid for any wave
     stream_k<TB, NW, U>(acc, w0, w1, wave, nsteps, KG, wfrag, xfrag);
-    reduce_store<TB, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
-                            [&](int tok) { return sx[tok]; });
+    auto sxf = [&](int tok) { return sx[tok]; };
+    reduce_store<TB, NW, O, decltype(sxf), EXT>(red, acc, wave, lane, n0, M, N, sw, Y, sxf, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -442,41 +442,45 @@ hipError_t fused_dt(const void* x, Dt xdt, const int8_t* wp, const float* sw, co
     return hipErrorInvalidValue;
 }
 
-template <int TB, Out O>
+template <int TB, Out O, bool EXT>
 hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                     int N, int K, void* y, bool packed, hipStream_t s) {
+                     int N, int K, void* y, bool packed, Epi epi, hipStream_t s) {
     const dim3 grid((unsigned)((N + 15) / 16)), block(kNW * 64);
     if (packed)
-        hipLaunchKernelGGL((gemm_skinny_packed_kernel<TB, kNW, kU, O>), grid, block, 0, s, xq, w,
-                           sx, sw, y, M, N, K);
+        hipLaunchKernelGGL((gemm_skinny_packed_kernel<TB, kNW, kU, O, EXT>), grid, block, 0, s, xq,
+                           w, sx, sw, y, M, N, K, epi);
     else if (K % 16 == 0)
-        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, true>), grid, block, 0, s, xq, w, sx,
-                           sw, y, M, N, K);
+        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, true, EXT>), grid, block, 0, s, xq,
+                           w, sx, sw, y, M, N, K, epi);
     else
-        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, false>), grid, block, 0, s, xq, w,
-                           sx, sw, y, M, N, K);
+        hipLaunchKernelGGL((gemm_skinny_kernel<TB, kNW, kU, O, false, EXT>), grid, block, 0, s, xq,
+                           w, sx, sw, y, M, N, K, epi);
     return hipGetLastError();
 }
 
-template <Out O>
+template <Out O, bool EXT>
 hipError_t skinny_out(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                      int N, int K, void* y, bool packed, hipStream_t s) {
-    if (M <= 16) return skinny_tb<1, O>(xq, sx, w, sw, M, N, K, y, packed, s);
-    if (M <= 32) return skinny_tb<2, O>(xq, sx, w, sw, M, N, K, y, packed, s);
-    if (M <= 48) return skinny_tb<3, O>(xq, sx, w, sw, M, N, K, y, packed, s);
-    return skinny_tb<4, O>(xq, sx, w, sw, M, N, K, y, packed, s);
+                      int N, int K, void* y, bool packed, Epi epi, hipStream_t s) {
+    if (M <= 16) return skinny_tb<1, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
+    if (M <= 32) return skinny_tb<2, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
+    if (M <= 48) return skinny_tb<3, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
+    return skinny_tb<4, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
-                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s) {
+                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s,
+                         Epi epi) {
+#define SQ_SK(O, E) return skinny_out<O, E>(xq, sx, w, sw, M, N, K, y, packed, epi, s)
+    const bool ext = epi.on();
     switch (out) {
-        case Out::I32: return skinny_out<Out::I32>(xq, sx, w, sw, M, N, K, y, packed, s);
-        case Out::F16: return skinny_out<Out::F16>(xq, sx, w, sw, M, N, K, y, packed, s);
-        case Out::BF16: return skinny_out<Out::BF16>(xq, sx, w, sw, M, N, K, y, packed, s);
-        case Out::F32: return skinny_out<Out::F32>(xq, sx, w, sw, M, N, K, y, packed, s);
+        case Out::I32: SQ_SK(Out::I32, false);
+        case Out::F16: if (ext) SQ_SK(Out::F16, true); SQ_SK(Out::F16, false);
+        case Out::BF16: if (ext) SQ_SK(Out::BF16, true); SQ_SK(Out::BF16, false);
+        case Out::F32: if (ext) SQ_SK(Out::F32, true); SQ_SK(Out::F32, false);
     }
+#undef SQ_SK
     return hipErrorInvalidValue;
 }
 

@@ -38,10 +38,10 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Tiled kernel.
-template <int BM, int BN, int BK, int WM, int WN, int SWS, Out O, bool KVEC>
+template <int BM, int BN, int BK, int WM, int WN, int SWS, Out O, bool KVEC, bool EXT>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_tiled_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -161,7 +161,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_tiled_kern
                 const int m = m0 + wm0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
                 if (nok && m < M) {
                     const float sxm = (O != Out::I32) ? sx[m] : 0.0f;
-                    store_out<O>(Y, (int64_t)m * N + n, acc[i][j][r], sxm, swn);
+                    store_out_ext<O, EXT>(Y, (int64_t)m * N + n, acc[i][j][r], sxm, swn, epi, n);
                 }
             }
         }
@@ -188,10 +188,10 @@ __device__ inline void wait_vm() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1,
-          int NSTAGE = 2>
+          int NSTAGE = 2, bool EXT = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     constexpr int SWS = 1, GM = 8;
     constexpr int KGT = BK / 64;  // packed k-groups per K tile
     static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
@@ -352,7 +352,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                     for (int e = 0; e < 4; ++e)
                         if (n + e < N) {
                             const float swn = (O == Out::F32) ? sw[n + e] : 0.0f;
-                            store_out<O>(Y, (int64_t)m * N + n + e, acc[j][i][4 * g + e], sxm, swn);
+                            store_out_ext<O, EXT>(Y, (int64_t)m * N + n + e, acc[j][i][4 * g + e],
+                                                  sxm, swn, epi, n + e);
                         }
                 }
         }
@@ -369,7 +370,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
         // (four float4) are live next to the accumulators.
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            float4 swv[4];
+            float4 swv[4], bv[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
@@ -378,6 +379,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                 else
                     swv[g] = make_float4(n < N ? sw[n] : 0.f, n + 1 < N ? sw[n + 1] : 0.f,
                                          n + 2 < N ? sw[n + 2] : 0.f, 0.f);
+                if constexpr (EXT) {
+                    const float* bb = epi.bias;
+                    if (!bb)
+                        bv[g] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    else if (n + 3 < N)
+                        bv[g] = *reinterpret_cast<const float4*>(bb + n);
+                    else
+                        bv[g] = make_float4(n < N ? bb[n] : 0.f, n + 1 < N ? bb[n + 1] : 0.f,
+                                            n + 2 < N ? bb[n + 2] : 0.f, 0.f);
+                }
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -387,10 +398,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                     const int nl = wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
                     const float4 w4 = swv[g];
                     T o[4];
-                    o[0] = Half<O>::cvt(dequant(acc[j][i][4 * g + 0], sxv[i], w4.x));
-                    o[1] = Half<O>::cvt(dequant(acc[j][i][4 * g + 1], sxv[i], w4.y));
-                    o[2] = Half<O>::cvt(dequant(acc[j][i][4 * g + 2], sxv[i], w4.z));
-                    o[3] = Half<O>::cvt(dequant(acc[j][i][4 * g + 3], sxv[i], w4.w));
+                    if constexpr (EXT) {
+                        const float4 b4 = bv[g];
+                        const int rl = epi.relu;
+                        o[0] = Half<O>::cvt(dequant_ext(acc[j][i][4 * g + 0], sxv[i], w4.x, b4.x, rl));
+                        o[1] = Half<O>::cvt(dequant_ext(acc[j][i][4 * g + 1], sxv[i], w4.y, b4.y, rl));
+                        o[2] = Half<O>::cvt(dequant_ext(acc[j][i][4 * g + 2], sxv[i], w4.z, b4.z, rl));
+                        o[3] = Half<O>::cvt(dequant_ext(acc[j][i][4 * g + 3], sxv[i], w4.w, b4.w, rl));
+                    } else {
+                        o[0] = Half<O>::cvt(dequant(acc[j][i][4 * g + 0], sxv[i], w4.x));
+                        o[1] = Half<O>::cvt(dequant(acc[j][i][4 * g + 1], sxv[i], w4.y));
+                        o[2] = Half<O>::cvt(dequant(acc[j][i][4 * g + 2], sxv[i], w4.z));
+                        o[3] = Half<O>::cvt(dequant(acc[j][i][4 * g + 3], sxv[i], w4.w));
+                    }
                     *reinterpret_cast<uint2*>(smem + ml * EPI_LD + nl * 2) =
                         *reinterpret_cast<const uint2*>(o);
                 }
@@ -466,22 +486,25 @@ int pick_tile(int M, int N) {
     return best;
 }
 
-template <Out O, bool PACKED>
+template <Out O, bool PACKED, bool EXT>
 hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                      int N, int K, void* y, hipStream_t s) {
+                      int N, int K, void* y, Epi epi, hipStream_t s) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     switch (pick_tile(M, N)) {
         case 0:
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2>),
-                               dim3(tiles(256, 256)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(256, 256)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                               epi);
             break;
         case 1:
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 192, 128, 64, 96, O, PACKED, 1, 2>),
-                               dim3(tiles(256, 192)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K);
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(256, 192)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
+                               epi);
             break;
         default:
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2>),
-                               dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K);
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2, EXT>),
+                               dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                               epi);
             break;
     }
     return hipGetLastError();
@@ -509,34 +532,35 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const int8_t* __restri
     }
 }
 
-template <Out O>
+template <Out O, bool EXT>
 hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t* wp,
-                                const float* sw, int M, int N, int K, void* y, hipStream_t s) {
-    if (M <= 64) return launch_skinny(xq, sx, wp, sw, M, N, K, y, O, true, s);
-    return launch_dma<O, true>(xq, sx, wp, sw, M, N, K, y, s);
+                                const float* sw, int M, int N, int K, void* y, Epi epi,
+                                hipStream_t s) {
+    if (M <= 64) return launch_skinny(xq, sx, wp, sw, M, N, K, y, O, true, s, epi);
+    return launch_dma<O, true, EXT>(xq, sx, wp, sw, M, N, K, y, epi, s);
 }
 
-template <Out O, bool KVEC>
+template <Out O, bool KVEC, bool EXT>
 hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                         int M, int N, int K, void* y, hipStream_t s) {
+                         int M, int N, int K, void* y, Epi epi, hipStream_t s) {
     if (M <= 64) {
-        return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s);
+        return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s, epi);
     } else if (KVEC && K % 128 == 0) {
-        return launch_dma<O, false>(xq, sx, wq, sw, M, N, K, y, s);
+        return launch_dma<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
     } else {
         constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, SWS = 1;
         const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, BK, WM, WN, SWS, O, KVEC>), dim3(tiles),
-                           dim3((BM / WM) * (BN / WN) * 64), 0, s, xq, wq, sx, sw, y, M, N, K);
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, BK, WM, WN, SWS, O, KVEC, EXT>), dim3(tiles),
+                           dim3((BM / WM) * (BN / WN) * 64), 0, s, xq, wq, sx, sw, y, M, N, K, epi);
     }
     return hipGetLastError();
 }
 
-template <Out O>
+template <Out O, bool EXT>
 hipError_t gemm_out(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M,
-                    int N, int K, void* y, hipStream_t s) {
-    if (K % 16 == 0) return gemm_dispatch<O, true>(xq, sx, wq, sw, M, N, K, y, s);
-    return gemm_dispatch<O, false>(xq, sx, wq, sw, M, N, K, y, s);
+                    int N, int K, void* y, Epi epi, hipStream_t s) {
+    if (K % 16 == 0) return gemm_dispatch<O, true, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
+    return gemm_dispatch<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
 }
 
 }  // namespace
@@ -554,27 +578,33 @@ hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp
 
 hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8_t* wp,
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
-                              Out out, hipStream_t s) {
+                              Out out, hipStream_t s, Epi epi) {
     const int m = (int)M, n = (int)N, k = (int)K;
+#define SQ_PK(O, E) return gemm_packed_dispatch<O, E>(xq, x_scale, wp, w_scale, m, n, k, y, epi, s)
+    const bool ext = epi.on();
     switch (out) {
-        case Out::I32: return gemm_packed_dispatch<Out::I32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
-        case Out::F16: return gemm_packed_dispatch<Out::F16>(xq, x_scale, wp, w_scale, m, n, k, y, s);
-        case Out::BF16: return gemm_packed_dispatch<Out::BF16>(xq, x_scale, wp, w_scale, m, n, k, y, s);
-        case Out::F32: return gemm_packed_dispatch<Out::F32>(xq, x_scale, wp, w_scale, m, n, k, y, s);
+        case Out::I32: SQ_PK(Out::I32, false);
+        case Out::F16: if (ext) SQ_PK(Out::F16, true); SQ_PK(Out::F16, false);
+        case Out::BF16: if (ext) SQ_PK(Out::BF16, true); SQ_PK(Out::BF16, false);
+        case Out::F32: if (ext) SQ_PK(Out::F32, true); SQ_PK(Out::F32, false);
     }
+#undef SQ_PK
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
-                       hipStream_t s) {
+                       hipStream_t s, Epi epi) {
     const int m = (int)M, n = (int)N, k = (int)K;
+#define SQ_G(O, E) return gemm_out<O, E>(xq, x_scale, wq, w_scale, m, n, k, y, epi, s)
+    const bool ext = epi.on();
     switch (out) {
-        case Out::I32: return gemm_out<Out::I32>(xq, x_scale, wq, w_scale, m, n, k, y, s);
-        case Out::F16: return gemm_out<Out::F16>(xq, x_scale, wq, w_scale, m, n, k, y, s);
-        case Out::BF16: return gemm_out<Out::BF16>(xq, x_scale, wq, w_scale, m, n, k, y, s);
-        case Out::F32: return gemm_out<Out::F32>(xq, x_scale, wq, w_scale, m, n, k, y, s);
+        case Out::I32: SQ_G(Out::I32, false);
+        case Out::F16: if (ext) SQ_G(Out::F16, true); SQ_G(Out::F16, false);
+        case Out::BF16: if (ext) SQ_G(Out::BF16, true); SQ_G(Out::BF16, false);
+        case Out::F32: if (ext) SQ_G(Out::F32, true); SQ_G(Out::F32, false);
     }
+#undef SQ_G
     return hipErrorInvalidValue;
 }
 

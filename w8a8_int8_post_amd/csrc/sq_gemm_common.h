@@ -7,10 +7,16 @@
 
 namespace sq {
 
+// Keeps v's fp32 rounding: without it the compiler merges a multiply or an
+// FMA with a following fp16 conversion into one mixed-precision FMA that
+// rounds the exact value once to fp16 (a different result at fp16 ties).
+__device__ inline void pin_f32(float& v) { __asm__("" : "+v"(v)); }
+
 __device__ inline float dequant(int acc, float sxm, float swn) {
     float f = (float)acc;  // round to nearest even
     f = f * sxm;
     f = f * swn;
+    pin_f32(f);
     return f;
 }
 
@@ -24,6 +30,39 @@ __device__ inline void store_out(void* y, int64_t idx, int acc, float sxm, float
         static_cast<_Float16*>(y)[idx] = (_Float16)dequant(acc, sxm, swn);
     } else {
         static_cast<uint16_t*>(y)[idx] = BF16::from_f32(dequant(acc, sxm, swn));
+    }
+}
+
+// Scale back followed by the rest of the layer: RN(RN(acc * sx) * sw + bias)
+// (the channel scale and the bias in one fp32 FMA), then ReLU as v > 0 ? v : +0.
+__device__ inline float dequant_ext(int acc, float sxm, float swn, float bn, int relu) {
+    float f = (float)acc;
+    f = f * sxm;
+    f = __builtin_fmaf(f, swn, bn);
+    pin_f32(f);
+    return (relu && !(f > 0.0f)) ? 0.0f : f;
+}
+
+template <Out O>
+__device__ inline void store_val(void* y, int64_t idx, float v) {
+    if constexpr (O == Out::F32) {
+        static_cast<float*>(y)[idx] = v;
+    } else if constexpr (O == Out::F16) {
+        static_cast<_Float16*>(y)[idx] = (_Float16)v;
+    } else {
+        static_cast<uint16_t*>(y)[idx] = BF16::from_f32(v);
+    }
+}
+
+// store_out, or with EXT the scale back extended by e (output channel n).
+template <Out O, bool EXT>
+__device__ inline void store_out_ext(void* y, int64_t idx, int acc, float sxm, float swn,
+                                     const Epi& e, int n) {
+    if constexpr (EXT) {
+        static_assert(O != Out::I32, "no epilogue on raw accumulators");
+        store_val<O>(y, idx, dequant_ext(acc, sxm, swn, e.bias ? e.bias[n] : 0.0f, e.relu));
+    } else {
+        store_out<O>(y, idx, acc, sxm, swn);
     }
 }
 

@@ -11,6 +11,14 @@ namespace sq {
 enum class Dt : int { F32 = 0, F16 = 1, BF16 = 2 };
 enum class Out : int { I32 = 0, F16 = 1, BF16 = 2, F32 = 3 };
 
+// Optional rest of a linear layer after the scale back:
+// y = relu?(scaled + bias[n]).  Off (the plain scale back) by default.
+struct Epi {
+    const float* bias = nullptr;  // fp32 [N] or null
+    int relu = 0;
+    bool on() const { return bias != nullptr || relu != 0; }
+};
+
 hipError_t launch_colmax(const void* x, Dt dt, int64_t R, int64_t C, float* out, bool zero_first,
                          hipStream_t s);
 hipError_t launch_smooth_fold(const float* a, const void* w, Dt dt, int64_t K, int64_t N,
@@ -27,21 +35,24 @@ hipError_t launch_static_act_step(const float* a, const float* smooth, int64_t K
                                   hipStream_t s);
 hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
                                          float* w_scale, hipStream_t s);
+hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_t Kp, int64_t K,
+                                  float* w_out, float* bias, hipStream_t s);
 hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                              void* x_hat, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
-                       hipStream_t s);
+                       hipStream_t s, Epi epi = Epi());
 
 int64_t packed_weight_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp, hipStream_t s);
 hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8_t* wp,
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
-                              Out out, hipStream_t s);
+                              Out out, hipStream_t s, Epi epi = Epi());
 
 // Few-token GEMM (M <= 64): row-major or fragment-packed weights.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
-                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s);
+                         int M, int N, int K, void* y, Out out, bool packed, hipStream_t s,
+                         Epi epi = Epi());
 
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,

@@ -228,6 +228,62 @@ __global__ void absmax_to_step_kernel(float* p, int64_t n) {
     if (i < n) p[i] = quant_step(p[i]);
 }
 
+// Fold of the next layer's smoothing into a preceding linear layer [P1
+// 数学的に何をしているのか: the scales may be absorbed by the preceding linear
+// layer]: w_out[i, j] = fp32(w[i, j]) / s[j] over its output columns j, 16
+// bytes of w per thread step when K is a multiple of the vector width.
+template <class D, bool VECT>
+__global__ __launch_bounds__(256) void fold_prev_kernel(const typename D::T* __restrict__ w,
+                                                        const float* __restrict__ sm, int64_t Kp,
+                                                        int64_t K, float* __restrict__ out) {
+    constexpr int V = VECT ? D::VEC : 1;
+    const int64_t total = Kp * K / V;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t e0 = i * V;
+        const int64_t j = e0 % K;
+        if constexpr (VECT) {
+            float v[V];
+            load_vec<D>(w + e0, v);
+#pragma unroll
+            for (int e = 0; e < V; e += 4) {
+                const float4 s4 = *reinterpret_cast<const float4*>(sm + j + e);
+                float4 o;
+                o.x = v[e] / s4.x;
+                o.y = v[e + 1] / s4.y;
+                o.z = v[e + 2] / s4.z;
+                o.w = v[e + 3] / s4.w;
+                *reinterpret_cast<float4*>(out + e0 + e) = o;
+            }
+        } else {
+            out[e0] = D::to_f32(w[e0]) / sm[j];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void div_inplace_kernel(float* __restrict__ b,
+                                                          const float* __restrict__ sm, int64_t K) {
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < K; j += (int64_t)gridDim.x * 256)
+        b[j] = b[j] / sm[j];
+}
+
+template <class D>
+hipError_t fold_prev_typed(const void* wv, int64_t Kp, int64_t K, const float* sm, float* out,
+                           hipStream_t s) {
+    const typename D::T* w = static_cast<const typename D::T*>(wv);
+    const bool vect = K % D::VEC == 0;
+    const int64_t items = vect ? Kp * K / D::VEC : Kp * K;
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (vect)
+        hipLaunchKernelGGL((fold_prev_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, w,
+                           sm, Kp, K, out);
+    else
+        hipLaunchKernelGGL((fold_prev_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           w, sm, Kp, K, out);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_colmax(const void* x, Dt dt, int64_t R, int64_t C, float* out, bool zero_first,
@@ -304,6 +360,20 @@ hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_
     // 3) w_scale <- absmax / 127
     hipLaunchKernelGGL(absmax_to_step_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
                        w_scale, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_t Kp, int64_t K,
+                                  float* w_out, float* bias, hipStream_t s) {
+    hipError_t e = hipErrorInvalidValue;
+    switch (dt) {
+        case Dt::F32: e = fold_prev_typed<F32>(w, Kp, K, sm, w_out, s); break;
+        case Dt::F16: e = fold_prev_typed<F16>(w, Kp, K, sm, w_out, s); break;
+        case Dt::BF16: e = fold_prev_typed<BF16>(w, Kp, K, sm, w_out, s); break;
+    }
+    if (e != hipSuccess || !bias) return e;
+    hipLaunchKernelGGL(div_inplace_kernel, dim3((unsigned)((K + 255) / 256 < 1024 ? (K + 255) / 256 : 1024)),
+                       dim3(256), 0, s, bias, sm, K);
     return hipGetLastError();
 }
 
