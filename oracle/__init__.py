@@ -7,7 +7,8 @@ GPU library: the two share no code.
 
 The arithmetic lives in ``sqref.c`` (plain C, built with gcc
 ``-O2 -ffp-contract=off -fno-fast-math``); this module only marshals numpy
-arrays into it.  Every function takes and returns host numpy arrays.
+arrays into it.  The LayerNorm that carries the folded smoothing (fused with
+per-token quantisation) is in ``layernorm.py`` (numpy and ``math.fsum``).  Every function takes and returns host numpy arrays.
 Input tensors of 16-bit types are widened to float32 by numpy before the call
 (exact for fp16 and bf16).
 

@@ -500,3 +500,93 @@ def test_dequant_bias_act_f32_within_fp32_bound_of_exact(ref):
         p = np.abs(ref.dequant(acc, sx, sw))
         y32 = ref.dequant_bias_act_f32(acc, sx, sw, b, relu).astype(np.float64)
         assert (np.abs(y32 - y) <= 2.0 ** -24 * (p + np.abs(y)) * (1 + 1e-9)).all()
+
+
+# --------------------------------------------------------------------------
+# LayerNorm carrying the folded smoothing, fused with per-token quantisation
+
+def test_layernorm_hand_example():
+    from oracle import layernorm as ln
+    x = np.array([[1.0, 2.0, 3.0, 4.0]], np.float32)
+    y = ln.layernorm_f32(x, np.ones(4, np.float32), np.zeros(4, np.float32), 0.0)
+    # mean 2.5, variance 1.25: (x - 2.5) / sqrt(1.25) = -3/sqrt5, -1/sqrt5, 1/sqrt5, 3/sqrt5
+    r5 = 1.0 / np.sqrt(5.0)
+    np.testing.assert_allclose(y[0], [-3 * r5, -r5, r5, 3 * r5], rtol=2 ** -22, atol=0)
+    xq, sx, _ = ln.layernorm_quant_pertoken(x, np.ones(4, np.float32), np.zeros(4, np.float32),
+                                            0.0, "f32")
+    # step = max/127; 1/sqrt5 over step = 127/3 = 42.33 -> 42
+    assert xq.tolist() == [[-127, -42, 42, 127]]
+    assert sx[0] == np.float32(y[0, 3]) / np.float32(127.0)
+
+
+def test_layernorm_statistics_are_rounded_once_from_exact_values():
+    from decimal import Decimal, getcontext
+    from oracle import layernorm as ln
+    getcontext().prec = 60
+    x = np.array([[1.0, 2.0, 4.0, 8.0]], np.float32)
+    mu, rstd = ln.layernorm_stats(x, 0.0)
+    assert mu[0] == np.float32(3.75)  # exact mean
+    var = Decimal("7.1875")  # (2.75^2 + 1.75^2 + 0.25^2 + 4.25^2) / 4, exact
+    exact = 1 / var.sqrt()
+    # fp32 neighbours of the exact 1/sqrt(7.1875): the oracle returns the nearer
+    f = np.float32(float(exact))
+    cands = [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(1))]
+    best = min(cands, key=lambda c: abs(Decimal(float(c)) - exact))
+    assert rstd[0] == best
+
+
+def test_layernorm_matches_double_layer_norm():
+    # a library routine in double: pins the formula (biased variance, eps
+    # inside the root, gamma scaling and beta shift); K = 8 makes a (K - 1)
+    # variance or eps outside the root visible
+    import torch
+    from oracle import layernorm as ln
+    r = np.random.default_rng(31)
+    for K, eps in ((8, 1e-5), (300, 1e-5), (4096, 1e-6)):
+        x = (r.standard_normal((7, K)) * 3 + 1).astype(np.float32)
+        g = (1 + 0.1 * r.standard_normal(K)).astype(np.float32)
+        b = (0.1 * r.standard_normal(K)).astype(np.float32)
+        y = ln.layernorm_f32(x, g, b, eps).astype(np.float64)
+        t = torch.nn.functional.layer_norm(torch.from_numpy(x).double(), (K,),
+                                           torch.from_numpy(g).double(),
+                                           torch.from_numpy(b).double(), eps).numpy()
+        np.testing.assert_allclose(y, t, rtol=3e-6, atol=3e-6)
+
+
+def test_layernorm_with_folded_factors_emits_smoothed_activation():
+    # LN with (gamma / s, beta / s) equals LN with (gamma, beta) divided by s
+    from oracle import layernorm as ln
+    import oracle as ref
+    r = np.random.default_rng(32)
+    K = 512
+    x = r.standard_normal((5, K)).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(K)).astype(np.float32)
+    b = (0.1 * r.standard_normal(K)).astype(np.float32)
+    s = np.exp(r.standard_normal(K)).astype(np.float32)
+    gf, bf = ref.fold_norm(s, g, b)
+    y_fold = ln.layernorm_f32(x, gf, bf, 1e-5).astype(np.float64)
+    y = ln.layernorm_f32(x, g, b, 1e-5).astype(np.float64) / s.astype(np.float64)
+    np.testing.assert_allclose(y_fold, y, rtol=2e-6, atol=1e-6)
+
+
+def test_layernorm_ambiguity_flag():
+    from oracle import layernorm as ln
+    one = np.float32(1.0)
+    x = np.array([[one, np.nextafter(one, np.float32(2))],      # mean on an fp32 midpoint
+                  [np.float32(1.0), np.float32(2.0)]], np.float32)  # mean 1.5, far from one
+    assert ln.ambiguous_rows(x, 1e-5) == [0]
+
+
+def test_layernorm_store_and_quantise_in_the_activation_dtype():
+    import torch
+    from oracle import layernorm as ln
+    import oracle as ref
+    r = np.random.default_rng(33)
+    x = torch.from_numpy(r.standard_normal((6, 256)).astype(np.float32)).half()
+    g = np.ones(256, np.float32)
+    b = np.zeros(256, np.float32)
+    xq, sx, y = ln.layernorm_quant_pertoken(x.float().numpy(), g, b, 1e-5, "f16")
+    y32 = ln.layernorm_f32(x.float().numpy(), g, b, 1e-5)
+    assert np.array_equal(y, torch.from_numpy(y32).half().float().numpy())
+    xq2, sx2 = ref.quant_act_pertoken(y)
+    assert np.array_equal(xq, xq2) and np.array_equal(sx, sx2)
