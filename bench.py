@@ -60,7 +60,11 @@ class Layer:
         xc = synth.activations(CFG, name, CFG.T, calibration=True).to(dev)
         self.x_eval_host = synth.activations(CFG, name, PREFILL_M)
         a = sq.calibrate_absmax(xc)
-        self.s, w_hat = sq.smooth_fold(a, w, ALPHA)
+        # the LayerNorm in front of the layer takes the smoothing (gamma / s, beta / s)
+        g, b = synth.layernorm_params(CFG, name)
+        self.ln_g = torch.as_tensor(g, dtype=torch.float32).contiguous().to(dev)
+        self.ln_b = torch.as_tensor(b, dtype=torch.float32).contiguous().to(dev)
+        self.s, w_hat = sq.smooth_fold(a, w, ALPHA, self.ln_g, self.ln_b)
         self.wq, self.sw = sq.quant_weight_perchannel(w_hat)
         self.wp = sq.pack_weight(self.wq)  # fragment-packed copy (offline re-layout)
         # O2/O3: per-tensor weights; O3's static activation step from calibration
@@ -70,6 +74,7 @@ class Layer:
         del wq_t
         x = self.x_eval_host.to(dev)
         self.x_hat = sq.smooth_activation(x, self.s)   # what a folded LayerNorm emits
+        self.x_res = x.clone()  # stand-in for the residual stream the LayerNorm reads
         torch.cuda.synchronize()
         self.w_host = None
         del w, xc, w_hat, x
@@ -354,6 +359,40 @@ def main():
                       "gbs": round(quant_bytes / quant_ms / 1e6, 1),
                       "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
     }
+    # ---- the LayerNorm in front of QKV and FC1 (it carries the folded
+    # smoothing) fused with the per-token quantisation: reads the residual
+    # stream once and writes only codes and steps
+    ln_layers = [ly for ly in layers if ly.name in ("qkv", "fc1")]
+    ln_bytes = sum(M * ly.K * 2 + M * ly.K + 4 * M + 8 * ly.K for ly in ln_layers) / len(ln_layers)
+    ln_ms = {}
+    for hat in (False, True):
+        bufs = []
+        for _ in range(2):
+            bufs.append([(ly.x_res.clone(), ly.ln_g, ly.ln_b,
+                          torch.empty(M, ly.K, dtype=torch.int8, device=dev),
+                          torch.empty(M, dtype=torch.float32, device=dev),
+                          torch.empty(M, ly.K, dtype=torch.float16, device=dev) if hat else None)
+                         for ly in ln_layers])
+
+        def ln_fn(bset):
+            for (x, g, b, xq, sx, xh) in bset:
+                sq.sq_layernorm_quant_pertoken(x, g, b, 1e-5, xq, sx, xh)
+        gr = [capture(lambda bs=bs: ln_fn(bs)) for bs in bufs]
+        ln_ms[hat] = time_graphs(gr, args.steps, args.warmup) / len(ln_layers)
+        del bufs, gr
+        torch.cuda.synchronize()
+    out["layernorm_quant"] = {
+        "avg_launch_us": round(ln_ms[False] * 1e3, 2),
+        "gbs": round(ln_bytes / ln_ms[False] / 1e6, 1),
+        "hbm_frac": round(ln_bytes / ln_ms[False] / 1e6 / PEAK_HBM_GBS, 3),
+        "with_x_hat_avg_launch_us": round(ln_ms[True] * 1e3, 2),
+        "layers": [ly.name for ly in ln_layers], "tokens": M,
+        "step": "sq_layernorm_quant_pertoken (LayerNorm with gamma/s, beta/s + per-token "
+                "quantisation, one kernel); bytes: fp16 x read + int8 codes + steps + gamma/beta",
+    }
+    log("layernorm+quant (fused): %.2f us per launch (%.0f GB/s); with X_hat also written %.2f us"
+        % (ln_ms[False] * 1e3, ln_bytes / ln_ms[False] / 1e6, ln_ms[True] * 1e3))
+
     # ---- decode shapes
     if not args.no_decode:
         dec = {}

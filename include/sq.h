@@ -57,7 +57,8 @@ typedef enum {
     SQ_ERR_ALPHA = 6,       /* alpha outside [0, 1] or not finite */
     SQ_ERR_HIP = 7,         /* the HIP runtime reported a launch error */
     SQ_ERR_ALIAS = 8,       /* two buffers overlap where the entry point forbids it */
-    SQ_ERR_ACT = 9          /* activation code not one of sq_act */
+    SQ_ERR_ACT = 9,         /* activation code not one of sq_act */
+    SQ_ERR_EPS = 10         /* LayerNorm epsilon negative or not finite */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
@@ -143,6 +144,32 @@ sq_status sq_quant_weight_pertensor(const void* w, sq_dtype wdt, int64_t K, int6
  * smoothed).  xq: int8 [M x K].  x_scale: fp32 [M]. */
 sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
                                 const float* smooth, int8_t* xq, float* x_scale, void* stream);
+
+/* LayerNorm carrying the folded smoothing factors, fused with per-token
+ * quantisation [P1 数学的に何をしているのか: diag(s)^-1 is absorbed by the
+ * LayerNorm in front of the layer, which then emits X_hat; P1 推論方法, O1:
+ * X_hat quantised per token].  The LayerNorm is the standard one of each row
+ * (Ba, Kiros and Hinton, "Layer Normalization", 2016):
+ *   mu   = fp32(S / K),  S = sum_k x[m, k]                   (double sums)
+ *   var  = sum_k (x[m, k] - S / K)^2 / K                     (double)
+ *   rstd = fp32(1 / sqrt(var + eps))                         (double)
+ *   h[k] = dt( (((x[m, k] - mu) * rstd) * gamma[k]) + beta[k] )
+ *          (fp32, one rounding per operation, no fused multiply-add, then
+ *          round to nearest even to the activation dtype xdt)
+ *   then xq[m, :], x_scale[m] exactly as sq_quant_act_pertoken of h.
+ * gamma, beta: fp32 [K], the LayerNorm's scale and shift already divided by
+ * the smoothing factors (sq_smooth_fold's in-place update).  eps >= 0.
+ * x_hat: [M x K] of dtype xdt receiving h, or NULL (not written).  The double
+ * sums are taken in the kernel's own order; a result can differ from a
+ * correctly rounded sum only where the exact statistic lies within that
+ * order's error bound (K * 2^-53 relative) of an fp32 rounding boundary.
+ * One workgroup per row, the row held in registers: K up to 65536 (fp16,
+ * bf16) or 32768 (fp32) when K is a multiple of 8 (4 for fp32), else up to
+ * 16384; larger K: SQ_ERR_SHAPE.  Outputs must not overlap the inputs or one
+ * another: SQ_ERR_ALIAS. */
+sq_status sq_layernorm_quant_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                      const float* gamma, const float* beta, double eps,
+                                      int8_t* xq, float* x_scale, void* x_hat, void* stream);
 
 /* Per-tensor activation quantisation [P1 推論方法, O2: activations per
  * tensor, dynamic; O3: per tensor, static, the step fixed offline from

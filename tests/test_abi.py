@@ -123,3 +123,23 @@ def test_epilogue_entry_points_validate(lib):
     assert lib.sq_fold_prev_linear(A, A, 0, 0, 4, A, None, None) == 2
     assert lib.sq_fold_prev_linear(A, A, 4, 4, 4, A, None, None) == 3
     assert lib.sq_fold_prev_linear(A, A, 0, 4, 4, A, A + 8, None) == 5
+
+
+def test_layernorm_quant_entry_point_validates(lib):
+    import ctypes
+    f = lib.sq_layernorm_quant_pertoken
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    B = 1 << 30  # fake, far-apart, aligned addresses: validation never dereferences
+    ok = (B, 1, 4, 16, 2 * B, 3 * B, 1e-5, 4 * B, 5 * B, None, None)
+    assert f(*ok[:4], None, *ok[5:]) == 1                       # null gamma
+    assert f(ok[0], 1, 4, 70000, *ok[4:]) == 2                   # K beyond the register budget
+    assert f(ok[0], 0, 4, 16385, *ok[4:]) == 2                   # fp32, K not a multiple of 4
+    assert f(ok[0], 7, *ok[2:]) == 3
+    assert f(*ok[:6], -1.0, *ok[7:]) == 10
+    assert f(*ok[:6], float("nan"), *ok[7:]) == 10
+    assert f(*ok[:6], float("inf"), *ok[7:]) == 10
+    assert f(ok[0] + 2, *ok[1:]) == 5
+    assert f(*ok[:7], ok[0], *ok[8:]) == 8                      # xq on top of x
+    assert f(*ok[:9], 4 * B + 32, None) == 8                    # x_hat inside xq

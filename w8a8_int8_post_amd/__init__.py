@@ -31,6 +31,7 @@ __all__ = [
     "quant_weight_pertensor", "linear_w8a8_packed_static", "sq_w8a8_gemm_dequant_ex",
     "sq_w8a8_gemm_dequant_packed_ex", "sq_fold_prev_linear", "w8a8_gemm_dequant_ex",
     "w8a8_gemm_dequant_packed_ex", "fold_prev_linear", "SQ_ACT_NONE", "SQ_ACT_RELU",
+    "sq_layernorm_quant_pertoken", "layernorm_quant_pertoken",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -39,7 +40,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE",
           4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP",
-          8: "SQ_ERR_ALIAS", 9: "SQ_ERR_ACT"}
+          8: "SQ_ERR_ALIAS", 9: "SQ_ERR_ACT", 10: "SQ_ERR_EPS"}
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_ACT_NONE, SQ_ACT_RELU = 0, 1
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}
@@ -80,6 +81,7 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_gemm_dequant_ex": [P, P, P, P, P, E, I64, I64, I64, P, E, P],
             "sq_w8a8_gemm_dequant_packed_ex": [P, P, P, P, P, E, I64, I64, I64, P, E, P],
             "sq_fold_prev_linear": [P, P, E, I64, I64, P, P, P],
+            "sq_layernorm_quant_pertoken": [P, E, I64, I64, P, P, ctypes.c_double, P, P, P, P],
             "sq_static_act_step": [P, P, I64, P, P],
             "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
         }
@@ -277,6 +279,19 @@ def sq_fold_prev_linear(s, w_prev, w_out, bias=None, stream=None):
           _opt(bias, "bias", torch.float32), _stream(w_prev, stream))
 
 
+def sq_layernorm_quant_pertoken(x, gamma, beta, eps, xq, x_scale, x_hat=None, stream=None):
+    M, K = x.shape
+    if gamma.shape[0] != K or beta.shape[0] != K or tuple(xq.shape) != (M, K) \
+            or x_scale.shape[0] != M or (x_hat is not None and tuple(x_hat.shape) != (M, K)):
+        raise ValueError("shape mismatch")
+    if x_hat is not None and x_hat.dtype != x.dtype:
+        raise TypeError("x_hat must have x's dtype")
+    _call("sq_layernorm_quant_pertoken", _dev(x, "x"), _DT[x.dtype], M, K,
+          _dev(gamma, "gamma", torch.float32), _dev(beta, "beta", torch.float32), float(eps),
+          _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32),
+          _opt(x_hat, "x_hat"), _stream(x, stream))
+
+
 def sq_w8a8_gemm_i32_packed(xq, wq_packed, N, acc, stream=None):
     M, K = xq.shape
     if tuple(acc.shape) != (M, N):
@@ -384,6 +399,17 @@ def fold_prev_linear(s, w_prev, bias=None, stream=None):
     out = torch.empty(w_prev.shape, dtype=torch.float32, device=w_prev.device)
     sq_fold_prev_linear(s, w_prev, out, bias, stream)
     return out
+
+
+def layernorm_quant_pertoken(x, gamma, beta, eps=1e-5, want_x_hat=False, stream=None):
+    """(xq, x_scale[, x_hat]): LayerNorm with the folded (gamma, beta), then
+    per-token quantisation, in one kernel."""
+    M, K = x.shape
+    xq = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    xh = torch.empty_like(x) if want_x_hat else None
+    sq_layernorm_quant_pertoken(x, gamma, beta, eps, xq, sx, xh, stream)
+    return (xq, sx, xh) if want_x_hat else (xq, sx)
 
 
 def w8a8_gemm_i32(xq, wq, stream=None):

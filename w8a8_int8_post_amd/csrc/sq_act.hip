@@ -405,6 +405,224 @@ __global__ __launch_bounds__(1024) void static_step_kernel(const float* __restri
     if (threadIdx.x == 0) out[0] = quant_step(m);
 }
 
+
+// ---------------------------------------------------------------------------
+// LayerNorm carrying the folded smoothing factors, fused with per-token
+// quantisation [P1 数学的に何をしているのか: diag(s)^-1 is folded into the
+// LayerNorm's scale and shift, so the LayerNorm emits X_hat; P1 推論方法: O1
+// quantises X_hat per token].  The LayerNorm is the standard one (Ba, Kiros
+// and Hinton 2016): (x - mean) / sqrt(var + eps) * gamma + beta, biased
+// variance.  One workgroup per row; the row stays in registers from the load
+// to the code store, so x is read once and X_hat never goes to memory unless
+// asked for.  Statistics: double sums (each lane over its pieces, then across
+// the workgroup), mean = S / K, var = sum((x - mean)^2) / K, rstd =
+// 1 / sqrt(var + eps), all in double, each rounded once to fp32.  Element-wise:
+// ((x - mean) * rstd) * gamma + beta in fp32, one rounding per operation,
+// then the store in the activation dtype; the stored values are quantised
+// like sq_quant_act_pertoken's.
+// Sum over the WPR waves of each row (WPR > 1: through LDS; every wave of the
+// workgroup takes part, so the barrier is reached by all).
+template <int NT, int WPR, class T>
+__device__ inline T row_sum(T v, T* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if constexpr (WPR > 1) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        const int w0 = wave - wave % WPR;
+        v = red[w0];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) v += red[w0 + w];
+        __syncthreads();
+    }
+    return v;
+}
+
+template <int NT, int WPR>
+__device__ inline float row_max(float v, float* red) {
+    v = wave_max(v);
+    if constexpr (WPR > 1) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        const int w0 = wave - wave % WPR;
+        v = red[w0];
+#pragma unroll
+        for (int w = 1; w < WPR; ++w) v = __builtin_fmaxf(v, red[w0 + w]);
+    }
+    return v;
+}
+
+// WPR waves per row, NT / (64 * WPR) rows per workgroup; each lane holds NCH
+// pieces of its row (piece (c * WPR + part) * 64 + lane: consecutive lanes,
+// consecutive pieces).  VECT: pieces of 16 bytes (K % VEC == 0), else single
+// elements.  With WPR == 1 the reductions are wavefront shuffles only.
+template <class D, int NT, int WPR, int NCH, bool VECT, bool HAT>
+__global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __restrict__ x,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta, double eps,
+                                                      int64_t M, int64_t K,
+                                                      int8_t* __restrict__ xq,
+                                                      float* __restrict__ sx,
+                                                      typename D::T* __restrict__ xhat) {
+    typedef typename D::T T;
+    constexpr int W = VECT ? D::VEC : 1;  // elements per piece
+    constexpr int RPW = NT / (64 * WPR);  // rows per workgroup
+    __shared__ double dred[NT / 64];
+    __shared__ float fred[NT / 64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const int part = wave % WPR;
+    const bool live = m < M;
+    const T* row = x + (live ? m : 0) * K;
+    const int64_t npc = K / W;  // pieces in the row
+    float v[NCH][W];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t pc = ((int64_t)c * WPR + part) * 64 + lane;
+        const int64_t pcl = pc < npc ? pc : npc - 1;  // clamped: loads stay straight-line
+        if constexpr (VECT)
+            load_vec<D>(row + pcl * W, v[c]);
+        else
+            v[c][0] = D::to_f32(row[pcl]);
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (((int64_t)c * WPR + part) * 64 + lane < npc)
+#pragma unroll
+            for (int e = 0; e < W; ++e) s += (double)v[c][e];
+    const double mu_d = row_sum<NT, WPR>(s, dred) / (double)K;
+    double q = 0.0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+        if (((int64_t)c * WPR + part) * 64 + lane < npc)
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                const double d = (double)v[c][e] - mu_d;
+                q += d * d;
+            }
+    const double var_d = row_sum<NT, WPR>(q, dred) / (double)K;
+    const float mu = (float)mu_d;
+    const float rstd = (float)(1.0 / __builtin_sqrt(var_d + eps));
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t pc = ((int64_t)c * WPR + part) * 64 + lane;
+        const int64_t k0 = (pc < npc ? pc : npc - 1) * W;
+        float g[W], b[W];
+        if constexpr (W % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < W; e += 4) {
+                const float4 g4 = *reinterpret_cast<const float4*>(gamma + k0 + e);
+                const float4 b4 = *reinterpret_cast<const float4*>(beta + k0 + e);
+                g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
+                b[e] = b4.x; b[e + 1] = b4.y; b[e + 2] = b4.z; b[e + 3] = b4.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+                g[e] = gamma[k0 + e];
+                b[e] = beta[k0 + e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+            float t = v[c][e] - mu;
+            t = t * rstd;
+            t = t * g[e];
+            t = t + b[e];
+            pin_f32(t);
+            v[c][e] = D::to_f32(D::from_f32(t));  // the value as stored in the activation dtype
+        }
+        if (pc < npc)
+#pragma unroll
+            for (int e = 0; e < W; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][e]));
+    }
+    amax = row_max<NT, WPR>(amax, fred);
+    if (!live) return;
+    const RowStep step = row_step(amax);
+    if (part == 0 && lane == 0) sx[m] = step.step;
+    int8_t* qrow = xq + m * K;
+    T* hrow = HAT ? xhat + m * K : nullptr;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t pc = ((int64_t)c * WPR + part) * 64 + lane;
+        if (pc >= npc) continue;
+        if constexpr (HAT) {
+            T h[W];
+#pragma unroll
+            for (int e = 0; e < W; ++e) h[e] = D::from_f32(v[c][e]);  // exact: already in T
+            if constexpr (VECT)
+                *reinterpret_cast<uint4*>(hrow + pc * W) = *reinterpret_cast<const uint4*>(h);
+            else
+                hrow[pc] = h[0];
+        }
+        if constexpr (VECT) {
+            if (step.fast)
+                store_codes<true, W>(qrow + pc * W, v[c], step);
+            else
+                store_codes<false, W>(qrow + pc * W, v[c], step);
+        } else {
+            qrow[pc] = (int8_t)(step.fast ? quant_code<true>(v[c][0], step)
+                                          : quant_code<false>(v[c][0], step));
+        }
+    }
+}
+
+template <class D, int NT, int WPR, int NCH, bool VECT>
+void ln_launch(const void* x, int64_t M, int64_t K, const float* g, const float* b, double eps,
+               int8_t* xq, float* sx, void* xhat, hipStream_t s) {
+    typedef typename D::T T;
+    constexpr int RPW = NT / (64 * WPR);
+    const dim3 grid((unsigned)((M + RPW - 1) / RPW));
+    if (xhat)
+        hipLaunchKernelGGL((ln_quant_kernel<D, NT, WPR, NCH, VECT, true>), grid, dim3(NT), 0, s,
+                           static_cast<const T*>(x), g, b, eps, M, K, xq, sx, static_cast<T*>(xhat));
+    else
+        hipLaunchKernelGGL((ln_quant_kernel<D, NT, WPR, NCH, VECT, false>), grid, dim3(NT), 0, s,
+                           static_cast<const T*>(x), g, b, eps, M, K, xq, sx, nullptr);
+}
+
+// Pieces per row npc: one wave per row while it holds the row in 8 pieces per
+// lane (many rows: no barrier at all); longer rows, or few rows (decode, where
+// one wave per row would leave most of the GPU idle), spread over 4 or 16 waves.
+template <class D>
+hipError_t ln_typed(const void* x, int64_t M, int64_t K, const float* g, const float* b,
+                    double eps, int8_t* xq, float* sx, void* xhat, hipStream_t s) {
+    const bool few = M < 1024;
+    if (K % D::VEC == 0) {
+        const int64_t npc = K / D::VEC;
+        if (npc <= 64 * 2 && !few)
+            ln_launch<D, 256, 1, 2, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 64 * 4 && !few)
+            ln_launch<D, 256, 1, 4, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 64 * 8 && !few)
+            ln_launch<D, 256, 1, 8, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 256 * 2)
+            ln_launch<D, 256, 4, 2, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 256 * 8)
+            ln_launch<D, 256, 4, 8, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 1024 * 4)
+            ln_launch<D, 1024, 16, 4, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (npc <= 1024 * 8)
+            ln_launch<D, 1024, 16, 8, true>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        if (K <= 256 * 4)
+            ln_launch<D, 256, 4, 4, false>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (K <= 1024 * 8)
+            ln_launch<D, 1024, 16, 8, false>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else if (K <= 1024 * 16)
+            ln_launch<D, 1024, 16, 16, false>(x, M, K, g, b, eps, xq, sx, xhat, s);
+        else
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_act_quant_pertensor(const void* x, Dt dt, int64_t M, int64_t K,
@@ -449,6 +667,22 @@ hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const f
         case Dt::BF16: return smooth_act_typed<BF16>(x, M, K, smooth, x_hat, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_ln_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* gamma,
+                           const float* beta, double eps, int8_t* xq, float* x_scale, void* x_hat,
+                           hipStream_t s) {
+    switch (dt) {
+        case Dt::F32: return ln_typed<F32>(x, M, K, gamma, beta, eps, xq, x_scale, x_hat, s);
+        case Dt::F16: return ln_typed<F16>(x, M, K, gamma, beta, eps, xq, x_scale, x_hat, s);
+        case Dt::BF16: return ln_typed<BF16>(x, M, K, gamma, beta, eps, xq, x_scale, x_hat, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+int64_t ln_max_k(Dt dt, int64_t K) {
+    const int64_t vec = dt == Dt::F32 ? 4 : 8;
+    return K % vec == 0 ? 1024 * 8 * vec : 1024 * 16;
 }
 
 }  // namespace sq

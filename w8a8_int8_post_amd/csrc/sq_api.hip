@@ -22,6 +22,15 @@ sq_status hip_status(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_ERR_HIP
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// [a, a + na) and [b, b + nb) share a byte (either may be null: no overlap).
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+    if (!a || !b) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int64_t dt_bytes(sq_dtype d) { return d == SQ_F32 ? 4 : 2; }
+
 }  // namespace
 
 extern "C" {
@@ -69,6 +78,32 @@ sq_status sq_quant_act_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t 
         return SQ_ERR_ALIGN;
     return hip_status(
         sq::launch_act_quant(x, to_dt(xdt), M, K, smooth, xq, x_scale, as_stream(stream)));
+}
+
+sq_status sq_layernorm_quant_pertoken(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                      const float* gamma, const float* beta, double eps,
+                                      int8_t* xq, float* x_scale, void* x_hat, void* stream) {
+    if (!x || !gamma || !beta || !xq || !x_scale) return SQ_ERR_NULL;
+    if (!dims_ok(M, K)) return SQ_ERR_SHAPE;
+    if (!dt_ok(xdt)) return SQ_ERR_DTYPE;
+    if (K > sq::ln_max_k(to_dt(xdt), K)) return SQ_ERR_SHAPE;
+    if (!(eps >= 0.0 && eps <= 1e300)) return SQ_ERR_EPS;  // also rejects NaN and inf
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(xq) ||
+        !aligned16(x_scale) || (x_hat && !aligned16(x_hat)))
+        return SQ_ERR_ALIGN;
+    const int64_t xb = M * K * dt_bytes(xdt);
+    const void* outs[3] = {xq, x_scale, x_hat};
+    const int64_t outn[3] = {M * K, M * 4, x_hat ? xb : 0};
+    const void* ins[3] = {x, gamma, beta};
+    const int64_t inn[3] = {xb, K * 4, K * 4};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(outs[o], outn[o], ins[i], inn[i])) return SQ_ERR_ALIAS;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlaps(outs[o], outn[o], outs[p], outn[p])) return SQ_ERR_ALIAS;
+    }
+    return hip_status(sq::launch_ln_quant(x, to_dt(xdt), M, K, gamma, beta, eps, xq, x_scale,
+                                          x_hat, as_stream(stream)));
 }
 
 sq_status sq_fold_prev_linear(const float* s, const void* w_prev, sq_dtype wdt, int64_t Kp,

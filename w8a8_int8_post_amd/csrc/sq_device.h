@@ -49,6 +49,11 @@ __device__ inline void load_vec(const typename D::T* p, float (&out)[D::VEC]) {
     for (int i = 0; i < D::VEC; ++i) out[i] = D::to_f32(e[i]);
 }
 
+// Keeps v's fp32 rounding: without it the compiler merges a multiply, add or
+// FMA with a following fp16 conversion into one mixed-precision FMA that
+// rounds the exact value once to fp16 (a different result at fp16 ties).
+__device__ inline void pin_f32(float& v) { __asm__("" : "+v"(v)); }
+
 // ------------------------------------------------------------- quantiser
 // step = absmax / 127 (fp32 IEEE division); code = clamp(round half away
 // from zero (v / step), -127, 127); a zero step gives code 0.

@@ -7,11 +7,6 @@
 
 namespace sq {
 
-// Keeps v's fp32 rounding: without it the compiler merges a multiply or an
-// FMA with a following fp16 conversion into one mixed-precision FMA that
-// rounds the exact value once to fp16 (a different result at fp16 ties).
-__device__ inline void pin_f32(float& v) { __asm__("" : "+v"(v)); }
-
 __device__ inline float dequant(int acc, float sxm, float swn) {
     float f = (float)acc;  // round to nearest even
     f = f * sxm;

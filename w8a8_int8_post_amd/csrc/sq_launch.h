@@ -37,6 +37,11 @@ hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_
                                          float* w_scale, hipStream_t s);
 hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_t Kp, int64_t K,
                                   float* w_out, float* bias, hipStream_t s);
+hipError_t launch_ln_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* gamma,
+                           const float* beta, double eps, int8_t* xq, float* x_scale, void* x_hat,
+                           hipStream_t s);
+// Largest K the fused LayerNorm kernels hold in registers for this dtype and K.
+int64_t ln_max_k(Dt dt, int64_t K);
 hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                              void* x_hat, hipStream_t s);
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
