@@ -222,6 +222,59 @@ def profiled_traffic():
         return None
 
 
+def attention_time(dev, args, H=32, S=2048, D=128):
+    """Time the two INT8 attention products and their quantisers."""
+    r = np.random.default_rng([7, H, S, D])
+    q = torch.from_numpy(r.standard_normal((H * S, D), dtype=np.float32)).half().to(dev)
+    k = torch.from_numpy(r.standard_normal((H * S, D), dtype=np.float32)).half().to(dev)
+    v = torch.from_numpy(r.standard_normal((H, S, D), dtype=np.float32)).half().to(dev)
+    z = torch.softmax(torch.from_numpy(r.standard_normal((H * S, S), dtype=np.float32)), -1)
+    p = z.half().to(dev)
+    del z
+    qq, sq_ = sq.quant_act_pertoken(q)
+    kq, sk = sq.quant_act_pertoken(k)
+    pq, sp = sq.quant_act_pertoken(p)
+    vq, sv = sq.quant_weight_perchannel_batched(v)
+    scores = torch.empty(H, S, S, dtype=torch.float16, device=dev)
+    o = torch.empty(H, S, D, dtype=torch.float16, device=dev)
+
+    def qk():
+        sq.sq_w8a8_bmm_dequant(qq.view(H, S, D), sq_.view(H, S), kq.view(H, S, D), sk.view(H, S),
+                               scores)
+
+    def pv():
+        sq.sq_w8a8_bmm_dequant(pq.view(H, S, S), sp.view(H, S), vq, sv, o)
+
+    def quants():
+        sq.sq_quant_act_pertoken(q, qq, sq_)
+        sq.sq_quant_act_pertoken(k, kq, sk)
+        sq.sq_quant_act_pertoken(p, pq, sp)
+        sq.sq_quant_weight_perchannel_batched(v, vq, sv)
+
+    ops = 2.0 * H * S * S * D
+    res = {"heads": H, "tokens": S, "head_dim": D, "dtype_out": "fp16"}
+    for name, fn, nbytes in (
+            ("qk", qk, 2 * H * S * D + 2 * H * S * S + 8 * H * S),
+            ("pv", pv, H * S * S + H * S * D + 2 * H * S * D + 4 * H * S + 4 * H * D)):
+        ms = time_graphs([capture(fn)], args.steps, args.warmup)
+        res[name] = {"us": round(ms * 1e3, 2), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+                     "bytes": nbytes}
+        log("attention %s: %.1f us, %.1f TOPS, %.0f GB/s" % (name, ms * 1e3, res[name]["tops"],
+                                                             res[name]["gbs"]))
+    ms = time_graphs([capture(quants)], args.steps, args.warmup)
+    qbytes = 3 * H * S * D * 2 + H * S * S * 3 + H * S * D * 2 + 12 * H * S
+    res["quant_all_us"] = round(ms * 1e3, 2)
+    res["quant_gbs"] = round(qbytes / (ms * 1e-3) / 1e9, 1)
+    res["step"] = ("sq_w8a8_bmm_dequant for Q K^T (scores fp16) and for P V; quantisers: "
+                   "sq_quant_act_pertoken for Q, K, P and sq_quant_weight_perchannel_batched for V")
+    log("attention quantisers: %.1f us" % (ms * 1e3))
+    del q, k, v, p, qq, kq, pq, vq, scores, o
+    torch.cuda.synchronize()
+    return res
+
+
 def n_sets(footprint_bytes):
     return max(2, math.ceil((1 << 30) / footprint_bytes))
 
@@ -266,6 +319,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offline", action="store_true")
     ap.add_argument("--no-levels", action="store_true", help="skip the O2/O3 measurements")
+    ap.add_argument("--no-attention", action="store_true", help="skip the INT8 attention products")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -392,6 +446,12 @@ def main():
     }
     log("layernorm+quant (fused): %.2f us per launch (%.0f GB/s); with X_hat also written %.2f us"
         % (ln_ms[False] * 1e3, ln_bytes / ln_ms[False] / 1e6, ln_ms[True] * 1e3))
+
+    # ---- INT8 attention products at the OPT-6.7B-like block's attention
+    # shape (32 heads x head_dim 128, 2048 tokens): Q K^T with Q and K per
+    # token, P V with P per row and V per head-dim channel; codes resident
+    if not args.no_attention:
+        out["attention"] = attention_time(dev, args)
 
     # ---- decode shapes
     if not args.no_decode:

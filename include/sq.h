@@ -224,6 +224,35 @@ sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const 
                                   const float* w_scale, const float* bias, int act, int64_t M,
                                   int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream);
 
+/* Batched INT8 products for attention [P1 推論方法: besides the linear layers,
+ * the attention BMMs run in INT8 (Q K^T and P V)].  `batch` independent
+ * products (batch x heads) lying back to back, each exactly as
+ * sq_w8a8_gemm_dequant:
+ *   acc[b, m, n] = sum_k xq[b, m, k] * wq[b, n, k]
+ *   y[b, m, n]   = ydt( (fp32(acc) * x_scale[b, m]) * w_scale[b, n] )
+ * xq: int8 [batch x M x K]; x_scale: fp32 [batch x M]; wq: int8
+ * [batch x N x K]; w_scale: fp32 [batch x N]; y: [batch x M x N].  For
+ * Q K^T: xq = per-token codes of Q (sq_quant_act_pertoken over batch*M rows),
+ * wq = per-row codes of K (the same call over its batch*N rows: each key is
+ * an output channel of the product).  For P V: xq = per-row codes of P, wq =
+ * V's codes per head-dim channel, transposed (sq_quant_weight_perchannel_batched).
+ * 1 <= batch <= 65535; other limits and errors as sq_w8a8_gemm_dequant.  One
+ * launch (the batch entry is the grid's second dimension). */
+sq_status sq_w8a8_bmm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                              const float* w_scale, int64_t batch, int64_t M, int64_t N,
+                              int64_t K, void* y, sq_dtype ydt, void* stream);
+
+/* Per-output-channel quantisation of `batch` matrices w [batch x K x N]
+ * lying back to back: for each entry b and column n,
+ *   w_scale[b, n] = max_k |w[b, k, n]| / 127,  wq[b, n, k] = code(w[b, k, n])
+ * exactly as sq_quant_weight_perchannel per entry (wq: int8 [batch x N x K],
+ * w_scale: fp32 [batch x N]).  For attention: V [keys x head_dim] per head
+ * becomes the weight operand of P V.  Four launches in all (zero, column
+ * maxima, codes, steps).  1 <= batch <= 65535. */
+sq_status sq_quant_weight_perchannel_batched(const void* w, sq_dtype wdt, int64_t batch,
+                                             int64_t K, int64_t N, int8_t* wq, float* w_scale,
+                                             void* stream);
+
 /* ------------------------------------------------------------- auxiliary */
 
 /* The INT8 GEMM's raw accumulators, for exact checking of the GEMM kernels:
@@ -232,6 +261,12 @@ sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const 
  * (M, N, K). */
 sq_status sq_w8a8_gemm_i32(const int8_t* xq, const int8_t* wq, int64_t M, int64_t N, int64_t K,
                            int32_t* acc, void* stream);
+
+/* sq_w8a8_bmm_dequant's raw accumulators (int32 [batch x M x N]), same
+ * kernels, for exact checking. */
+sq_status sq_w8a8_bmm_i32(const int8_t* xq, const int8_t* wq, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, int32_t* acc, void* stream);
+
 
 /* X diag(s)^-1 at run time, for inputs whose LayerNorm was not folded [P1
  * 数学的に何をしているのか]:  x_hat[m, k] = dt(fp32(x[m, k]) / s[k]), rounded to

@@ -315,6 +315,27 @@ def dequant_bias_act_f32(acc, sx, sw, bias=None, relu=False):
     return y
 
 
+# --------------------------------------------------------------------------
+# Attention products (P1 推論方法: the BMMs run in INT8 as well): the same
+# steps applied to each batch entry (batch x heads), nothing else.
+
+
+def bmm_i32(xq, wq):
+    """acc [B x M x N] = per entry xq[b] wq[b]^T (exact)."""
+    return np.stack([gemm_i32(xq[b], wq[b]) for b in range(xq.shape[0])])
+
+
+def bmm_dequant(acc, sx, sw):
+    """y [B x M x N] (double) = per entry dequant(acc[b], sx[b], sw[b])."""
+    return np.stack([dequant(acc[b], sx[b], sw[b]) for b in range(acc.shape[0])])
+
+
+def quant_weight_perchannel_batched(w):
+    """(wq [B x N x K], sw [B x N]) = per entry quant_weight_perchannel(w[b])."""
+    outs = [quant_weight_perchannel(w[b]) for b in range(w.shape[0])]
+    return np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs])
+
+
 def linear_w8a8(x_hat, wq, sw):
     """Per-token quant + INT8 GEMM + scale back, row by row; y float64 [M x N]."""
     x = _f32(x_hat)

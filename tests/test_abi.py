@@ -143,3 +143,19 @@ def test_layernorm_quant_entry_point_validates(lib):
     assert f(ok[0] + 2, *ok[1:]) == 5
     assert f(*ok[:7], ok[0], *ok[8:]) == 8                      # xq on top of x
     assert f(*ok[:9], 4 * B + 32, None) == 8                    # x_hat inside xq
+
+
+def test_batched_entry_points_validate(lib):
+    # sq_w8a8_bmm_dequant(xq, sx, wq, sw, batch, M, N, K, y, ydt, stream)
+    assert lib.sq_w8a8_bmm_dequant(A, A, A, A, 0, 4, 4, 16, A, 1, None) == 2
+    assert lib.sq_w8a8_bmm_dequant(A, A, A, A, 65536, 4, 4, 16, A, 1, None) == 2
+    assert lib.sq_w8a8_bmm_dequant(A, A, A, A, 2, 4, 4, 200000, A, 1, None) == 4
+    assert lib.sq_w8a8_bmm_dequant(A, None, A, A, 2, 4, 4, 16, A, 1, None) == 1
+    assert lib.sq_w8a8_bmm_dequant(A, A, A, A, 2, 4, 4, 16, A, 9, None) == 3
+    assert lib.sq_w8a8_bmm_dequant(A, A, A + 1, A, 2, 4, 4, 16, A, 1, None) == 5
+    assert lib.sq_w8a8_bmm_i32(A, A, -1, 4, 4, 16, A, None) == 2
+    assert lib.sq_w8a8_bmm_i32(A, A, 2, 4, 4, 16, A + 4, None) == 5
+    # sq_quant_weight_perchannel_batched(w, wdt, batch, K, N, wq, sw, stream)
+    assert lib.sq_quant_weight_perchannel_batched(A, 1, 0, 4, 4, A, A, None) == 2
+    assert lib.sq_quant_weight_perchannel_batched(A, 5, 2, 4, 4, A, A, None) == 3
+    assert lib.sq_quant_weight_perchannel_batched(None, 1, 2, 4, 4, A, A, None) == 1

@@ -590,3 +590,34 @@ def test_layernorm_store_and_quantise_in_the_activation_dtype():
     assert np.array_equal(y, torch.from_numpy(y32).half().float().numpy())
     xq2, sx2 = ref.quant_act_pertoken(y)
     assert np.array_equal(xq, xq2) and np.array_equal(sx, sx2)
+
+
+# --------------------------------------------------------------------------
+# Attention products: per-entry application of the pinned steps
+
+def test_bmm_entries_are_independent_products(ref):
+    from oracle.brute import gemm_int as brute_gemm
+    r = np.random.default_rng(41)
+    xq = r.integers(-127, 128, (3, 5, 9)).astype(np.int8)
+    wq = r.integers(-127, 128, (3, 4, 9)).astype(np.int8)
+    xq[1] = 127
+    wq[2] = -127
+    acc = ref.bmm_i32(xq, wq)
+    for b in range(3):
+        assert acc[b].tolist() == brute_gemm(xq[b].tolist(), wq[b].tolist())
+    sx = r.random((3, 5)).astype(np.float32)
+    sw = r.random((3, 4)).astype(np.float32)
+    y = ref.bmm_dequant(acc, sx, sw)
+    for b in range(3):
+        assert np.array_equal(y[b], ref.dequant(acc[b], sx[b], sw[b]))
+
+
+def test_batched_weight_quant_is_per_entry(ref):
+    r = np.random.default_rng(42)
+    w = r.standard_normal((4, 33, 7)).astype(np.float32)
+    w[2, :, 3] = 0.0  # a zero channel in one entry only
+    wq, sw = ref.quant_weight_perchannel_batched(w)
+    for b in range(4):
+        q1, s1 = ref.quant_weight_perchannel(w[b])
+        assert np.array_equal(wq[b], q1) and np.array_equal(sw[b], s1)
+    assert sw[2, 3] == 0.0 and not wq[2, 3].any()

@@ -31,7 +31,9 @@ __all__ = [
     "quant_weight_pertensor", "linear_w8a8_packed_static", "sq_w8a8_gemm_dequant_ex",
     "sq_w8a8_gemm_dequant_packed_ex", "sq_fold_prev_linear", "w8a8_gemm_dequant_ex",
     "w8a8_gemm_dequant_packed_ex", "fold_prev_linear", "SQ_ACT_NONE", "SQ_ACT_RELU",
-    "sq_layernorm_quant_pertoken", "layernorm_quant_pertoken",
+    "sq_layernorm_quant_pertoken", "layernorm_quant_pertoken", "sq_w8a8_bmm_dequant",
+    "sq_w8a8_bmm_i32", "sq_quant_weight_perchannel_batched", "w8a8_bmm_dequant", "w8a8_bmm_i32",
+    "quant_weight_perchannel_batched",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -82,6 +84,9 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_gemm_dequant_packed_ex": [P, P, P, P, P, E, I64, I64, I64, P, E, P],
             "sq_fold_prev_linear": [P, P, E, I64, I64, P, P, P],
             "sq_layernorm_quant_pertoken": [P, E, I64, I64, P, P, ctypes.c_double, P, P, P, P],
+            "sq_w8a8_bmm_dequant": [P, P, P, P, I64, I64, I64, I64, P, E, P],
+            "sq_w8a8_bmm_i32": [P, P, I64, I64, I64, I64, P, P],
+            "sq_quant_weight_perchannel_batched": [P, E, I64, I64, I64, P, P, P],
             "sq_static_act_step": [P, P, I64, P, P],
             "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
         }
@@ -220,6 +225,34 @@ def sq_w8a8_gemm_i32(xq, wq, acc, stream=None):
         raise ValueError("shape mismatch")
     _call("sq_w8a8_gemm_i32", _dev(xq, "xq", torch.int8), _dev(wq, "wq", torch.int8), M, N, K,
           _dev(acc, "acc", torch.int32), _stream(xq, stream))
+
+
+def sq_w8a8_bmm_dequant(xq, x_scale, wq, w_scale, y, stream=None):
+    B, M, K = xq.shape
+    N = wq.shape[1]
+    if tuple(wq.shape) != (B, N, K) or tuple(x_scale.shape) != (B, M) \
+            or tuple(w_scale.shape) != (B, N) or tuple(y.shape) != (B, M, N):
+        raise ValueError("shape mismatch")
+    _call("sq_w8a8_bmm_dequant", _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32),
+          _dev(wq, "wq", torch.int8), _dev(w_scale, "w_scale", torch.float32), B, M, N, K,
+          _dev(y, "y"), _DT[y.dtype], _stream(xq, stream))
+
+
+def sq_w8a8_bmm_i32(xq, wq, acc, stream=None):
+    B, M, K = xq.shape
+    N = wq.shape[1]
+    if tuple(wq.shape) != (B, N, K) or tuple(acc.shape) != (B, M, N):
+        raise ValueError("shape mismatch")
+    _call("sq_w8a8_bmm_i32", _dev(xq, "xq", torch.int8), _dev(wq, "wq", torch.int8), B, M, N, K,
+          _dev(acc, "acc", torch.int32), _stream(xq, stream))
+
+
+def sq_quant_weight_perchannel_batched(w, wq, w_scale, stream=None):
+    B, K, N = w.shape
+    if tuple(wq.shape) != (B, N, K) or tuple(w_scale.shape) != (B, N):
+        raise ValueError("shape mismatch")
+    _call("sq_quant_weight_perchannel_batched", _dev(w, "w"), _DT[w.dtype], B, K, N,
+          _dev(wq, "wq", torch.int8), _dev(w_scale, "w_scale", torch.float32), _stream(w, stream))
 
 
 def sq_smooth_activation(x, s, x_hat, stream=None):
@@ -410,6 +443,30 @@ def layernorm_quant_pertoken(x, gamma, beta, eps=1e-5, want_x_hat=False, stream=
     xh = torch.empty_like(x) if want_x_hat else None
     sq_layernorm_quant_pertoken(x, gamma, beta, eps, xq, sx, xh, stream)
     return (xq, sx, xh) if want_x_hat else (xq, sx)
+
+
+def w8a8_bmm_dequant(xq, x_scale, wq, w_scale, out_dtype=torch.float16, stream=None):
+    """y [B x M x N] = scale back of the batched INT8 products xq[b] wq[b]^T."""
+    B, M, _ = xq.shape
+    y = torch.empty(B, M, wq.shape[1], dtype=out_dtype, device=xq.device)
+    sq_w8a8_bmm_dequant(xq, x_scale, wq, w_scale, y, stream)
+    return y
+
+
+def w8a8_bmm_i32(xq, wq, stream=None):
+    B, M, _ = xq.shape
+    acc = torch.empty(B, M, wq.shape[1], dtype=torch.int32, device=xq.device)
+    sq_w8a8_bmm_i32(xq, wq, acc, stream)
+    return acc
+
+
+def quant_weight_perchannel_batched(w, stream=None):
+    """(wq [B x N x K], w_scale [B x N]) from w [B x K x N] (e.g. V per head)."""
+    B, K, N = w.shape
+    wq = torch.empty(B, N, K, dtype=torch.int8, device=w.device)
+    sw = torch.empty(B, N, dtype=torch.float32, device=w.device)
+    sq_quant_weight_perchannel_batched(w, wq, sw, stream)
+    return wq, sw
 
 
 def w8a8_gemm_i32(xq, wq, stream=None):

@@ -247,6 +247,42 @@ sq_status sq_w8a8_gemm_dequant_packed_ex(const int8_t* xq, const float* x_scale,
                                              as_stream(stream), epi));
 }
 
+sq_status sq_w8a8_bmm_dequant(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                              const float* w_scale, int64_t batch, int64_t M, int64_t N,
+                              int64_t K, void* y, sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || batch < 1 || batch > 65535) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return SQ_ERR_ALIGN;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_gemm(xq, x_scale, wq, w_scale, M, N, K, y, out, as_stream(stream),
+                                      sq::Epi(), (int)batch));
+}
+
+sq_status sq_w8a8_bmm_i32(const int8_t* xq, const int8_t* wq, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, int32_t* acc, void* stream) {
+    if (!xq || !wq || !acc) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || batch < 1 || batch > 65535) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(acc)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_gemm(xq, nullptr, wq, nullptr, M, N, K, acc, sq::Out::I32,
+                                      as_stream(stream), sq::Epi(), (int)batch));
+}
+
+sq_status sq_quant_weight_perchannel_batched(const void* w, sq_dtype wdt, int64_t batch,
+                                             int64_t K, int64_t N, int8_t* wq, float* w_scale,
+                                             void* stream) {
+    if (!w || !wq || !w_scale) return SQ_ERR_NULL;
+    if (!dims_ok(K, N) || batch < 1 || batch > 65535) return SQ_ERR_SHAPE;
+    if (!dt_ok(wdt)) return SQ_ERR_DTYPE;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)) return SQ_ERR_ALIGN;
+    return hip_status(sq::launch_quant_weight_batched(w, to_dt(wdt), batch, K, N, wq, w_scale,
+                                                      as_stream(stream)));
+}
+
 sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,
                                   int64_t K, int32_t* acc, void* stream) {
     if (!xq || !wq_packed || !acc) return SQ_ERR_NULL;

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ W, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     __shared__ v4i red[NW][TB][64];
+    batch_entry<O>(X, W, sx, sw, Y, M, N, K, (int64_t)N * K);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16;
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     __shared__ v4i red[NW][TB][64];
+    batch_entry<O>(X, Wp, sx, sw, Y, M, N, K, (int64_t)((N + 15) / 16) * 16 * K);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b0 = blockIdx.x, n0 = b0 * 16;
@@ -444,8 +446,8 @@ hipError_t fused_dt(const void* x, Dt xdt, const int8_t* wp, const float* sw, co
 
 template <int TB, Out O, bool EXT>
 hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                     int N, int K, void* y, bool packed, Epi epi, hipStream_t s) {
-    const dim3 grid((unsigned)((N + 15) / 16)), block(kNW * 64);
+                     int N, int K, void* y, bool packed, Epi epi, hipStream_t s, int batch) {
+    const dim3 grid((unsigned)((N + 15) / 16), (unsigned)batch), block(kNW * 64);
     if (packed)
         hipLaunchKernelGGL((gemm_skinny_packed_kernel<TB, kNW, kU, O, EXT>), grid, block, 0, s, xq,
                            w, sx, sw, y, M, N, K, epi);
@@ -460,19 +462,19 @@ hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const f
 
 template <Out O, bool EXT>
 hipError_t skinny_out(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                      int N, int K, void* y, bool packed, Epi epi, hipStream_t s) {
-    if (M <= 16) return skinny_tb<1, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
-    if (M <= 32) return skinny_tb<2, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
-    if (M <= 48) return skinny_tb<3, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
-    return skinny_tb<4, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s);
+                      int N, int K, void* y, bool packed, Epi epi, hipStream_t s, int batch) {
+    if (M <= 16) return skinny_tb<1, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s, batch);
+    if (M <= 32) return skinny_tb<2, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s, batch);
+    if (M <= 48) return skinny_tb<3, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s, batch);
+    return skinny_tb<4, O, EXT>(xq, sx, w, sw, M, N, K, y, packed, epi, s, batch);
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
                          int M, int N, int K, void* y, Out out, bool packed, hipStream_t s,
-                         Epi epi) {
-#define SQ_SK(O, E) return skinny_out<O, E>(xq, sx, w, sw, M, N, K, y, packed, epi, s)
+                         Epi epi, int batch) {
+#define SQ_SK(O, E) return skinny_out<O, E>(xq, sx, w, sw, M, N, K, y, packed, epi, s, batch)
     const bool ext = epi.on();
     switch (out) {
         case Out::I32: SQ_SK(Out::I32, false);

@@ -52,6 +52,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_tiled_kern
     static_assert(BK % 32 == 0, "BK must be a multiple of the MFMA K (32)");
     constexpr int STAGE = (BM + BN) * BK;
     __shared__ __attribute__((aligned(16))) int8_t smem[2 * STAGE];
+    batch_entry<O>(A, B, sx, sw, Y, M, N, K, (int64_t)N * K);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
@@ -207,6 +208,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
     static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 operand stages");
     __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
+    batch_entry<O>(A, B, sx, sw, Y, M, N, K,
+                   PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
@@ -366,6 +369,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             sxv[i] = m < M ? sx[m] : 0.0f;
         }
         asm volatile("s_barrier" ::: "memory");  // all waves are done with the operand stages
+        // float4 scale loads need a 16-byte aligned row of scales (a batch
+        // entry of a product whose N is not a multiple of 4 is not)
+        const bool sw_al = (reinterpret_cast<uintptr_t>(sw) & 15) == 0;
         // One 32-channel column block at a time, so that only its scales
         // (four float4) are live next to the accumulators.
 #pragma unroll
@@ -374,11 +380,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
-                if (n + 3 < N)
+                if (n + 3 < N && sw_al)
                     swv[g] = *reinterpret_cast<const float4*>(sw + n);  // n % 4 == 0
                 else
                     swv[g] = make_float4(n < N ? sw[n] : 0.f, n + 1 < N ? sw[n + 1] : 0.f,
-                                         n + 2 < N ? sw[n + 2] : 0.f, 0.f);
+                                         n + 2 < N ? sw[n + 2] : 0.f, n + 3 < N ? sw[n + 3] : 0.f);
                 if constexpr (EXT) {
                     const float* bb = epi.bias;
                     if (!bb)
@@ -488,22 +494,22 @@ int pick_tile(int M, int N) {
 
 template <Out O, bool PACKED, bool EXT>
 hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
-                      int N, int K, void* y, Epi epi, hipStream_t s) {
+                      int N, int K, void* y, Epi epi, hipStream_t s, int batch = 1) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     switch (pick_tile(M, N)) {
         case 0:
             hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2, EXT>),
-                               dim3(tiles(256, 256)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                               dim3(tiles(256, 256), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
         case 1:
             hipLaunchKernelGGL((gemm_dma_kernel<256, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
-                               dim3(tiles(256, 192)), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
+                               dim3(tiles(256, 192), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
         default:
             hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2, EXT>),
-                               dim3(tiles(128, 128)), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                               dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
     }
@@ -542,15 +548,15 @@ hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t*
 
 template <Out O, bool KVEC, bool EXT>
 hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
-                         int M, int N, int K, void* y, Epi epi, hipStream_t s) {
+                         int M, int N, int K, void* y, Epi epi, hipStream_t s, int batch) {
     if (M <= 64) {
-        return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s, epi);
+        return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s, epi, batch);
     } else if (KVEC && K % 128 == 0) {
-        return launch_dma<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
+        return launch_dma<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s, batch);
     } else {
         constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, SWS = 1;
         const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, BK, WM, WN, SWS, O, KVEC, EXT>), dim3(tiles),
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, BK, WM, WN, SWS, O, KVEC, EXT>), dim3(tiles, batch),
                            dim3((BM / WM) * (BN / WN) * 64), 0, s, xq, wq, sx, sw, y, M, N, K, epi);
     }
     return hipGetLastError();
@@ -558,9 +564,9 @@ hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, co
 
 template <Out O, bool EXT>
 hipError_t gemm_out(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw, int M,
-                    int N, int K, void* y, Epi epi, hipStream_t s) {
-    if (K % 16 == 0) return gemm_dispatch<O, true, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
-    return gemm_dispatch<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s);
+                    int N, int K, void* y, Epi epi, hipStream_t s, int batch) {
+    if (K % 16 == 0) return gemm_dispatch<O, true, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s, batch);
+    return gemm_dispatch<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s, batch);
 }
 
 }  // namespace
@@ -594,9 +600,9 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
-                       hipStream_t s, Epi epi) {
+                       hipStream_t s, Epi epi, int batch) {
     const int m = (int)M, n = (int)N, k = (int)K;
-#define SQ_G(O, E) return gemm_out<O, E>(xq, x_scale, wq, w_scale, m, n, k, y, epi, s)
+#define SQ_G(O, E) return gemm_out<O, E>(xq, x_scale, wq, w_scale, m, n, k, y, epi, s, batch)
     const bool ext = epi.on();
     switch (out) {
         case Out::I32: SQ_G(Out::I32, false);

@@ -7,6 +7,22 @@
 
 namespace sq {
 
+// Entry blockIdx.y of a batched product whose operands, scales and outputs
+// lie back to back (entry z: A + z*M*K, B + z*b_stride, sx + z*M, sw + z*N,
+// Y + z*M*N elements).  Entry 0 is the unbatched call.
+template <Out O, class PA, class PB, class PX, class PW, class PY>
+__device__ inline void batch_entry(PA& A, PB& B, PX& sx, PW& sw, PY& Y, int M, int N, int K,
+                                   int64_t b_stride) {
+    const int64_t z = blockIdx.y;
+    if (z == 0) return;
+    A += z * (int64_t)M * K;
+    B += z * b_stride;
+    if (sx) sx += z * M;
+    if (sw) sw += z * N;
+    constexpr int ES = (O == Out::F16 || O == Out::BF16) ? 2 : 4;
+    Y = static_cast<void*>(static_cast<char*>(Y) + z * (int64_t)M * N * ES);
+}
+
 __device__ inline float dequant(int acc, float sxm, float swn) {
     float f = (float)acc;  // round to nearest even
     f = f * sxm;

@@ -35,6 +35,8 @@ hipError_t launch_static_act_step(const float* a, const float* smooth, int64_t K
                                   hipStream_t s);
 hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
                                          float* w_scale, hipStream_t s);
+hipError_t launch_quant_weight_batched(const void* w, Dt dt, int64_t batch, int64_t K, int64_t N,
+                                       int8_t* wq, float* w_scale, hipStream_t s);
 hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_t Kp, int64_t K,
                                   float* w_out, float* bias, hipStream_t s);
 hipError_t launch_ln_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* gamma,
@@ -44,9 +46,11 @@ hipError_t launch_ln_quant(const void* x, Dt dt, int64_t M, int64_t K, const flo
 int64_t ln_max_k(Dt dt, int64_t K);
 hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
                              void* x_hat, hipStream_t s);
+// batch > 1: `batch` products back to back (see batch_entry), blockIdx.y
+// selecting the entry.
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
-                       hipStream_t s, Epi epi = Epi());
+                       hipStream_t s, Epi epi = Epi(), int batch = 1);
 
 int64_t packed_weight_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp, hipStream_t s);
@@ -57,7 +61,7 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
 // Few-token GEMM (M <= 64): row-major or fragment-packed weights.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
                          int M, int N, int K, void* y, Out out, bool packed, hipStream_t s,
-                         Epi epi = Epi());
+                         Epi epi = Epi(), int batch = 1);
 
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,

@@ -36,6 +36,8 @@ __global__ __launch_bounds__(kColThreads) void colmax_kernel(const typename D::T
                                                              int64_t rows_per_block,
                                                              float* __restrict__ out) {
     constexpr int V = VECT ? D::VEC : 1;
+    x += (int64_t)blockIdx.z * R * C;  // batch entry (0 unbatched)
+    out += (int64_t)blockIdx.z * C;
     const int64_t c0 = ((int64_t)blockIdx.x * kColThreads + threadIdx.x) * V;
     if (c0 >= C) return;
     const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
@@ -69,19 +71,20 @@ __global__ __launch_bounds__(kColThreads) void colmax_kernel(const typename D::T
 }
 
 template <class D>
-hipError_t colmax_typed(const void* xv, int64_t R, int64_t C, float* out, hipStream_t s) {
+hipError_t colmax_typed(const void* xv, int64_t R, int64_t C, float* out, hipStream_t s,
+                        int64_t batch = 1) {
     const typename D::T* x = static_cast<const typename D::T*>(xv);
     const bool vect = (C % D::VEC) == 0;
     const int64_t per_thread = vect ? D::VEC : 1;
     const int64_t col_blocks = (C + kColThreads * per_thread - 1) / (kColThreads * per_thread);
     // Split rows so that the grid has a few thousand workgroups.
-    int64_t splits = (4096 + col_blocks - 1) / col_blocks;
+    int64_t splits = (4096 + col_blocks * batch - 1) / (col_blocks * batch);
     if (splits > R) splits = R;
     if (splits > 65535) splits = 65535;
     if (splits < 1) splits = 1;
     const int64_t rows_per_block = (R + splits - 1) / splits;
     splits = (R + rows_per_block - 1) / rows_per_block;
-    dim3 grid((unsigned)col_blocks, (unsigned)splits);
+    dim3 grid((unsigned)col_blocks, (unsigned)splits, (unsigned)batch);
     if (vect)
         hipLaunchKernelGGL((colmax_kernel<D, true>), grid, dim3(kColThreads), 0, s, x, R, C,
                            rows_per_block, out);
@@ -178,6 +181,9 @@ __global__ __launch_bounds__(kTileThreads) void quant_transpose_kernel(
     const typename D::T* __restrict__ w, int64_t K, int64_t N, const float* __restrict__ absmax,
     int8_t* __restrict__ wq) {
     __shared__ int8_t tile[kTile][kTile + 4];
+    w += (int64_t)blockIdx.z * K * N;  // batch entry (0 unbatched)
+    absmax += (int64_t)blockIdx.z * N;
+    wq += (int64_t)blockIdx.z * N * K;
     const int64_t j0 = (int64_t)blockIdx.y * kTile;
     const int64_t n0 = (int64_t)blockIdx.x * kTile;
     const int t = threadIdx.x;
@@ -316,8 +322,9 @@ hipError_t launch_smooth_fold(const float* a, const void* w, Dt dt, int64_t K, i
 
 template <class D>
 static hipError_t quant_transpose_typed(const void* wv, int64_t K, int64_t N, const float* absmax,
-                                        int8_t* wq, hipStream_t s) {
-    dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile));
+                                        int8_t* wq, hipStream_t s, int64_t batch = 1) {
+    dim3 grid((unsigned)((N + kTile - 1) / kTile), (unsigned)((K + kTile - 1) / kTile),
+              (unsigned)batch);
     hipLaunchKernelGGL((quant_transpose_kernel<D>), grid, dim3(kTileThreads), 0, s,
                        static_cast<const typename D::T*>(wv), K, N, absmax, wq);
     return hipGetLastError();
@@ -374,6 +381,34 @@ hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_
     if (e != hipSuccess || !bias) return e;
     hipLaunchKernelGGL(div_inplace_kernel, dim3((unsigned)((K + 255) / 256 < 1024 ? (K + 255) / 256 : 1024)),
                        dim3(256), 0, s, bias, sm, K);
+    return hipGetLastError();
+}
+
+// Per-column quantisation of `batch` matrices [K x N] lying back to back
+// (each column n of entry b gets its own step; codes transposed to [N x K]).
+hipError_t launch_quant_weight_batched(const void* w, Dt dt, int64_t batch, int64_t K, int64_t N,
+                                       int8_t* wq, float* w_scale, hipStream_t s) {
+    const int64_t n = batch * N;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       w_scale, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (dt) {
+        case Dt::F32: e = colmax_typed<F32>(w, K, N, w_scale, s, batch); break;
+        case Dt::F16: e = colmax_typed<F16>(w, K, N, w_scale, s, batch); break;
+        case Dt::BF16: e = colmax_typed<BF16>(w, K, N, w_scale, s, batch); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    switch (dt) {
+        case Dt::F32: e = quant_transpose_typed<F32>(w, K, N, w_scale, wq, s, batch); break;
+        case Dt::F16: e = quant_transpose_typed<F16>(w, K, N, w_scale, wq, s, batch); break;
+        case Dt::BF16: e = quant_transpose_typed<BF16>(w, K, N, w_scale, wq, s, batch); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(absmax_to_step_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       w_scale, n);
     return hipGetLastError();
 }
 
