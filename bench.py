@@ -202,6 +202,18 @@ def time_graphs(graphs, iters, warmup):
     return e0.elapsed_time(e1) / iters  # ms per replay
 
 
+def time_rotation(fns, iters, warmup, min_calls=4):
+    """ms per call of fns[i]: one graph runs the functions back to back in
+    order (a rotation over buffer sets, repeated to at least `min_calls`
+    calls), as a serving loop would, and is replayed until `iters` calls
+    have run between the events."""
+    seq = list(fns) * max(1, -(-min_calls // len(fns)))
+    g = capture(lambda: [f() for f in seq])
+    reps = max(1, -(-iters // len(seq)))
+    wreps = max(1, -(-warmup // len(seq)))
+    return time_graphs([g], reps, wreps) / len(seq)
+
+
 def profiled_traffic():
     """HBM bytes per GEMM launch from the committed rocprofv3 summary, if it
     was taken on the current GEMM source (else None)."""
@@ -256,14 +268,14 @@ def attention_time(dev, args, H=32, S=2048, D=128):
     for name, fn, nbytes in (
             ("qk", qk, 2 * H * S * D + 2 * H * S * S + 8 * H * S),
             ("pv", pv, H * S * S + H * S * D + 2 * H * S * D + 4 * H * S + 4 * H * D)):
-        ms = time_graphs([capture(fn)], args.steps, args.warmup)
+        ms = time_rotation([fn], args.steps, args.warmup)
         res[name] = {"us": round(ms * 1e3, 2), "tops": round(ops / (ms * 1e-3) / 1e12, 1),
                      "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                      "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
                      "bytes": nbytes}
         log("attention %s: %.1f us, %.1f TOPS, %.0f GB/s" % (name, ms * 1e3, res[name]["tops"],
                                                              res[name]["gbs"]))
-    ms = time_graphs([capture(quants)], args.steps, args.warmup)
+    ms = time_rotation([quants], args.steps, args.warmup)
     qbytes = 3 * H * S * D * 2 + H * S * S * 3 + H * S * D * 2 + 12 * H * S
     res["quant_all_us"] = round(ms * 1e3, 2)
     res["quant_gbs"] = round(qbytes / (ms * 1e-3) / 1e9, 1)
@@ -271,6 +283,64 @@ def attention_time(dev, args, H=32, S=2048, D=128):
                    "sq_quant_act_pertoken for Q, K, P and sq_quant_weight_perchannel_batched for V")
     log("attention quantisers: %.1f us" % (ms * 1e3))
     del q, k, v, p, qq, kq, pq, vq, scores, o
+    torch.cuda.synchronize()
+    return res
+
+
+def decode_llama70b(dev, args):
+    """The decode configuration of the workload set: Llama-70B-like up
+    [8192 x 28672] and down [28672 x 8192] layers, fp16, N(0, 0.015) weights
+    quantised per output channel, 8 persistent outlier channels x50, 1 to 16
+    tokens; one call per layer (sq_w8a8_linear_packed), weights rotated over
+    buffer sets so that every call streams them from HBM."""
+    cfg = synth.CONFIGS[5]
+    lys = []
+    for ly in cfg.layers:
+        w = synth.weight(cfg, ly.name).to(dev)
+        xc = synth.activations(cfg, ly.name, cfg.T, calibration=True).to(dev)
+        a = sq.calibrate_absmax(xc)
+        s_, w_hat = sq.smooth_fold(a, w, ALPHA)
+        wq, sw = sq.quant_weight_perchannel(w_hat)
+        wp = sq.pack_weight(wq)
+        x = sq.smooth_activation(synth.activations(cfg, ly.name, max(cfg.M)).to(dev), s_)
+        lys.append((ly, wp, sw, x))
+        del w, xc, a, w_hat, wq
+        torch.cuda.synchronize()
+    res = {"layers": [[ly.name, ly.K, ly.N] for ly, _, _, _ in lys]}
+    for Md in cfg.M:
+        foot = sum(ly.N * ly.K + Md * ly.K * 3 + Md * ly.N * 2 for ly, _, _, _ in lys)
+        R = n_sets(foot)
+        sets = []
+        for _ in range(R):
+            sets.append([(x[:Md].clone(), wp.clone(), sw.clone(),
+                          torch.empty(Md, ly.K, dtype=torch.int8, device=dev),
+                          torch.empty(Md, dtype=torch.float32, device=dev),
+                          torch.empty(Md, ly.N, dtype=torch.float16, device=dev))
+                         for ly, wp, sw, x in lys])
+        ent = {"buffer_sets": R}
+
+        def run(bset, which):
+            for i in which:
+                xh, wp, sw, xq, sx, y = bset[i]
+                sq.sq_w8a8_linear_packed(xh, wp, sw, xq, sx, y)
+        for key, which in (("step", (0, 1)), ("up", (0,)), ("down", (1,))):
+            nbytes = sum(lys[i][0].N * lys[i][0].K + 4 * lys[i][0].N + 2 * Md * lys[i][0].K
+                         + 2 * Md * lys[i][0].N + 4 * Md for i in which)
+            ms = time_rotation([lambda b=b, w_=which: run(b, w_) for b in sets],
+                               max(args.steps, 4 * R), args.warmup)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            ent[key] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log("llama-70b decode M=%d: step %.1f us (%.1f%% HBM); up %.1f us (%.1f%%), down %.1f us "
+            "(%.1f%%)" % (Md, ent["step"]["us"], 100 * ent["step"]["hbm_frac"], ent["up"]["us"],
+                          100 * ent["up"]["hbm_frac"], ent["down"]["us"],
+                          100 * ent["down"]["hbm_frac"]))
+        res["M=%d" % Md] = ent
+        del sets
+        torch.cuda.synchronize()
+    res["step"] = ("per layer sq_w8a8_linear_packed (per-token quantisation + packed INT8 GEMM "
+                   "+ scale back), up then down; bytes: weights + w_scale + fp16 x + fp16 y")
+    del lys
     torch.cuda.synchronize()
     return res
 
@@ -352,19 +422,17 @@ def main():
     res = {}
     for packed in (False, True):
         sets = [Bufs(layers, M, dev, packed) for _ in range(2)]
-        step_graphs = [capture(b.step) for b in sets]
-        ms = time_graphs(step_graphs, args.steps, args.warmup)
-        gemm_graphs = [capture(b.gemm_only) for b in sets]
-        gemm_ms = time_graphs(gemm_graphs, args.steps, args.warmup) / len(layers)
-        quant_graphs = [capture(b.quant_only) for b in sets]
-        quant_ms = time_graphs(quant_graphs, args.steps, args.warmup) / len(layers)
+        ms = time_rotation([b.step for b in sets], args.steps, args.warmup)
+        gemm_ms = time_rotation([b.gemm_only for b in sets], args.steps, args.warmup) / len(layers)
+        quant_ms = time_rotation([b.quant_only for b in sets], args.steps,
+                                 args.warmup) / len(layers)
         res[packed] = (ms, gemm_ms, quant_ms)
         log("prefill (%s weights): step %.3f ms  %.1f TOPS; gemm avg %.1f us (%.1f TOPS); "
             "quant avg %.1f us (%.0f GB/s)" % ("packed" if packed else "row-major", ms,
                                                ops_step / ms / 1e9, gemm_ms * 1e3,
                                                ops_step / len(layers) / gemm_ms / 1e9,
                                                quant_ms * 1e3, quant_bytes / quant_ms / 1e6))
-        del sets, step_graphs, gemm_graphs, quant_graphs
+        del sets
         torch.cuda.synchronize()
     packed_best = res[True][0] < res[False][0]
     ms, gemm_ms, quant_ms = res[packed_best]
@@ -431,9 +499,9 @@ def main():
         def ln_fn(bset):
             for (x, g, b, xq, sx, xh) in bset:
                 sq.sq_layernorm_quant_pertoken(x, g, b, 1e-5, xq, sx, xh)
-        gr = [capture(lambda bs=bs: ln_fn(bs)) for bs in bufs]
-        ln_ms[hat] = time_graphs(gr, args.steps, args.warmup) / len(ln_layers)
-        del bufs, gr
+        ln_ms[hat] = time_rotation([lambda bs=bs: ln_fn(bs) for bs in bufs], args.steps,
+                                   args.warmup) / len(ln_layers)
+        del bufs
         torch.cuda.synchronize()
     out["layernorm_quant"] = {
         "avg_launch_us": round(ln_ms[False] * 1e3, 2),
@@ -464,10 +532,9 @@ def main():
             entry = {"buffer_sets": R}
             for packed in (True, False):
                 sets = [Bufs(layers, Md, dev, packed) for _ in range(R)]
-                g_step = [capture(b.step) for b in sets]
-                g_gemm = [capture(b.gemm_only) for b in sets]
-                ms_d = time_graphs(g_step, max(args.steps, 4 * R), args.warmup)
-                ms_g = time_graphs(g_gemm, max(args.steps, 4 * R), args.warmup) / len(layers)
+                ms_d = time_rotation([b.step for b in sets], max(args.steps, 4 * R), args.warmup)
+                ms_g = time_rotation([b.gemm_only for b in sets], max(args.steps, 4 * R),
+                                     args.warmup) / len(layers)
                 gbs = nbytes / (ms_d * 1e-3) / 1e9
                 gbs_g = nbytes / len(layers) / (ms_g * 1e-3) / 1e9
                 key = "packed" if packed else "row_major"
@@ -478,10 +545,11 @@ def main():
                               "gemm_hbm_frac": round(gbs_g / PEAK_HBM_GBS, 4)}
                 log("decode M=%d (%s): %.2f us/step, %.0f GB/s (%.1f%% HBM); gemm %.2f us, %.0f GB/s"
                     % (Md, key, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS, ms_g * 1e3, gbs_g))
-                del sets, g_step, g_gemm
+                del sets
                 torch.cuda.synchronize()
             dec["M=%d" % Md] = entry
         out["decode"] = dec
+        out["decode_llama70b"] = decode_llama70b(dev, args)
 
     # ---- O2 (per-tensor dynamic) and O3 (per-tensor static) activations with
     # per-tensor weights, packed layout
@@ -489,9 +557,9 @@ def main():
         lv = {}
         for mode in ("o2", "o3"):
             sets = [Bufs(layers, M, dev, True, mode) for _ in range(2)]
-            ms_l = time_graphs([capture(b.step) for b in sets], args.steps, args.warmup)
-            q_l = time_graphs([capture(b.quant_only) for b in sets], args.steps,
-                              args.warmup) / len(layers)
+            ms_l = time_rotation([b.step for b in sets], args.steps, args.warmup)
+            q_l = time_rotation([b.quant_only for b in sets], args.steps,
+                                args.warmup) / len(layers)
             ent = {"prefill_ms_per_step": round(ms_l, 4),
                    "prefill_tops": round(ops_step / (ms_l * 1e-3) / 1e12, 2),
                    "act_quant_avg_us": round(q_l * 1e3, 2)}
@@ -506,8 +574,8 @@ def main():
                     nbytes = sum(ly.N * ly.K + 4 * ly.N + 2 * Md * ly.K + 2 * Md * ly.N + 4 * Md
                                  for ly in layers)
                     sets = [Bufs(layers, Md, dev, True, mode) for _ in range(R)]
-                    ms_d = time_graphs([capture(b.step) for b in sets], max(args.steps, 4 * R),
-                                       args.warmup)
+                    ms_d = time_rotation([b.step for b in sets], max(args.steps, 4 * R),
+                                         args.warmup)
                     gbs = nbytes / (ms_d * 1e-3) / 1e9
                     ent["decode_M=%d" % Md] = {"us_per_step": round(ms_d * 1e3, 2),
                                                "gbs": round(gbs, 1),

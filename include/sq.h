@@ -305,10 +305,11 @@ sq_status sq_w8a8_gemm_dequant_packed_ex(const int8_t* xq, const float* x_scale,
 
 /* The whole run-time layer on packed weights: per-token quantisation of x
  * (exactly sq_quant_act_pertoken with smooth = NULL, writing xq and x_scale)
- * followed by sq_w8a8_gemm_dequant_packed, in one call.  For M <= 16 and
- * M * K <= 32768 the two steps run as one kernel (every workgroup quantises
- * the few tokens itself while its first weight loads are in flight); other
- * shapes take two launches.  x: [M x K] of dtype xdt; xq: int8 [M x K];
+ * followed by sq_w8a8_gemm_dequant_packed, in one call.  For M <= 2 and
+ * M * K <= 16384 the two steps run as one kernel (every workgroup quantises
+ * the one or two tokens itself while its first weight loads are in flight,
+ * then streams its share of the weight blocks); other shapes take two
+ * launches.  x: [M x K] of dtype xdt; xq: int8 [M x K];
  * x_scale: fp32 [M]; wq_packed as above; w_scale: fp32 [N]; y: [M x N] of
  * ydt.  K % 128 == 0.  xq and x_scale are written in both cases. */
 sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t K,
@@ -319,7 +320,7 @@ sq_status sq_w8a8_linear_packed(const void* x, sq_dtype xdt, int64_t M, int64_t 
  * quantisation is exactly sq_quant_act_pertensor with smooth = NULL and
  * step_in given (no run-time maximum: every token uses *step_in, values
  * beyond 127 steps saturate), followed by sq_w8a8_gemm_dequant_packed.  One
- * kernel for M <= 16 and M * K <= 32768, else two launches.  step_in: device
+ * kernel for M <= 2 and M * K <= 16384, else two launches.  step_in: device
  * pointer to one fp32 (sq_static_act_step's output), not inside x_scale
  * (SQ_ERR_ALIAS).  Other arguments and outputs as sq_w8a8_linear_packed;
  * every x_scale entry is *step_in. */

@@ -236,7 +236,10 @@ def test_pack_weight_layout(dev, N, K):
     assert_equal(wp, _pack_ref(wq), "packed weight bytes")
 
 
-PACKED_SHAPES = [s for s in GEMM_SHAPES if s[2] % 128 == 0] + [(1, 4096, 16384), (16, 300, 128)]
+PACKED_SHAPES = [s for s in GEMM_SHAPES if s[2] % 128 == 0] + [
+    (1, 4096, 16384), (16, 300, 128),
+    # 4 to 16 tokens over 2 or 4 16-channel blocks per workgroup (ragged N too)
+    (4, 8192, 256), (16, 12288, 512), (8, 12300, 1024), (5, 8200, 384), (16, 16384, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", PACKED_SHAPES)
@@ -261,13 +264,14 @@ def test_gemm_packed(ref, dev, M, N, K):
 # ------------------------------------------- whole run-time layer (packed)
 
 LINEAR_CASES = [
-    # M <= 16 and M * K <= 32768: one fused kernel (4 token slots up to M = 4, else 16)
-    (1, 37, 128, "f16", "f16"), (2, 4099, 4096, "bf16", "bf16"), (3, 300, 1024, "f32", "f32"),
-    (4, 12288, 4096, "f16", "f16"), (2, 700, 16384, "f16", "f32"),
-    (1, 512, 28672, "bf16", "f16"),
-    (5, 300, 1024, "f16", "f16"), (8, 300, 2048, "bf16", "f32"), (16, 4099, 2048, "f16", "f16"),
-    (13, 1000, 2048, "f32", "bf16"),
+    # M <= 2 and M * K <= 16384: one fused kernel (persistent over 16-channel blocks)
+    (1, 37, 128, "f16", "f16"), (2, 4099, 4096, "bf16", "bf16"), (2, 300, 1024, "f32", "f32"),
+    (1, 12288, 4096, "f16", "f16"), (1, 4096, 16384, "f16", "f32"), (2, 700, 8192, "bf16", "f16"),
+    (1, 28672, 8192, "f16", "f16"),
     # two launches: quantiser then the packed GEMM
+    (1, 512, 28672, "bf16", "f16"), (2, 700, 16384, "f16", "f32"), (3, 300, 1024, "f32", "f32"),
+    (4, 12288, 4096, "f16", "f16"), (5, 300, 1024, "f16", "f16"), (8, 300, 2048, "bf16", "f32"),
+    (16, 4099, 2048, "f16", "f16"), (13, 1000, 2048, "f32", "bf16"),
     (4, 1000, 16384, "f16", "f32"), (4, 200, 16512, "f16", "f16"), (16, 200, 4096, "f16", "f16"),
     (17, 300, 1024, "f16", "f16"), (64, 600, 2048, "f16", "bf16"), (300, 513, 2048, "bf16", "f16"),
 ]
@@ -303,14 +307,16 @@ def test_linear_packed(ref, dev, M, N, K, xdt, ydt):
     _linear_check(ref, dev, x, wq, ydt)
 
 
-@pytest.mark.parametrize("M", [4, 12])
-def test_linear_packed_special_rows(ref, dev, M):
+@pytest.mark.parametrize("M,pattern", [(2, (0.0, 1e-40)), (2, (1e31, 1.0)), (1, (1e-40,)),
+                                       (4, (0.0, 1e-40, 1e31, 1.0)),
+                                       (12, (0.0, 1e-40, 1e31, 1.0) * 3)])
+def test_linear_packed_special_rows(ref, dev, M, pattern):
     # zero rows (step 0), subnormal steps, steps above 2^96 (IEEE division
-    # path) and ordinary rows, through the fused kernel (4 and 16 token slots).
-    # 1e31 puts the step above 2^96 while fp32(acc) * step stays finite (the
-    # scale-back multiplies in fp32, the oracle in double).
+    # path) and ordinary rows, through the fused kernel (M <= 2) and the
+    # two-launch path.  1e31 puts the step above 2^96 while fp32(acc) * step
+    # stays finite (the scale-back multiplies in fp32, the oracle in double).
     K = 256
-    scale = np.array([0.0, 1e-40, 1e31, 1.0] * (M // 4))[:, None]
+    scale = np.array(pattern)[:, None]
     x = torch.from_numpy((np.random.default_rng(6 + M).standard_normal((M, K)) * scale)
                          .astype(np.float32))
     _, wq = _codes(M, 100, K, 11)

@@ -182,13 +182,14 @@ def _y_check(ref, dev, y, xq_r, sx_r, wq_r, sw_r, what):
     assert_y_close(y_s, y_r, what + " (sampled)")
 
 
-# (M, N, K, x dtype, y dtype): one kernel while M <= 16 and M * K <= 32768,
+# (M, N, K, x dtype, y dtype): one kernel while M <= 2 and M * K <= 16384,
 # else the per-tensor codes kernel and the packed GEMM
 STATIC_LINEAR = [(1, 4096, 4096, "f16", "f16"), (4, 12288, 4096, "f16", "f16"),
                  (2, 28672, 8192, "f16", "bf16"), (16, 1000, 2048, "bf16", "f16"),
                  (3, 4100, 8192, "f32", "f32"), (1, 8, 128, "f16", "f16"),
                  (16, 4096, 4096, "f16", "f16"), (64, 16384, 4096, "f16", "bf16"),
-                 (300, 1000, 1024, "bf16", "f32"), (2048, 12288, 4096, "f16", "f16")]
+                 (300, 1000, 1024, "bf16", "f32"), (2048, 12288, 4096, "f16", "f16"),
+                 (1, 28672, 16384, "f16", "f16"), (2, 700, 4096, "bf16", "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,xdt,ydt", STATIC_LINEAR)

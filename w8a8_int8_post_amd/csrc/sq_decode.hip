@@ -224,12 +224,125 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
 //     from LDS, one stage of two 256-byte steps per wave in flight.
 // LDS: M * K bytes of codes.  STATIC (O3, one step for the whole tensor,
 // given in step_in[0]): step 2 disappears and every token takes that step.
-constexpr int kFusedMaxM = 16;
+// Fragment-packed weights, up to 16 tokens, RB 16-channel blocks per
+// workgroup: each activation fragment a wave loads serves RB weight
+// fragments (RB MFMAs), so with many tokens the activation reads (one
+// kilobyte per fragment, 16 distinct rows) stop doubling the bytes each CU
+// loads per weight byte.
+template <int RB, int NW, int U, Out O, bool EXT>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_rb_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
+    __shared__ v4i red[NW][RB][64];
+    batch_entry<O>(X, Wp, sx, sw, Y, M, N, K, (int64_t)((N + 15) / 16) * 16 * K);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = (N + 15) / 16;
+    const int b0 = blockIdx.x * RB, n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64, nsteps = (KG + 3) / 4;
+    const int8_t* wblk[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+        const int rb = b0 + i < nb ? b0 + i : nb - 1;  // clamped: never stored
+        wblk[i] = Wp + (int64_t)rb * KG * 1024 + lane * 16;
+    }
+    auto load_w = [&](v4i(&w)[U][RB][4], int st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int c = (st + u * NW) * 4 + t;
+                    w[u][i][t] = __builtin_nontemporal_load(
+                        reinterpret_cast<const v4i*>(wblk[i] + (int64_t)(c < KG ? c : KG - 1) * 1024));
+                }
+    };
+    auto load_x = [&](v4i(&x)[U][4], int st) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st + u * NW) * 4 + t;
+                const int tt = r < M ? r : M - 1, cc = c < KG ? c : KG - 1;
+                const v4i v = *reinterpret_cast<const v4i*>(X + (int64_t)tt * K + cc * 64 + g * 16);
+                x[u][t] = (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
+            }
+    };
+    v4i acc[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) acc[i] = v4i{0, 0, 0, 0};
+    auto mf = [&](const v4i(&w)[U][RB][4], const v4i(&x)[U][4]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < RB; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[u][i][t], x[u][t], acc[i], 0, 0, 0);
+    };
+    // the wave's steps st = wave, wave + S, ..., double-buffered as stream_k
+    constexpr int S = NW * U;
+    v4i w0[U][RB][4], w1[U][RB][4];
+    load_w(w0, wave);  // clamped: valid for any wave
+    int st = wave;
+    if (st < nsteps) {
+        while (true) {
+            v4i x[U][4];
+            load_x(x, st);
+            if (st + S >= nsteps) {
+                mf(w0, x);
+                break;
+            }
+            load_w(w1, st + S);
+            mf(w0, x);
+            st += S;
+            load_x(x, st);
+            if (st + S >= nsteps) {
+                mf(w1, x);
+                break;
+            }
+            load_w(w0, st + S);
+            mf(w1, x);
+            st += S;
+        }
+    }
+    // cross-wave sums: wave i adds up block i (accumulator layout as reduce_store)
+#pragma unroll
+    for (int i = 0; i < RB; ++i) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    if (wave < RB) {
+        const int i = wave;
+        v4i tot = red[0][i][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tot += red[w][i][lane];
+        const int tok = lane & 15;
+        if (tok < M) {
+            const float sxm = (O != Out::I32) ? sx[tok] : 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int n = n0 + i * 16 + 4 * g + qq;
+                if (n < N) {
+                    const float swn = (O != Out::I32) ? sw[n] : 0.0f;
+                    store_out_ext<O, EXT>(Y, (int64_t)tok * N + n, tot[qq], sxm, swn, epi, n);
+                }
+            }
+        }
+    }
+}
+
 // Every workgroup quantises all M x K activations itself, which pays off
-// only while that work is small next to streaming the workgroup's weights
-// (measured: 16 x 4096 tokens x channels took 4x longer fused than as two
-// launches; 1 x 28672 and 4 x 8192 are faster fused).
+// only while that work is small next to streaming the workgroup's weights.
+// Measured on one box against quantiser + packed GEMM (two launches):
+// faster fused for 1 token with K = 4096, 8192 and 16384 (10.6 / 39.5 / 15.0
+// us against 13.9 / 42.3 / 17.9); slower for 1 x 28672 (46.9 against 43.9)
+// and for 4 and 8 tokens (4 x 4096: 16.4 against 14.6; 8 x 4096: 38.4
+// against 15.1), where the redundant quantisation dominates.
+constexpr int kFusedMaxM = 2;
+constexpr int kFusedMaxElems = 16384;  // M * K
 constexpr int kFusedMaxLds = 32 * 1024;
+constexpr int kXsPad = 16;  // bytes after each token row of codes in LDS
 constexpr int kFusedMaxCpt = 16;
 constexpr int kFusedU = 2;  // 256-byte K steps per stage in the one-call layer
 
@@ -258,17 +371,23 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     const float* __restrict__ sw, const float* __restrict__ step_in, int8_t* __restrict__ xq_out,
     float* __restrict__ sx_out, void* __restrict__ Y, int M, int N, int K) {
     constexpr int NT = NW * 64, V = D::VEC;
-    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [M][K] codes
+    // [M][K + kXsPad] codes: the pad puts the rows of one MFMA fragment
+    // (16 tokens, same k) on distinct LDS banks; a row pitch of K bytes (a
+    // multiple of 256) would put them all on the same ones
+    extern __shared__ __attribute__((aligned(16))) int8_t xs[];
+    const int XP = K + kXsPad;
     __shared__ v4i red[NW][1][64];
     __shared__ float rmax[MM][NW];
     __shared__ float smax[MM];  // per-token absmax
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int b0 = blockIdx.x, n0 = b0 * 16;
+    const int nblk = (N + 15) / 16;
+    int blk = blockIdx.x;  // this workgroup's 16-channel blocks: blk, blk + gridDim.x, ...
+    const bool wg0 = blockIdx.x == 0;
     const int r = lane & 15, g = lane >> 4;
     const int KG = K / 64, nsteps = (KG + 3) / 4;
     const int nch = K / V, TC = M * nch;  // 16-byte chunks of x
-    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+    const int8_t* wblk = Wp + (int64_t)blk * KG * 1024 + lane * 16;
 
     // 1) activations first, then the first weight stage
     uint4 xr[CPT];
@@ -342,46 +461,69 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
             }
             if constexpr (V == 8) {
                 const uint2 p = *reinterpret_cast<const uint2*>(q);
-                *reinterpret_cast<uint2*>(xs + (int64_t)j * V) = p;
-                if (b0 == 0) *reinterpret_cast<uint2*>(xq_out + (int64_t)j * V) = p;
+                *reinterpret_cast<uint2*>(xs + (j / nch) * XP + (j % nch) * V) = p;
+                if (wg0) *reinterpret_cast<uint2*>(xq_out + (int64_t)j * V) = p;
             } else {
                 const uint32_t p = *reinterpret_cast<const uint32_t*>(q);
-                *reinterpret_cast<uint32_t*>(xs + (int64_t)j * V) = p;
-                if (b0 == 0) *reinterpret_cast<uint32_t*>(xq_out + (int64_t)j * V) = p;
+                *reinterpret_cast<uint32_t*>(xs + (j / nch) * XP + (j % nch) * V) = p;
+                if (wg0) *reinterpret_cast<uint32_t*>(xq_out + (int64_t)j * V) = p;
             }
         }
     }
-    if (b0 == 0 && tid < M) sx_out[tid] = step_of(tid);
+    if (wg0 && tid < M) sx_out[tid] = step_of(tid);
     __syncthreads();
 
     // 4) the weight stream
     auto xfrag = [&](int, int c) -> v4i {
         const int t = r < M ? r : M - 1, cc = c < KG ? c : KG - 1;
-        const v4i v = *reinterpret_cast<const v4i*>(xs + t * K + cc * 64 + g * 16);
+        const v4i v = *reinterpret_cast<const v4i*>(xs + t * XP + cc * 64 + g * 16);
         return (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
     };
     // One stage of U steps in flight per wave, the next issued after the
     // MFMAs of the current one: the first stage (all of a short K) was in
-    // flight during the quantisation, and the stage registers stay few.
-    v4i acc[1] = {v4i{0, 0, 0, 0}};
-    constexpr int S = NW * U;
-    for (int st = wave; st < nsteps; st += S) {
-        v4i x[U][1][4];
-        load_x<1, NW, U>(x, st, xfrag);
-        mfma_stage<1, U>(acc, w, x);
-        if (st + S < nsteps) load_stage<NW, U>(w, st + S, KG, wfrag);
-    }
+    // flight during the quantisation, and the stage registers stay few.  The
+    // workgroup then moves on to its next block (the codes stay in LDS), whose
+    // first stage is issued before this block's cross-wave sum.
     const int tok = lane & 15;  // this lane's token (stored only if < M)
     const float sx_lane = step_of(tok < MM ? tok : 0);
-    reduce_store<1, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
-                           [sx_lane](int) { return sx_lane; });
+    constexpr int S = NW * U;
+    while (true) {
+        v4i acc[1] = {v4i{0, 0, 0, 0}};
+        for (int st = wave; st < nsteps; st += S) {
+            v4i x[U][1][4];
+            load_x<1, NW, U>(x, st, xfrag);
+            mfma_stage<1, U>(acc, w, x);
+            if (st + S < nsteps) load_stage<NW, U>(w, st + S, KG, wfrag);
+        }
+        const int n0 = blk * 16;
+        const int nxt = blk + (int)gridDim.x;
+        if (nxt < nblk) {
+            wblk = Wp + (int64_t)nxt * KG * 1024 + lane * 16;
+            load_stage<NW, U>(w, wave, KG, wfrag);
+        }
+        reduce_store<1, NW, O>(red, acc, wave, lane, n0, M, N, sw, Y,
+                               [sx_lane](int) { return sx_lane; });
+        if (nxt >= nblk) break;
+        __syncthreads();  // every wave has read `red` before the next block writes it
+        blk = nxt;
+    }
 }
 
 template <class D, Out O, int CPT, int MM, bool STATIC>
 hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, const float* step,
                             int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
+    // Persistent workgroups: as many as fit on the GPU at once (LDS holds the
+    // codes, M * K bytes, next to the 8.5 KB reduction buffer), each taking an
+    // equal share of the 16-channel blocks, so that the quantisation is done
+    // once per workgroup rather than once per block.
+    const int nblk = (N + 15) / 16;
+    int per_cu = 163840 / (M * (K + kXsPad) + 9216);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    const int slots = device_cu_count() * per_cu;
+    const int per = (nblk + slots - 1) / slots;
+    const int G = (nblk + per - 1) / per;
     hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT, MM, STATIC>),
-                       dim3((unsigned)((N + 15) / 16)), dim3(kNW * 64), (size_t)M * K, s,
+                       dim3((unsigned)G), dim3(kNW * 64), (size_t)M * (K + kXsPad), s,
                        static_cast<const typename D::T*>(x), wp, sw, step, xq, sx, y, M, N, K);
     return hipGetLastError();
 }
@@ -394,14 +536,6 @@ hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const 
     const int cpt = (M * (K / D::VEC) + kNW * 64 - 1) / (kNW * 64);
 #define SQ_FUSED(C, MMV) \
     return launch_fused_cpt<D, O, C, MMV, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s)
-    if constexpr (!STATIC) {
-        if (M > 4) {
-            if (cpt <= 2) SQ_FUSED(2, 16);
-            if (cpt <= 4) SQ_FUSED(4, 16);
-            if (cpt <= 8) SQ_FUSED(8, 16);
-            SQ_FUSED(16, 16);
-        }
-    }
     if (cpt <= 1) SQ_FUSED(1, 4);
     if (cpt <= 2) SQ_FUSED(2, 4);
     if (cpt <= 4) SQ_FUSED(4, 4);
@@ -414,7 +548,7 @@ hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const 
 // (and LDS) budget, x within the per-thread register budget.
 bool fused_fits(Dt xdt, int64_t M, int64_t K) {
     const int64_t vec = xdt == Dt::F32 ? 4 : 8;
-    return M <= kFusedMaxM && M * K <= kFusedMaxLds &&
+    return M <= kFusedMaxM && M * K <= kFusedMaxElems && M * K <= kFusedMaxLds &&
            M * (K / vec) <= (int64_t)kFusedMaxCpt * kNW * 64;
 }
 
@@ -447,8 +581,23 @@ hipError_t fused_dt(const void* x, Dt xdt, const int8_t* wp, const float* sw, co
 template <int TB, Out O, bool EXT>
 hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
                      int N, int K, void* y, bool packed, Epi epi, hipStream_t s, int batch) {
-    const dim3 grid((unsigned)((N + 15) / 16), (unsigned)batch), block(kNW * 64);
-    if (packed)
+    const int nb = (N + 15) / 16;
+    const dim3 grid((unsigned)nb, (unsigned)batch), block(kNW * 64);
+    // 4 to 16 tokens, packed weights: RB blocks per workgroup share each
+    // activation fragment, as long as the grid keeps >= 192 workgroups (fewer
+    // starve the HBM stream).  Measured on one box, 16 tokens: 28672 x 8192
+    // 48.6 -> 40.9 us (RB 4), 8192 x 28672 52.6 -> 40.9 us (RB 2), 12288 x
+    // 4096 14.7 -> 12.1 us (RB 4); 4096 x 16384 keeps RB 1.
+    if (packed && TB == 1 && M >= 4 && nb >= 512) {
+        if (nb >= 768)
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, kNW, kU, O, EXT>),
+                               dim3((unsigned)((nb + 3) / 4), (unsigned)batch), block, 0, s, xq, w,
+                               sx, sw, y, M, N, K, epi);
+        else
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<2, kNW, kU, O, EXT>),
+                               dim3((unsigned)((nb + 1) / 2), (unsigned)batch), block, 0, s, xq, w,
+                               sx, sw, y, M, N, K, epi);
+    } else if (packed)
         hipLaunchKernelGGL((gemm_skinny_packed_kernel<TB, kNW, kU, O, EXT>), grid, block, 0, s, xq,
                            w, sx, sw, y, M, N, K, epi);
     else if (K % 16 == 0)

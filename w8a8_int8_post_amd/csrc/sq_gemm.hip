@@ -571,6 +571,8 @@ hipError_t gemm_out(const int8_t* xq, const float* sx, const int8_t* wq, const f
 
 }  // namespace
 
+int device_cu_count() { return cu_count(); }
+
 int64_t packed_weight_bytes(int64_t N, int64_t K) { return ((N + 15) / 16) * (K / 64) * 1024; }
 
 hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp, hipStream_t s) {

@@ -52,6 +52,8 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, Out out,
                        hipStream_t s, Epi epi = Epi(), int batch = 1);
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
 int64_t packed_weight_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp, hipStream_t s);
 hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8_t* wp,
