@@ -267,7 +267,7 @@ LINEAR_CASES = [
     # M <= 2 and M * K <= 16384: one fused kernel (persistent over 16-channel blocks)
     (1, 37, 128, "f16", "f16"), (2, 4099, 4096, "bf16", "bf16"), (2, 300, 1024, "f32", "f32"),
     (1, 12288, 4096, "f16", "f16"), (1, 4096, 16384, "f16", "f32"), (2, 700, 8192, "bf16", "f16"),
-    (1, 28672, 8192, "f16", "f16"),
+    (1, 28672, 8192, "f16", "f16"), (2, 16400, 8192, "f32", "f32"),  # 4-wave workgroups
     # two launches: quantiser then the packed GEMM
     (1, 512, 28672, "bf16", "f16"), (2, 700, 16384, "f16", "f32"), (3, 300, 1024, "f32", "f32"),
     (4, 12288, 4096, "f16", "f16"), (5, 300, 1024, "f16", "f16"), (8, 300, 2048, "bf16", "f32"),

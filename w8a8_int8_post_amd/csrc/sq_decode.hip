@@ -509,39 +509,53 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     }
 }
 
-template <class D, Out O, int CPT, int MM, bool STATIC>
+template <class D, Out O, int NW, int U, int CPT, int MM, bool STATIC>
 hipError_t launch_fused_cpt(const void* x, const int8_t* wp, const float* sw, const float* step,
                             int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
     // Persistent workgroups: as many as fit on the GPU at once (LDS holds the
-    // codes, M * K bytes, next to the 8.5 KB reduction buffer), each taking an
-    // equal share of the 16-channel blocks, so that the quantisation is done
-    // once per workgroup rather than once per block.
+    // codes, M * K bytes, next to the reduction buffer; at most 32 waves per
+    // CU), each taking an equal share of the 16-channel blocks, so that the
+    // quantisation is done once per workgroup rather than once per block.
     const int nblk = (N + 15) / 16;
-    int per_cu = 163840 / (M * (K + kXsPad) + 9216);
-    per_cu = per_cu < 1 ? 1 : (per_cu > 4 ? 4 : per_cu);
+    int per_cu = 163840 / (M * (K + kXsPad) + NW * 1024 + 1024);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 32 / NW ? 32 / NW : per_cu);
     const int slots = device_cu_count() * per_cu;
     const int per = (nblk + slots - 1) / slots;
     const int G = (nblk + per - 1) / per;
-    hipLaunchKernelGGL((linear_decode_fused_kernel<D, kNW, kFusedU, O, CPT, MM, STATIC>),
-                       dim3((unsigned)G), dim3(kNW * 64), (size_t)M * (K + kXsPad), s,
+    hipLaunchKernelGGL((linear_decode_fused_kernel<D, NW, U, O, CPT, MM, STATIC>),
+                       dim3((unsigned)G), dim3(NW * 64), (size_t)M * (K + kXsPad), s,
                        static_cast<const typename D::T*>(x), wp, sw, step, xq, sx, y, M, N, K);
     return hipGetLastError();
 }
 
 // CPT: 16-byte chunks of x per thread; MM: token slots of the absmax (the
 // static variant has none and always takes MM = 4).
-template <class D, Out O, bool STATIC>
-hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const float* step,
-                        int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
-    const int cpt = (M * (K / D::VEC) + kNW * 64 - 1) / (kNW * 64);
+template <class D, Out O, int NW, int U, bool STATIC>
+hipError_t launch_fused_nw(const void* x, const int8_t* wp, const float* sw, const float* step,
+                           int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
+    const int cpt = (M * (K / D::VEC) + NW * 64 - 1) / (NW * 64);
 #define SQ_FUSED(C, MMV) \
-    return launch_fused_cpt<D, O, C, MMV, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s)
+    return launch_fused_cpt<D, O, NW, U, C, MMV, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s)
     if (cpt <= 1) SQ_FUSED(1, 4);
     if (cpt <= 2) SQ_FUSED(2, 4);
     if (cpt <= 4) SQ_FUSED(4, 4);
     if (cpt <= 8) SQ_FUSED(8, 4);
     SQ_FUSED(16, 4);
 #undef SQ_FUSED
+}
+
+// Wide layers with long rows take 4-wave workgroups with 4 steps per stage
+// (the same 64 KB of weights in flight per workgroup, twice as many
+// workgroups resident per CU): measured on one box, 1 token x 8192 channels
+// x 28672 outputs 40.6 -> 38.0 us; 4096-channel rows and narrow layers keep
+// 8 waves x 2 steps (4096 x 12288: 10.7 against 11.0 us; 16384 x 4096: 15.3
+// against 16.9 us).
+template <class D, Out O, bool STATIC>
+hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const float* step,
+                        int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
+    if ((N + 15) / 16 >= 1024 && K >= 8192)
+        return launch_fused_nw<D, O, 4, 4, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
+    return launch_fused_nw<D, O, kNW, kFusedU, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
 }
 
 // The one-kernel path applies: few tokens, M * K within the redundant-work
