@@ -84,10 +84,28 @@ def _near_f32_boundary(v: float, err: float) -> bool:
     return abs(v - mid_lo) <= err or abs(v - mid_hi) <= err
 
 
+def sum_exact_in_any_order(row) -> bool:
+    """True when every double sum of the row's values, in any order, is exact:
+    all values are integer multiples of 2^q (q the exponent of the lowest set
+    bit over the row) and sum|values| stays below 2^(52 + q), so every partial
+    sum fits a 53-bit significand.  Holds for 16-bit inputs (fp16, bf16) of
+    ordinary range at the hidden sizes of the workloads."""
+    v = np.asarray(row, np.float64)
+    v = v[v != 0]
+    if v.size == 0:
+        return True
+    mant, ex = np.frexp(np.abs(v))
+    ints = (mant * 2.0 ** 53).astype(np.int64)  # exact: mant holds 53 bits
+    low = ints & -ints  # lowest set bit of each significand
+    q = int((ex - 53 + np.log2(low.astype(np.float64)).astype(np.int64)).min())
+    return math.fsum(np.abs(v).tolist()) < math.ldexp(1.0, 52 + q)
+
+
 def ambiguous_rows(x, eps: float):
     """Rows whose fp32 mu or rstd may differ by one unit when the double sums
     are taken in another order.  A double sum of K terms in any order is
-    within K * 2^-53 * sum|terms| of the exact sum; the bound below carries
+    within K * 2^-53 * sum|terms| of the exact sum (zero when the sum is
+    exact in any order, ``sum_exact_in_any_order``); the bound below carries
     that through mu_d, var_d and rstd_d with margin (a factor of 4) and adds
     two double ulps for each correctly rounded operation."""
     x = np.asarray(x, np.float32).astype(np.float64)
@@ -97,13 +115,16 @@ def ambiguous_rows(x, eps: float):
     for m in range(M):
         row = x[m]
         mu_d, var_d, rstd_d = _row_stats(row, eps)
-        e_mu = 4 * (K * u * float(np.abs(row).sum()) / K + 2 * u * abs(mu_d))
+        # an exact sum makes mu_d the same correctly rounded quotient on both
+        # sides, so fp32(mu_d) is then decided even on a midpoint
+        exact = sum_exact_in_any_order(row)
+        e_mu = 0.0 if exact else 4 * (u * float(np.abs(row).sum()) + 2 * u * abs(mu_d))
         d = np.abs(row - mu_d)
         e_var = 4 * (K * u * float((d * d).sum()) / K + 2 * e_mu * float(d.sum()) / K
                      + e_mu * e_mu + 2 * u * var_d)
         # rstd = (var + eps)^-1/2: relative error half that of var + eps
         e_rstd = 4 * (0.5 * e_var / (var_d + eps) * rstd_d + 4 * u * rstd_d)
-        if _near_f32_boundary(mu_d, e_mu) or _near_f32_boundary(rstd_d, e_rstd):
+        if (not exact and _near_f32_boundary(mu_d, e_mu)) or _near_f32_boundary(rstd_d, e_rstd):
             out.append(m)
     return out
 

@@ -141,3 +141,55 @@ def test_int8_attention_chain(ref, dev, B, S, D):
     rel = np.linalg.norm(to_np(out).astype(np.float64) - of) / np.linalg.norm(of)
     log("  relative error vs float attention:", rel)
     assert rel < 0.08
+
+
+def test_attention_full_size_sampled(ref, dev):
+    """Both products at the timed attention shape (32 heads, 2048 tokens,
+    head_dim 128), fp16 out, in the launch configuration the benchmark uses:
+    every code and step of Q, K, P and V compared in full on sampled heads;
+    accumulators and outputs at sampled (head, query, key / channel) triples."""
+    H, S, D = 32, 2048, 128
+    r = np.random.default_rng([11, H, S, D])
+    q = torch.from_numpy(r.standard_normal((H * S, D), dtype=np.float32)).half()
+    k = torch.from_numpy(r.standard_normal((H * S, D), dtype=np.float32)).half()
+    v = torch.from_numpy(r.standard_normal((H, S, D), dtype=np.float32)).half()
+    # a row-normalised positive matrix standing in for the softmax output
+    p32 = r.exponential(1.0, (H * S, S)).astype(np.float32)
+    p = torch.from_numpy(p32 / p32.sum(axis=1, keepdims=True)).half()
+    del p32
+    qq, sq_ = sq.quant_act_pertoken(q.to(dev))
+    kq, sk = sq.quant_act_pertoken(k.to(dev))
+    pq, sp = sq.quant_act_pertoken(p.to(dev))
+    vq, sv = sq.quant_weight_perchannel_batched(v.to(dev))
+    scores = sq.w8a8_bmm_dequant(qq.view(H, S, D), sq_.view(H, S), kq.view(H, S, D),
+                                 sk.view(H, S), torch.float16)
+    out = sq.w8a8_bmm_dequant(pq.view(H, S, S), sp.view(H, S), vq, sv, torch.float16)
+    torch.cuda.synchronize()
+    rs = np.random.default_rng([12, H, S, D])
+    for h in (0, 13, H - 1):
+        rows = np.sort(rs.choice(S, 40, replace=False))
+        cols = np.sort(rs.choice(S, 40, replace=False))
+        dcols = np.sort(rs.choice(D, 24, replace=False))
+        sl = slice(h * S, (h + 1) * S)
+        xq_r, sx_r = ref.quant_act_pertoken(q[sl].float().numpy())
+        kq_r, sk_r = ref.quant_act_pertoken(k[sl].float().numpy())
+        pq_r, sp_r = ref.quant_act_pertoken(p[sl].float().numpy())
+        vq_r, sv_r = ref.quant_weight_perchannel_batched(v[h:h + 1].float().numpy())
+        assert_equal(qq[sl], xq_r, "Q codes, head %d" % h)
+        assert_equal(sq_[sl], sx_r, "Q steps, head %d" % h)
+        assert_equal(kq[sl], kq_r, "K codes, head %d" % h)
+        assert_equal(sk[sl], sk_r, "K steps, head %d" % h)
+        assert_equal(pq[sl], pq_r, "P codes, head %d" % h)
+        assert_equal(sp[sl], sp_r, "P steps, head %d" % h)
+        assert_equal(vq[h], vq_r[0], "V codes, head %d" % h)
+        assert_equal(sv[h], sv_r[0], "V steps, head %d" % h)
+        for name, y, a, sa, b, sb, c in (
+                ("scores", scores, xq_r, sx_r, kq_r, sk_r, cols),
+                ("output", out, pq_r, sp_r, vq_r[0], sv_r[0], dcols)):
+            acc_r = ref.gemm_i32_sampled(a, b, rows, c)
+            y32 = torch.from_numpy(ref.dequant_bias_act_f32(acc_r, sa[rows], sb[c])).half()
+            ys = y[h].cpu()[torch.from_numpy(rows)][:, torch.from_numpy(c)]
+            assert_equal(ys.view(torch.int16), y32.view(torch.int16).numpy(),
+                         "%s bits, head %d" % (name, h))
+            assert_y_close(ys, ref.dequant(acc_r, sa[rows], sb[c]), "%s, head %d" % (name, h))
+        log("  head %d: ok" % h)

@@ -94,7 +94,7 @@ def test_config_layer(ref, dev, cid, layer):
             y_p = torch.empty(M, N, dtype=ydt, device=dev)
             sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y_p)
             acc_p = sq.w8a8_gemm_i32_packed(xq, wp, N)
-            # the one-call layer (a single fused kernel at M <= 4)
+            # the one-call layer (a single fused kernel at M <= 2 and M * K <= 16384)
             y_f, xq_f, sx_f = sq.linear_w8a8_packed(x_hat, wp, sw, ydt)
             torch.cuda.synchronize()
             rows = _sample(M, NSAMPLE, 3000 * cid + M)
@@ -115,6 +115,11 @@ def test_config_layer(ref, dev, cid, layer):
             assert_equal(xq_f[rows_d], xq_r, "Xq (one-call layer)")
             assert_equal(sx_f[rows_d], sx_r, "x_scale (one-call layer)")
             assert_y_close(y_f[rows_d][:, cols_d], y_r, "y (one-call layer)")
+            # every path rounds RN(RN(fp32(acc) * sx) * sw) once to the output dtype
+            y32 = torch.from_numpy(ref.dequant_bias_act_f32(acc_r, sx_r, sw_r)).to(ydt)
+            for yy, nm in ((y, "y"), (y_p, "y, packed"), (y_f, "y, one-call")):
+                assert_equal(yy[rows_d][:, cols_d].cpu().view(torch.int16),
+                             y32.view(torch.int16).numpy(), nm + " (fp32 order, bits)")
             log("  alpha %.2f M %5d: ok (y bit-equal to RNE(oracle) %.4f)" % (alpha, M, same))
             del x_hat, xq, sx, y, acc, y_p, acc_p, y_f, xq_f, sx_f
         del s, w_hat, wq, sw, wp

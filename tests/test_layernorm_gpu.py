@@ -70,7 +70,7 @@ def _check(dev, x, g, b, eps, dt):
 CASES = [(1, 512, "f32"), (16, 4096, "f16"), (37, 1000, "f16"), (5, 1001, "bf16"),
          (300, 4096, "bf16"), (64, 12288, "f16"), (3, 16384, "f16"), (2, 65536, "f16"),
          (4, 16383, "f32"), (2, 32768, "f32"), (7, 3, "f16"), (129, 5120, "f16"),
-         (2048, 4096, "f16")]
+         (2048, 4096, "f16"), (2048, 12288, "bf16")]
 
 
 @pytest.mark.parametrize("M,K,dt", CASES)
@@ -97,11 +97,13 @@ def test_layernorm_quant_constant_and_special_rows(ref, dev):
         _check(dev, xt, g, b, 1e-5, dt)
 
 
-def test_layernorm_quant_config_opt6_7b(ref, dev):
-    """2048 tokens of the OPT-6.7B-like residual stream (hidden 4096, fp16,
-    0.5% persistent outlier channels x60) through the QKV layer's folded
-    LayerNorm: the calibration, smoothing and fold are the library's own."""
-    cfg = synth.CONFIGS[2]
+@pytest.mark.parametrize("cid", [2, 4])
+def test_layernorm_quant_config(ref, dev, cid):
+    """2048 tokens of the residual stream through the QKV layer's folded
+    LayerNorm: OPT-6.7B-like (hidden 4096, fp16, 0.5% persistent outlier
+    channels x60) and OPT-175B-like (hidden 12288, bf16); the calibration,
+    smoothing and fold are the library's own."""
+    cfg = synth.CONFIGS[cid]
     x = synth.activations(cfg, "qkv", 2048)
     xc = synth.activations(cfg, "qkv", cfg.T, calibration=True)
     w = synth.weight(cfg, "qkv")
@@ -111,4 +113,4 @@ def test_layernorm_quant_config_opt6_7b(ref, dev):
     bd = torch.as_tensor(beta, dtype=torch.float32).contiguous().to(dev)
     sq.smooth_fold(a, w.to(dev), 0.5, gd, bd)
     torch.cuda.synchronize()
-    _check(dev, x, to_np(gd), to_np(bd), 1e-5, "f16")
+    _check(dev, x, to_np(gd), to_np(bd), 1e-5, cfg.act)

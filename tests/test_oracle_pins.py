@@ -572,9 +572,39 @@ def test_layernorm_with_folded_factors_emits_smoothed_activation():
 def test_layernorm_ambiguity_flag():
     from oracle import layernorm as ln
     one = np.float32(1.0)
-    x = np.array([[one, np.nextafter(one, np.float32(2))],      # mean on an fp32 midpoint
-                  [np.float32(1.0), np.float32(2.0)]], np.float32)  # mean 1.5, far from one
+    big = np.float32(2.0 ** 40)
+    x = np.array([
+        # mean 0.5 + 2^-25, an fp32 midpoint, from a sum that depends on the order
+        [one, np.nextafter(one, np.float32(2)), big, -big],
+        # mean 0.75, far from a midpoint; the sum is exact in any order
+        [one, np.float32(2.0), big, -big],
+        # mean 1 + 2^-24, a midpoint, but the sum is exact in any order: decided
+        [one, np.nextafter(one, np.float32(2)), one, one]], np.float32)
     assert ln.ambiguous_rows(x, 1e-5) == [0]
+
+
+def test_sum_exact_in_any_order_against_brute_force():
+    # where the criterion holds, every summation order (sequential double adds
+    # over random permutations) gives the correctly rounded sum; the first
+    # row's sum does depend on the order
+    import math
+    from oracle import layernorm as ln
+    import torch
+    r = np.random.default_rng(34)
+    a = np.array([1.0, 1.0 + 2.0 ** -23, 2.0 ** 40, -2.0 ** 40])
+    assert not ln.sum_exact_in_any_order(a)
+    sums = {float(np.cumsum(a[r.permutation(4)])[-1]) for _ in range(200)}
+    assert len(sums) > 1
+    rows = [torch.from_numpy(r.standard_normal(4096).astype(np.float32) * 20).half()
+            .double().numpy(),
+            torch.from_numpy(r.standard_normal(12288).astype(np.float32)).bfloat16()
+            .double().numpy(),
+            np.array([1.0, 2.0, 2.0 ** 40, -2.0 ** 40]), np.zeros(5)]
+    for row in rows:
+        assert ln.sum_exact_in_any_order(row)
+        want = math.fsum(row.tolist())
+        for _ in range(20):
+            assert float(np.cumsum(row[r.permutation(row.size)])[-1]) == want
 
 
 def test_layernorm_store_and_quantise_in_the_activation_dtype():
