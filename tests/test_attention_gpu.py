@@ -74,7 +74,9 @@ def test_bmm(ref, dev, B, M, N, K, ydt):
 
 @pytest.mark.parametrize("B,K,N,dt", [(4, 256, 128, "f32"), (3, 1000, 64, "f16"),
                                       (2, 77, 33, "bf16"), (32, 2048, 128, "f16"),
-                                      (1, 5, 3, "f16")])
+                                      (1, 5, 3, "f16"), (5, 8192, 16, "bf16"), (7, 528, 24, "f32"),
+                                      (3, 4096, 160, "f16"), (2, 16, 8, "f32"),
+                                      (9, 2048, 64, "bf16")])
 def test_quant_weight_perchannel_batched(ref, dev, B, K, N, dt):
     log("quant_weight_perchannel_batched", B, K, N, dt)
     w = torch.stack([synth.random_matrix(B * 13 + b, K, N, dt, outlier_cols=[b % N], factor=9.0)

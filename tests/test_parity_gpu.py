@@ -78,9 +78,13 @@ def test_smooth_fold(ref, dev, K, N, dt, alpha):
 
 # --------------------------------------------------------------- weight quant
 
-@pytest.mark.parametrize("K,N,dt", [(512, 512, "f32"), (4096, 1000, "f32"), (77, 333, "f32"),
-                                    (1000, 4096, "f16"), (130, 70, "bf16"), (1, 3, "f32"),
-                                    (63, 65, "f16")])
+@pytest.mark.parametrize("K,N,dt", [
+    # one-pass kernel (K % 16 == 0, K <= 8192, N a multiple of 8 fp32 / 16 16-bit columns)
+    (512, 512, "f32"), (4096, 1000, "f32"), (16, 16, "f16"), (528, 24, "f32"),
+    (2064, 32, "f16"), (8192, 48, "bf16"), (4096, 4096, "f16"),
+    # column maxima, then a transposing quantiser
+    (77, 333, "f32"), (1000, 4096, "f16"), (130, 70, "bf16"), (1, 3, "f32"), (63, 65, "f16"),
+    (8208, 16, "f16"), (512, 40, "f16")])
 def test_quant_weight_perchannel(ref, dev, K, N, dt):
     log("quant_weight", K, N, dt)
     w = synth.random_matrix(K * 11 + N, K, N, dt, scale=0.02)
@@ -95,6 +99,11 @@ def test_quant_weight_perchannel(ref, dev, K, N, dt):
 # --------------------------------------------------------------- act quant
 
 @pytest.mark.parametrize("M,K,dt", [(16, 512, "f32"), (2048, 4096, "f16"), (5, 16384, "f16"),
+                                    # many short rows: 8, 16 or 32 lanes per row
+                                    (1024, 64, "f16"), (700, 128, "f16"), (2048, 256, "bf16"),
+                                    (512, 32, "f32"), (515, 16, "f16"), (4096, 128, "f16"),
+                                    # one wave per row, 1, 2 or 4 pieces per lane
+                                    (513, 512, "f16"), (600, 1024, "f32"), (1000, 2048, "f16"),
                                     (3, 49152, "bf16"), (4, 50000, "f16"), (9, 1001, "f16"),
                                     (300, 28672, "f16"), (1, 8, "bf16"), (7, 13, "f32"),
                                     (2, 24576, "f32"), (3, 24580, "f32")])

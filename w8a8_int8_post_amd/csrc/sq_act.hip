@@ -8,9 +8,10 @@
 // One or more wavefronts per token row.  Each lane keeps its slice of the row
 // in registers between the absmax reduction and the quantisation, so the row
 // is read from HBM once; loads are 16 bytes per lane and consecutive lanes
-// read consecutive 16-byte pieces of the row.  Many short rows (prefill) take
-// one wavefront each, reduced without LDS; few rows (decode) are spread over
-// up to 16 wavefronts.  Rows whose length is not a multiple of 16 bytes, or
+// read consecutive 16-byte pieces of the row.  Many rows (prefill) take one
+// wavefront each, or share one when a row has fewer than 64 pieces (the
+// head_dim-long rows of attention), reduced without LDS; few rows (decode)
+// are spread over up to 16 wavefronts.  Rows whose length is not a multiple of 16 bytes, or
 // longer than the register budget, take a two-pass variant (the second pass
 // re-reads the row).
 #include "sq_device.h"
@@ -52,21 +53,34 @@ __device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowSt
     }
 }
 
+// Max over aligned groups of G lanes (G a power of two, at most 64).
+template <int G>
+__device__ inline float group_max(float v) {
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
 // Register-resident variant: WPR waves per token row, each lane holding up to
-// NCH 16-byte pieces of the row (K / VEC <= 64 * WPR * NCH).  A workgroup of
-// NT threads handles NT / (64 * WPR) rows; with WPR == 1 the reduction is a
+// NCH 16-byte pieces of the row (K / VEC <= LPR * WPR * NCH).  Short rows take
+// LPR < 64 lanes each (64 / LPR rows per wave, WPR == 1), so that a wave load
+// still covers 1 KB of consecutive rows.  A workgroup of NT threads handles
+// NT / (64 * WPR) * (64 / LPR) rows; with WPR == 1 the reduction is a
 // wavefront reduction only (no LDS, no barrier).
-template <class D, int NT, int WPR, int NCH, bool SMOOTH>
+template <class D, int NT, int WPR, int NCH, bool SMOOTH, int LPR = 64>
 __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* __restrict__ x,
                                                            const float* __restrict__ smooth,
                                                            int64_t M, int64_t K,
                                                            int8_t* __restrict__ xq,
                                                            float* __restrict__ sx) {
+    static_assert(LPR == 64 || WPR == 1, "rows shorter than a wave take one wave part");
     constexpr int V = D::VEC;
-    constexpr int RPW = NT / (64 * WPR);  // rows per workgroup
+    constexpr int RPV = 64 / LPR;               // rows per wave
+    constexpr int RPW = NT / (64 * WPR) * RPV;  // rows per workgroup
     __shared__ float red[NT / 64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const int sub = lane % LPR;  // the lane's place in its row's lane group
+    const int64_t m = (int64_t)blockIdx.x * RPW + (wave / WPR) * RPV + lane / LPR;
     const int part = wave % WPR;  // which of the row's waves
     const bool live = m < M;
     const typename D::T* row = x + (live ? m : 0) * K;
@@ -78,14 +92,14 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
     uint4 raw[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+        const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
         raw[c] = *reinterpret_cast<const uint4*>(row + (ci < nch ? ci : nch - 1) * V);
     }
     float4 sm[NCH][V / 4];
     if constexpr (SMOOTH) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
             const float* sp = smooth + (ci < nch ? ci : nch - 1) * V;
 #pragma unroll
             for (int q = 0; q < V / 4; ++q) sm[c][q] = *reinterpret_cast<const float4*>(sp + 4 * q);
@@ -95,7 +109,7 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
     float amax = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-        const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+        const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
         const typename D::T* e = reinterpret_cast<const typename D::T*>(&raw[c]);
 #pragma unroll
         for (int q = 0; q < V; ++q) {
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
             for (int q = 0; q < V; ++q) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][q]));
         }
     }
-    amax = wave_max(amax);
+    amax = group_max<LPR>(amax);
     if constexpr (WPR > 1) {
         if (lane == 0) red[wave] = amax;
         __syncthreads();
@@ -121,18 +135,18 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
     }
     if (!live) return;
     const RowStep step = row_step(amax);
-    if (part == 0 && lane == 0) sx[m] = step.step;
+    if (part == 0 && sub == 0) sx[m] = step.step;
     int8_t* qrow = xq + m * K;
     if (step.fast) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
             if (ci < nch) store_codes<true, V>(qrow + ci * V, v[c], step);
         }
     } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            const int64_t ci = ((int64_t)c * WPR + part) * 64 + lane;
+            const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
             if (ci < nch) store_codes<false, V>(qrow + ci * V, v[c], step);
         }
     }
@@ -174,8 +188,28 @@ hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* sm
         hipLaunchKernelGGL((act_quant_2pass_kernel<D, 512, SMOOTH>), dim3((unsigned)M), dim3(512), 0,
                            s, x, smooth, K, xq, sx);
     } else if (M >= 512) {
-        // Many rows: as few waves per row as hold the row at 8 pieces per lane.
-        if (nch <= 64 * 8)
+        // Many rows: short rows share a wave (8, 16 or 32 lanes per row, one
+        // piece per lane); otherwise as few waves per row as hold the row at
+        // up to 8 pieces per lane, and no more pieces per lane than it needs.
+        if (nch <= 8)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 1, SMOOTH, 8>), grid(32), dim3(256),
+                               0, s, x, smooth, M, K, xq, sx);
+        else if (nch <= 16)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 1, SMOOTH, 16>), grid(16), dim3(256),
+                               0, s, x, smooth, M, K, xq, sx);
+        else if (nch <= 32)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 1, SMOOTH, 32>), grid(8), dim3(256),
+                               0, s, x, smooth, M, K, xq, sx);
+        else if (nch <= 64)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 1, SMOOTH>), grid(4), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 64 * 2)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 2, SMOOTH>), grid(4), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 64 * 4)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH>), grid(4), dim3(256), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 64 * 8)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 8, SMOOTH>), grid(4), dim3(256), 0,
                                s, x, smooth, M, K, xq, sx);
         else if (nch <= 128 * 8)

@@ -219,6 +219,137 @@ __global__ __launch_bounds__(kTileThreads) void quant_transpose_kernel(
     }
 }
 
+// One-pass per-column quantisation of [K x N] matrices (K a multiple of 16,
+// at most 4 * NT * 2 rows; N a multiple of CB = 2 * VEC columns).  Workgroup
+// (column block, entry): each thread keeps 4 consecutive rows x one 16-byte
+// piece per pass in registers (raw, NR passes), so the block is read from HBM
+// once; the column maxima are reduced across the workgroup; the codes of the
+// CB output rows, a contiguous [CB x K] block of wq, are assembled in LDS and
+// written with 16-byte stores.  Blocks of neighbouring columns (which share
+// the 128-byte lines of each input row) are mapped to one XCD.
+template <class D, int NT, int NR>
+__global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __restrict__ w,
+                                                      int64_t K, int64_t N, int64_t batch,
+                                                      int8_t* __restrict__ wq,
+                                                      float* __restrict__ w_scale) {
+    constexpr int V = D::VEC, CB = 2 * V, NWV = NT / 64;
+    constexpr int ROWS = NT / 2 * 4;        // rows per pass
+    constexpr int PITCH = ROWS * NR + 16;   // LDS row pitch (bytes): 16-byte aligned, banks shifted
+    __shared__ __attribute__((aligned(16))) int8_t tile[CB * PITCH];
+    __shared__ float red[NWV][CB];
+    __shared__ float steps[CB];
+    // XCD-aware order: hardware block b runs on XCD b % 8; logical blocks
+    // ceil(T / 8) apart go to one XCD, consecutive ones to the same XCD.
+    const int64_t nb = N / CB, T = nb * batch, per = (T + 7) / 8;
+    const int64_t b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    const int64_t full = T - 8 * (per - 1);  // XCDs that hold `per` blocks (the rest per - 1)
+    const int64_t L = xcd < full ? xcd * per + slot : full * per + (xcd - full) * (per - 1) + slot;
+    const int64_t entry = L / nb, n0 = (L % nb) * CB;
+    w += entry * K * N;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int p = t & 1;          // which 16-byte piece of the CB columns
+    const int g = t >> 1;         // row group (4 rows) within a pass
+    uint4 raw[NR][4];
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = (int64_t)q * ROWS + g * 4 + i;
+            raw[q][i] = *reinterpret_cast<const uint4*>(w + (r < K ? r : K - 1) * N + n0 + p * V);
+        }
+    float m[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) m[e] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if ((int64_t)q * ROWS + g * 4 + i < K) {
+                const typename D::T* v = reinterpret_cast<const typename D::T*>(&raw[q][i]);
+#pragma unroll
+                for (int e = 0; e < V; ++e) m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(D::to_f32(v[e])));
+            }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+#pragma unroll
+        for (int off = 32; off >= 2; off >>= 1) m[e] = __builtin_fmaxf(m[e], __shfl_xor(m[e], off, 64));
+    }
+    if (lane < 2) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) red[wave][lane * V + e] = m[e];
+    }
+    __syncthreads();
+    if (t < CB) {
+        float a = red[0][t];
+#pragma unroll
+        for (int v = 1; v < NWV; ++v) a = __builtin_fmaxf(a, red[v][t]);
+        const float st = quant_step(a);
+        steps[t] = st;
+        w_scale[entry * N + n0 + t] = st;
+    }
+    __syncthreads();
+    float st[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) st[e] = steps[p * V + e];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+        if ((int64_t)q * ROWS + g * 4 >= K) continue;  // K % 4 == 0: whole groups
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const typename D::T* v = reinterpret_cast<const typename D::T*>(&raw[q][i]);
+                word |= (uint32_t)(uint8_t)quant_code(D::to_f32(v[e]), st[e]) << (8 * i);
+            }
+            *reinterpret_cast<uint32_t*>(tile + (p * V + e) * PITCH + q * ROWS + g * 4) = word;
+        }
+    }
+    __syncthreads();
+    int8_t* dst = wq + (entry * N + n0) * K;
+    const int64_t per_row = K / 16, pieces = CB * per_row;
+    for (int64_t i = t; i < pieces; i += NT) {
+        const int64_t c = i / per_row, k = (i - c * per_row) * 16;
+        *reinterpret_cast<uint4*>(dst + c * K + k) =
+            *reinterpret_cast<const uint4*>(tile + c * PITCH + k);
+    }
+}
+
+// The one-pass kernel when the shape and alignment allow it (returns false
+// when they do not, and nothing was launched).
+template <class D>
+bool colquant_typed(const void* wv, int64_t batch, int64_t K, int64_t N, int8_t* wq,
+                    float* w_scale, hipStream_t s, hipError_t* err) {
+    constexpr int CB = 2 * D::VEC;
+    const auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (K <= 0 || K % 16 != 0 || K > 8192 || N % CB != 0 || batch > 65535 || !al(wv) || !al(wq))
+        return false;
+    const int64_t T = (N / CB) * batch;
+    if (T > 0x7fffffff) return false;
+    const typename D::T* w = static_cast<const typename D::T*>(wv);
+    const dim3 grid((unsigned)T);
+    if (K <= 512)
+        hipLaunchKernelGGL((colquant_kernel<D, 256, 1>), grid, dim3(256), 0, s, w, K, N, batch, wq, w_scale);
+    else if (K <= 2048)
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 1>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+    else if (K <= 4096)
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 2>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+    else
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 4>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+    *err = hipGetLastError();
+    return true;
+}
+
+bool colquant(const void* w, Dt dt, int64_t batch, int64_t K, int64_t N, int8_t* wq,
+              float* w_scale, hipStream_t s, hipError_t* err) {
+    switch (dt) {
+        case Dt::F32: return colquant_typed<F32>(w, batch, K, N, wq, w_scale, s, err);
+        case Dt::F16: return colquant_typed<F16>(w, batch, K, N, wq, w_scale, s, err);
+        case Dt::BF16: return colquant_typed<BF16>(w, batch, K, N, wq, w_scale, s, err);
+    }
+    return false;
+}
+
 // p[0..n) <- max of p[0..n) (non-negative values).  One workgroup: every
 // read happens before the barriers in block_max, every write after them.
 __global__ __launch_bounds__(1024) void max_fill_kernel(float* p, int64_t n) {
@@ -353,6 +484,8 @@ hipError_t launch_quant_weight_pertensor(const void* w, Dt dt, int64_t K, int64_
 
 hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
                                float* w_scale, hipStream_t s) {
+    hipError_t e1 = hipSuccess;
+    if (colquant(w, dt, 1, K, N, wq, w_scale, s, &e1)) return e1;
     // 1) w_scale <- per-column absmax (zeroed first)
     hipError_t e = launch_colmax(w, dt, K, N, w_scale, true, s);
     if (e != hipSuccess) return e;
@@ -388,6 +521,8 @@ hipError_t launch_fold_prev_linear(const float* sm, const void* w, Dt dt, int64_
 // (each column n of entry b gets its own step; codes transposed to [N x K]).
 hipError_t launch_quant_weight_batched(const void* w, Dt dt, int64_t batch, int64_t K, int64_t N,
                                        int8_t* wq, float* w_scale, hipStream_t s) {
+    hipError_t e1 = hipSuccess;
+    if (colquant(w, dt, batch, K, N, wq, w_scale, s, &e1)) return e1;
     const int64_t n = batch * N;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        w_scale, n);
