@@ -206,7 +206,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     constexpr int EPI = HALF_OUT ? BM * EPI_LD : 0;
     constexpr int SMEM = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
     constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
-    static_assert(NSTAGE >= 2 && NSTAGE <= 4, "2 to 4 operand stages");
+    static_assert(NSTAGE >= 1 && NSTAGE <= 4, "1 to 4 operand stages");
     __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
     batch_entry<O>(A, B, sx, sw, Y, M, N, K,
                    PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
@@ -282,11 +282,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 
     // NSTAGE operand stages in a ring: tiles kt+1 .. kt+NSTAGE-2 stay in
     // flight while tile kt is multiplied, and tile kt+NSTAGE-1 is issued into
-    // the stage that tile kt-1 used.
+    // the stage that tile kt-1 used.  One stage (short K, where a small LDS
+    // footprint lets more workgroups share a CU): tile kt+1 is issued once
+    // every wave is done with tile kt.
     const int nk = K / BK;
+    if constexpr (NSTAGE == 1) {
+        if (nk > 0) issue(0, 0);
+    } else {
 #pragma unroll
-    for (int p = 0; p < NSTAGE - 1; ++p)
-        if (p < nk) issue(p, p * BK);
+        for (int p = 0; p < NSTAGE - 1; ++p)
+            if (p < nk) issue(p, p * BK);
+    }
     int cur = 0;  // stage of tile kt
     for (int kt = 0; kt < nk; ++kt) {
         // This wave's loads of tile kt have landed (loads complete in order,
@@ -309,7 +315,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             bf[0][j] = *reinterpret_cast<const v4i*>(sB + boff(wn0 + j * 32 + (lane & 31), lane >> 5));
-        {
+        if constexpr (NSTAGE > 1) {
             const int nxt = kt + NSTAGE - 1;
             int nbuf = cur + NSTAGE - 1;
             nbuf = nbuf >= NSTAGE ? nbuf - NSTAGE : nbuf;
@@ -335,6 +341,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                     acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[cb][j], af[cb][i], acc[j][i], 0, 0, 0);
         }
         __builtin_amdgcn_iglp_opt(0);  // interleave the LDS reads with the MFMAs
+        if constexpr (NSTAGE == 1) {
+            if (kt + 1 < nk) {
+                __syncthreads();  // every wave's fragment reads of tile kt are done
+                issue(0, (kt + 1) * BK);
+            }
+        }
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
     }
 
@@ -474,13 +486,13 @@ int cu_count() {
     return cached[dev];
 }
 
-int pick_tile(int M, int N) {
+int pick_tile(int M, int N, int batch) {
     const int cus = cu_count();
     int best = 0;
     double best_cost = 0.0;
     for (int c = 0; c < 3; ++c) {
         const TileCfg& t = kTiles[c];
-        const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+        const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * batch;
         const int64_t slots = (int64_t)cus * t.per_cu;
         const int64_t rounds = (tiles + slots - 1) / slots;
         const double cost = (double)rounds * t.bm * t.bn * t.per_cu / t.eff;
@@ -496,7 +508,17 @@ template <Out O, bool PACKED, bool EXT>
 hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
                       int N, int K, void* y, Epi epi, hipStream_t s, int batch = 1) {
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    switch (pick_tile(M, N)) {
+    if (K <= 128) {
+        // One k-tile (attention scores Q K^T over head_dim 128): the launch is
+        // bound by writing the outputs; one operand stage keeps the LDS at
+        // 34 KB, so four workgroups share a CU and one's loads overlap
+        // another's output stores (measured 29% faster than two per CU).
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 4, 1, EXT>),
+                           dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                           epi);
+        return hipGetLastError();
+    }
+    switch (pick_tile(M, N, batch)) {
         case 0:
             hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2, EXT>),
                                dim3(tiles(256, 256), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
