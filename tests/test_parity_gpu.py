@@ -159,10 +159,11 @@ GEMM_SHAPES = [
     (64, 1000, 2000), (48, 64, 512), (33, 200, 1040),            # skinny kernel
     (65, 300, 1040), (300, 513, 2064), (70, 100, 100),
     (1000, 1000, 1008), (129, 255, 48),                          # register-staged tiles
-    (512, 2048, 4096), (257, 256, 4096), (300, 130, 128),        # 128 x 128 DMA tiles
+    (512, 2048, 4096), (257, 256, 4096),                         # 128 x 128 DMA tiles
     (2048, 4096, 256),
     (2048, 12288, 256), (1999, 4100, 384),                       # 256 x 192 DMA tiles
-    (2000, 12300, 128), (2047, 16380, 640),                      # 256 x 256, four stages
+    (2047, 16380, 640),                                          # 256 x 256 DMA tiles
+    (300, 130, 128), (2000, 12300, 128), (65, 64, 128),          # K = 128: one operand stage
 ]
 
 
