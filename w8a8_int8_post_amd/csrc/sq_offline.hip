@@ -220,21 +220,24 @@ __global__ __launch_bounds__(kTileThreads) void quant_transpose_kernel(
 }
 
 // One-pass per-column quantisation of [K x N] matrices (K a multiple of 16,
-// at most 4 * NT * 2 rows; N a multiple of CB = 2 * VEC columns).  Workgroup
-// (column block, entry): each thread keeps 4 consecutive rows x one 16-byte
-// piece per pass in registers (raw, NR passes), so the block is read from HBM
-// once; the column maxima are reduced across the workgroup; the codes of the
-// CB output rows, a contiguous [CB x K] block of wq, are assembled in LDS and
-// written with 16-byte stores.  Blocks of neighbouring columns (which share
-// the 128-byte lines of each input row) are mapped to one XCD.
-template <class D, int NT, int NR>
+// at most 4 * NT / PPR * NR rows; N a multiple of CB = PPR * VEC columns).
+// Workgroup (column block, entry): each thread keeps 4 consecutive rows x one
+// 16-byte piece per pass in registers (raw, NR passes), so the block is read
+// from HBM once; the column maxima are reduced across the workgroup; the codes
+// of the CB output rows, a contiguous [CB x K] block of wq, are assembled in
+// LDS and written with 16-byte stores.  Blocks of neighbouring columns (which
+// share the 128-byte lines of each input row) are mapped to one XCD.  Codes
+// are the IEEE quotient v / step, formed as in the per-token quantiser
+// (Markstein's correction from RN(1 / step)) when the step is in range.
+template <class D, int NT, int NR, int PPR>
 __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __restrict__ w,
                                                       int64_t K, int64_t N, int64_t batch,
                                                       int8_t* __restrict__ wq,
                                                       float* __restrict__ w_scale) {
-    constexpr int V = D::VEC, CB = 2 * V, NWV = NT / 64;
-    constexpr int ROWS = NT / 2 * 4;        // rows per pass
+    constexpr int V = D::VEC, CB = PPR * V, NWV = NT / 64;
+    constexpr int ROWS = NT / PPR * 4;      // rows per pass
     constexpr int PITCH = ROWS * NR + 16;   // LDS row pitch (bytes): 16-byte aligned, banks shifted
+    static_assert(PPR == 1 || PPR == 2, "one or two pieces per row");
     __shared__ __attribute__((aligned(16))) int8_t tile[CB * PITCH];
     __shared__ float red[NWV][CB];
     __shared__ float steps[CB];
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __res
     const int64_t entry = L / nb, n0 = (L % nb) * CB;
     w += entry * K * N;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int p = t & 1;          // which 16-byte piece of the CB columns
-    const int g = t >> 1;         // row group (4 rows) within a pass
+    const int p = t % PPR;        // which 16-byte piece of the CB columns
+    const int g = t / PPR;        // row group (4 rows) within a pass
     uint4 raw[NR][4];
 #pragma unroll
     for (int q = 0; q < NR; ++q)
@@ -272,9 +275,9 @@ __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __res
 #pragma unroll
     for (int e = 0; e < V; ++e) {
 #pragma unroll
-        for (int off = 32; off >= 2; off >>= 1) m[e] = __builtin_fmaxf(m[e], __shfl_xor(m[e], off, 64));
+        for (int off = 32; off >= PPR; off >>= 1) m[e] = __builtin_fmaxf(m[e], __shfl_xor(m[e], off, 64));
     }
-    if (lane < 2) {
+    if (lane < PPR) {
 #pragma unroll
         for (int e = 0; e < V; ++e) red[wave][lane * V + e] = m[e];
     }
@@ -288,9 +291,9 @@ __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __res
         w_scale[entry * N + n0 + t] = st;
     }
     __syncthreads();
-    float st[V];
+    RowStep st[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) st[e] = steps[p * V + e];
+    for (int e = 0; e < V; ++e) st[e] = given_step(steps[p * V + e]);
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
         if ((int64_t)q * ROWS + g * 4 >= K) continue;  // K % 4 == 0: whole groups
@@ -300,7 +303,9 @@ __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __res
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const typename D::T* v = reinterpret_cast<const typename D::T*>(&raw[q][i]);
-                word |= (uint32_t)(uint8_t)quant_code(D::to_f32(v[e]), st[e]) << (8 * i);
+                const float x = D::to_f32(v[e]);
+                const int c = st[e].fast ? quant_code<true>(x, st[e]) : quant_code<false>(x, st[e]);
+                word |= (uint32_t)(uint8_t)c << (8 * i);
             }
             *reinterpret_cast<uint32_t*>(tile + (p * V + e) * PITCH + q * ROWS + g * 4) = word;
         }
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(NT) void colquant_kernel(const typename D::T* __res
 template <class D>
 bool colquant_typed(const void* wv, int64_t batch, int64_t K, int64_t N, int8_t* wq,
                     float* w_scale, hipStream_t s, hipError_t* err) {
-    constexpr int CB = 2 * D::VEC;
+    constexpr int CB = 2 * D::VEC;  // two pieces per row and workgroup
     const auto al = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     if (K <= 0 || K % 16 != 0 || K > 8192 || N % CB != 0 || batch > 65535 || !al(wv) || !al(wq))
         return false;
@@ -329,13 +334,13 @@ bool colquant_typed(const void* wv, int64_t batch, int64_t K, int64_t N, int8_t*
     const typename D::T* w = static_cast<const typename D::T*>(wv);
     const dim3 grid((unsigned)T);
     if (K <= 512)
-        hipLaunchKernelGGL((colquant_kernel<D, 256, 1>), grid, dim3(256), 0, s, w, K, N, batch, wq, w_scale);
+        hipLaunchKernelGGL((colquant_kernel<D, 256, 1, 2>), grid, dim3(256), 0, s, w, K, N, batch, wq, w_scale);
     else if (K <= 2048)
-        hipLaunchKernelGGL((colquant_kernel<D, 1024, 1>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 1, 2>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
     else if (K <= 4096)
-        hipLaunchKernelGGL((colquant_kernel<D, 1024, 2>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 2, 2>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
     else
-        hipLaunchKernelGGL((colquant_kernel<D, 1024, 4>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
+        hipLaunchKernelGGL((colquant_kernel<D, 1024, 4, 2>), grid, dim3(1024), 0, s, w, K, N, batch, wq, w_scale);
     *err = hipGetLastError();
     return true;
 }
