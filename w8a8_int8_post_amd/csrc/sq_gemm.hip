@@ -353,6 +353,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     // Epilogue.  Sub-tile (j, i), lane l: token m = i*32 + l%32; elements
     // 4g..4g+3 are output channels 8g + 4*(l/32) + 0..3.
     if constexpr (!HALF_OUT) {
+        // 32-bit outputs: a lane's four consecutive channels as one 16-byte
+        // store where the row allows it (N % 4 == 0, Y 16-byte aligned)
+        const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int m = m0 + wm0 + i * 32 + (lane & 31);
@@ -363,6 +366,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+                    if (vec && n + 3 < N) {
+                        if constexpr (O == Out::I32) {
+                            const v4i v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
+                                           acc[j][i][4 * g + 3]};
+                            *reinterpret_cast<v4i*>(static_cast<int*>(Y) + (int64_t)m * N + n) = v;
+                        } else {
+                            float v[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (EXT)
+                                    v[e] = dequant_ext(acc[j][i][4 * g + e], sxm, sw[n + e],
+                                                       epi.bias ? epi.bias[n + e] : 0.0f, epi.relu);
+                                else
+                                    v[e] = dequant(acc[j][i][4 * g + e], sxm, sw[n + e]);
+                            }
+                            *reinterpret_cast<float4*>(static_cast<float*>(Y) + (int64_t)m * N + n) =
+                                make_float4(v[0], v[1], v[2], v[3]);
+                        }
+                        continue;
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (n + e < N) {
@@ -466,7 +489,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 // two rounds of the 2048 x 12288 QKV shape that 256 x 256 covers in one and
 // a half), 128 x 128 (two per CU).  All use BK 128 and two operand stages.
 // The efficiencies are measured relative throughputs per unit of tile area
-// on whole rounds.
+// on whole rounds.  (K <= 128 bypasses the model: see launch_dma.)
 struct TileCfg {
     int bm, bn, per_cu;
     double eff;
