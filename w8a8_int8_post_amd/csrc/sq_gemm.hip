@@ -189,7 +189,7 @@ __device__ inline void wait_vm() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1,
-          int NSTAGE = 2, bool EXT = false>
+          int NSTAGE = 2, bool EXT = false, bool NTS = false /* non-temporal output stores */>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
@@ -367,23 +367,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
                 for (int g = 0; g < 4; ++g) {
                     const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
                     if (vec && n + 3 < N) {
+                        v4i v;
                         if constexpr (O == Out::I32) {
-                            const v4i v = {acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
-                                           acc[j][i][4 * g + 3]};
-                            *reinterpret_cast<v4i*>(static_cast<int*>(Y) + (int64_t)m * N + n) = v;
+                            v = v4i{acc[j][i][4 * g], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
+                                    acc[j][i][4 * g + 3]};
                         } else {
-                            float v[4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
+                                float f;
                                 if constexpr (EXT)
-                                    v[e] = dequant_ext(acc[j][i][4 * g + e], sxm, sw[n + e],
-                                                       epi.bias ? epi.bias[n + e] : 0.0f, epi.relu);
+                                    f = dequant_ext(acc[j][i][4 * g + e], sxm, sw[n + e],
+                                                    epi.bias ? epi.bias[n + e] : 0.0f, epi.relu);
                                 else
-                                    v[e] = dequant(acc[j][i][4 * g + e], sxm, sw[n + e]);
+                                    f = dequant(acc[j][i][4 * g + e], sxm, sw[n + e]);
+                                v[e] = __float_as_int(f);
                             }
-                            *reinterpret_cast<float4*>(static_cast<float*>(Y) + (int64_t)m * N + n) =
-                                make_float4(v[0], v[1], v[2], v[3]);
                         }
+                        v4i* dst = reinterpret_cast<v4i*>(static_cast<int*>(Y) + (int64_t)m * N + n);
+                        if constexpr (NTS)
+                            __builtin_nontemporal_store(v, dst);
+                        else
+                            *dst = v;
                         continue;
                     }
 #pragma unroll
@@ -468,7 +472,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             T* y = static_cast<T*>(Y) + (int64_t)m * N + n0 + col;
             const int8_t* src = smem + row * EPI_LD + col * 2;
             if (full_n) {
-                *reinterpret_cast<uint4*>(y) = *reinterpret_cast<const uint4*>(src);
+                const v4i v = *reinterpret_cast<const v4i*>(src);
+                if constexpr (NTS)
+                    __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(y));
+                else
+                    *reinterpret_cast<v4i*>(y) = v;
             } else {
                 const T* s16 = reinterpret_cast<const T*>(src);
                 for (int e = 0; e < 8; ++e)
@@ -535,8 +543,10 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         // One k-tile (attention scores Q K^T over head_dim 128): the launch is
         // bound by writing the outputs; one operand stage keeps the LDS at
         // 34 KB, so four workgroups share a CU and one's loads overlap
-        // another's output stores (measured 29% faster than two per CU).
-        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 4, 1, EXT>),
+        // another's output stores (measured 29% faster than two per CU), and
+        // the outputs are stored non-temporally (another 20%: they are far
+        // larger than the caches and are not read again by this launch).
+        hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 4, 1, EXT, true>),
                            dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
                            epi);
         return hipGetLastError();
