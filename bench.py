@@ -14,8 +14,8 @@ The same layers at 1 and 16 tokens (decode) are timed as well and reported
 under "decode" in GB/s.  Buffer sets rotate so that weights are streamed from
 HBM rather than served by the 256 MB Infinity Cache.
 
-Prints one JSON line.  `--gpus N` with N > 1 exits: this build measures one
-GPU (see the design doc for how the path shards).
+Prints one JSON line.  `--gpus N` with N > 1 exits: the benchmark measures
+one GPU (one GPU's share of a layer at its real shape).
 """
 from __future__ import annotations
 
@@ -396,8 +396,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the SmoothQuant W8A8 path is benchmarked on a single "
-              "MI355X (one GPU's shard at its real shape); multi-GPU runs are not part of this "
-              "build.", file=sys.stderr)
+              "MI355X (one GPU's shard at its real shape); it has no multi-GPU mode.",
+              file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
