@@ -58,7 +58,8 @@ typedef enum {
     SQ_ERR_HIP = 7,         /* the HIP runtime reported a launch error */
     SQ_ERR_ALIAS = 8,       /* two buffers overlap where the entry point forbids it */
     SQ_ERR_ACT = 9,         /* activation code not one of sq_act */
-    SQ_ERR_EPS = 10         /* LayerNorm epsilon negative or not finite */
+    SQ_ERR_EPS = 10,        /* LayerNorm epsilon negative or not finite */
+    SQ_ERR_WORKSPACE = 11   /* workspace NULL, misaligned or smaller than required */
 } sq_status;
 
 typedef enum { SQ_F32 = 0, SQ_F16 = 1, SQ_BF16 = 2 } sq_dtype;
@@ -295,6 +296,36 @@ sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
                                       int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream);
 sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int64_t M, int64_t N,
                                   int64_t K, int32_t* acc, void* stream);
+
+/* Split-K forms of sq_w8a8_gemm_dequant and sq_w8a8_gemm_dequant_packed
+ * (identical results), for few tokens against a narrow, deep layer, where the
+ * output tiles alone leave most compute units idle (e.g. 512 tokens through a
+ * 16384 x 4096 layer; the split is taken for K >= 8192 when the 128 x 128
+ * output tiles fill at most a quarter of the GPU's workgroup slots).  K is
+ * split into 2, 4 or 8 ranges; each range's int32
+ * partial products go to the workspace, and the scale back runs once the
+ * ranges of an output tile are summed (integer sums, so the result does not
+ * depend on their order).  When the shape does not call for a split
+ * (sq_gemm_workspace_bytes returns 0) the call is the plain GEMM and the
+ * workspace is not touched.
+ *
+ * workspace: device memory owned by the caller, 16-byte aligned, at least
+ * sq_gemm_workspace_bytes(M, N, K) bytes (queried with the same device
+ * current), all zero before its first use; every call leaves its counters at
+ * zero again, so one zero fill serves any number of calls of any shapes.
+ * Calls that run at the same time must not share a workspace.  Errors:
+ * SQ_ERR_WORKSPACE for a NULL, misaligned or too small workspace (when one
+ * is needed), SQ_ERR_ALIAS when it overlaps an operand or y; else as the
+ * plain entry points (the packed form needs K % 128 == 0). */
+int64_t sq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+sq_status sq_w8a8_gemm_dequant_ws(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                                  sq_dtype ydt, void* workspace, int64_t workspace_bytes,
+                                  void* stream);
+sq_status sq_w8a8_gemm_dequant_packed_ws(const int8_t* xq, const float* x_scale,
+                                         const int8_t* wq_packed, const float* w_scale, int64_t M,
+                                         int64_t N, int64_t K, void* y, sq_dtype ydt,
+                                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* sq_w8a8_gemm_dequant_ex with the weights in the packed layout; identical
  * results.  K % 128 == 0. */

@@ -89,6 +89,8 @@ def load_library() -> ctypes.CDLL:
             "sq_quant_weight_perchannel_batched": [P, E, I64, I64, I64, P, P, P],
             "sq_static_act_step": [P, P, I64, P, P],
             "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
+            "sq_w8a8_gemm_dequant_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
+            "sq_w8a8_gemm_dequant_packed_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -96,6 +98,8 @@ def load_library() -> ctypes.CDLL:
             fn.restype = ctypes.c_int
         lib.sq_packed_weight_bytes.argtypes = [I64, I64]
         lib.sq_packed_weight_bytes.restype = I64
+        lib.sq_gemm_workspace_bytes.argtypes = [I64, I64, I64]
+        lib.sq_gemm_workspace_bytes.restype = I64
         lib.sq_version.argtypes = []
         lib.sq_version.restype = ctypes.c_char_p
         _lib = lib
@@ -288,6 +292,46 @@ def sq_w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, N, y, stream=No
     _call("sq_w8a8_gemm_dequant_packed", _dev(xq, "xq", torch.int8),
           _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
           _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype],
+          _stream(xq, stream))
+
+
+def sq_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes the split-K entry points need for this shape on the
+    current device (0: no split, the plain GEMM runs)."""
+    n = load_library().sq_gemm_workspace_bytes(M, N, K)
+    if n < 0:
+        raise ValueError("invalid shape")
+    return n
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def sq_w8a8_gemm_dequant_ws(xq, x_scale, wq, w_scale, y, workspace, stream=None):
+    M, K = xq.shape
+    N = wq.shape[0]
+    if tuple(wq.shape) != (N, K) or tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    wp, wb = _ws(workspace)
+    _call("sq_w8a8_gemm_dequant_ws", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq, "wq", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype], wp, wb,
+          _stream(xq, stream))
+
+
+def sq_w8a8_gemm_dequant_packed_ws(xq, x_scale, wq_packed, w_scale, N, y, workspace,
+                                   stream=None):
+    M, K = xq.shape
+    if tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    wp, wb = _ws(workspace)
+    _call("sq_w8a8_gemm_dequant_packed_ws", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype], wp, wb,
           _stream(xq, stream))
 
 
@@ -497,6 +541,24 @@ def w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, out_dtype=torch.fl
     N = w_scale.shape[0]
     y = torch.empty(xq.shape[0], N, dtype=out_dtype, device=xq.device)
     sq_w8a8_gemm_dequant_packed(xq, x_scale, wq_packed, w_scale, N, y, stream)
+    return y
+
+
+def gemm_workspace(M: int, N: int, K: int, device) -> torch.Tensor:
+    """A zero-filled workspace for the split-K entry points (at least 16
+    bytes, so that a shape without a split still gets a valid pointer)."""
+    n = max(sq_gemm_workspace_bytes(M, N, K), 16)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def w8a8_gemm_dequant_packed_ws(xq, x_scale, wq_packed, w_scale, out_dtype=torch.float16,
+                                workspace=None, stream=None):
+    N = w_scale.shape[0]
+    M, K = xq.shape
+    if workspace is None:
+        workspace = gemm_workspace(M, N, K, xq.device)
+    y = torch.empty(M, N, dtype=out_dtype, device=xq.device)
+    sq_w8a8_gemm_dequant_packed_ws(xq, x_scale, wq_packed, w_scale, N, y, workspace, stream)
     return y
 
 

@@ -208,6 +208,57 @@ sq_status sq_w8a8_gemm_dequant_packed(const int8_t* xq, const float* x_scale,
                                              as_stream(stream)));
 }
 
+int64_t sq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (!dims_ok(M, N) || K < 1 || K > SQ_MAX_K) return -1;
+    return sq::splitk_workspace_bytes(M, N, K);
+}
+
+}  // extern "C"
+
+namespace {
+sq_status gemm_ws(const int8_t* xq, const float* x_scale, const int8_t* w, const float* w_scale,
+                  int64_t M, int64_t N, int64_t K, void* y, sq_dtype ydt, void* workspace,
+                  int64_t workspace_bytes, bool packed, void* stream) {
+    if (!xq || !x_scale || !w || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || (packed && K % 128 != 0)) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(w) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return SQ_ERR_ALIGN;
+    const int64_t need = sq::splitk_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SQ_ERR_WORKSPACE;
+        const int64_t wbytes = packed ? sq::packed_weight_bytes(N, K) : N * K;
+        if (overlaps(workspace, need, y, M * N * dt_bytes(ydt)) ||
+            overlaps(workspace, need, xq, M * K) || overlaps(workspace, need, w, wbytes) ||
+            overlaps(workspace, need, x_scale, 4 * M) || overlaps(workspace, need, w_scale, 4 * N))
+            return SQ_ERR_ALIAS;
+    }
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_gemm_splitk(xq, x_scale, w, w_scale, M, N, K, y, out, packed,
+                                             static_cast<int32_t*>(workspace), as_stream(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+sq_status sq_w8a8_gemm_dequant_ws(const int8_t* xq, const float* x_scale, const int8_t* wq,
+                                  const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                                  sq_dtype ydt, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+    return gemm_ws(xq, x_scale, wq, w_scale, M, N, K, y, ydt, workspace, workspace_bytes, false,
+                   stream);
+}
+
+sq_status sq_w8a8_gemm_dequant_packed_ws(const int8_t* xq, const float* x_scale,
+                                         const int8_t* wq_packed, const float* w_scale, int64_t M,
+                                         int64_t N, int64_t K, void* y, sq_dtype ydt,
+                                         void* workspace, int64_t workspace_bytes, void* stream) {
+    return gemm_ws(xq, x_scale, wq_packed, w_scale, M, N, K, y, ydt, workspace, workspace_bytes,
+                   true, stream);
+}
+
 sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                   const float* w_scale, const float* bias, int act, int64_t M,
                                   int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream) {

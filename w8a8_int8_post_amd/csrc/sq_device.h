@@ -10,6 +10,7 @@
 namespace sq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- dtypes

@@ -189,7 +189,8 @@ __device__ inline void wait_vm() {
 }
 
 template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1,
-          int NSTAGE = 2, bool EXT = false, bool NTS = false /* non-temporal output stores */>
+          int NSTAGE = 2, bool EXT = false, bool NTS = false /* non-temporal output stores */,
+          bool SPLITK = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
@@ -208,8 +209,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
     static_assert(NSTAGE >= 1 && NSTAGE <= 4, "1 to 4 operand stages");
     __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
-    batch_entry<O>(A, B, sx, sw, Y, M, N, K,
-                   PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
+    // SPLITK: blockIdx.y is the split (a contiguous range of K / epi.splits,
+    // a multiple of BK); otherwise it is the batch entry
+    int koff = 0;
+    if constexpr (SPLITK)
+        koff = (int)blockIdx.y * (K / epi.splits);
+    else
+        batch_entry<O>(A, B, sx, sw, Y, M, N, K,
+                       PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
@@ -240,7 +247,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     for (int i = 0; i < A_INS; ++i) {
         const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
         const int gm = m0 + row < M ? m0 + row : M - 1;
-        asrc[i] = A + (int64_t)gm * K + c * 16;
+        asrc[i] = A + (int64_t)gm * K + koff + c * 16;
     }
     const int KG = K / 64;  // 64-byte k-groups per packed row block
 #pragma unroll
@@ -250,11 +257,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             const int q = i * NW + wave;
             const int nb = (N + 15) / 16;
             const int rb = n0 / 16 + q / KGT < nb ? n0 / 16 + q / KGT : nb - 1;
-            bsrc[i] = B + ((int64_t)rb * KG + (q % KGT)) * 1024 + lane * 16;
+            bsrc[i] = B + ((int64_t)rb * KG + koff / 64 + (q % KGT)) * 1024 + lane * 16;
         } else {
             const int p = (i * NW + wave) * 64 + lane, row = p / CPR, c = (p % CPR) ^ swz(row);
             const int gn = n0 + row < N ? n0 + row : N - 1;
-            bsrc[i] = B + (int64_t)gn * K + c * 16;
+            bsrc[i] = B + (int64_t)gn * K + koff + c * 16;
         }
     }
     auto issue = [&](int buf, int k0) {
@@ -285,7 +292,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     // the stage that tile kt-1 used.  One stage (short K, where a small LDS
     // footprint lets more workgroups share a CU): tile kt+1 is issued once
     // every wave is done with tile kt.
-    const int nk = K / BK;
+    const int nk = (SPLITK ? K / epi.splits : K) / BK;
     if constexpr (NSTAGE == 1) {
         if (nk > 0) issue(0, 0);
     } else {
@@ -348,6 +355,78 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             }
         }
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+    }
+
+    if constexpr (SPLITK) {
+        // Split-K: every split stores its int32 partial tile in its own slice
+        // [M x N] of the workspace (after kSplitkCounters tile counters), then
+        // counts itself in the tile's counter; the split that arrives last
+        // adds the other slices to its accumulators (integer sums: exact in
+        // any order), resets the counter to zero for the next call and runs
+        // the scale back.  No split waits for another.  N % 4 == 0 (one
+        // 16-byte access per lane).  The slices are written and read with the
+        // sc0 sc1 cache policy, i.e. through to and from the device's
+        // coherence point (the XCDs' L2 caches are not coherent with one
+        // another): a split's stores have completed there (vmcnt 0) before it
+        // counts itself, and the last split reads only after its count
+        // returned, so it sees every other slice without flushing any cache.
+        constexpr int kCoherent = 1 | 16;  // sc0 | sc1
+        __shared__ int sk_last;
+        const int split = blockIdx.y, S = epi.splits;
+        int32_t* slices = epi.ws + kSplitkCounters;
+        const int64_t MN = (int64_t)M * N;
+        auto slice = [&](int o) {
+            return __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(slices + o * MN), (short)0,
+                                                     (int)(MN * 4), 0x00020000);
+        };
+        {
+            const __amdgpu_buffer_rsrc_t mine = slice(split);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = m0 + wm0 + i * 32 + (lane & 31);
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+                        if (n < N)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(v4u, v4i{acc[j][i][4 * g], acc[j][i][4 * g + 1],
+                                                            acc[j][i][4 * g + 2], acc[j][i][4 * g + 3]}),
+                                mine, (m * N + n) * 4, 0, kCoherent);
+                    }
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slice stores are done
+        __syncthreads();
+        int* cnt = reinterpret_cast<int*>(epi.ws) + (m0 / BM) * nbn + n0 / BN;
+        if (tid == 0) sk_last = atomicAdd(cnt, 1) == S - 1;
+        __syncthreads();
+        if (!sk_last) return;
+        for (int o = 0; o < S; ++o) {
+            if (o == split) continue;
+            const __amdgpu_buffer_rsrc_t theirs = slice(o);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = m0 + wm0 + i * 32 + (lane & 31);
+                if (m >= M) continue;
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + wn0 + j * 32 + 8 * g + 4 * (lane >> 5);
+                        if (n < N) {
+                            const v4i p = __builtin_bit_cast(
+                                v4i, __builtin_amdgcn_raw_buffer_load_b128(theirs, (m * N + n) * 4, 0,
+                                                                           kCoherent));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[j][i][4 * g + e] += p[e];
+                        }
+                    }
+            }
+        }
+        if (tid == 0) atomicExch(cnt, 0);
     }
 
     // Epilogue.  Sub-tile (j, i), lane l: token m = i*32 + l%32; elements
@@ -652,6 +731,66 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
         case Out::F32: if (ext) SQ_PK(Out::F32, true); SQ_PK(Out::F32, false);
     }
 #undef SQ_PK
+    return hipErrorInvalidValue;
+}
+
+// Split-K: 128 x 128 tiles, two workgroups per CU.  Workspace layout: a
+// fixed block of kSplitkCounters tile counters (only ever zero between
+// calls, whatever the shape), then the splits' int32 slices [S][M][N].
+// K is split only for deep layers (K >= 8192) whose output tiles fill at
+// most a quarter of the slots (few tokens against a narrow layer: 512 x 4096
+// x 16384 has 128 tiles for 512 slots), in 2, 4 or 8 ranges of at least 1024
+// (a multiple of 128) so that tiles x splits fills at most all slots.
+// Measured on 4096 x 16384 (N x K) layers: 65 tokens 99 -> 50 us, 512 tokens
+// 105 -> 78 us; 8192 x 28672 at 65 tokens 190 -> 80 us.  Layers with K = 4096
+// lose (the partial sums cost more than the idle CUs), so they are not split.
+int splitk_splits(int64_t M, int64_t N, int64_t K) {
+    if (M <= 64 || N % 4 != 0 || K % 128 != 0 || K < 8192) return 1;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t slots = 2 * (int64_t)cu_count();
+    if (tiles > kSplitkCounters || 4 * tiles > slots) return 1;
+    int S = 1;
+    while (S < 8 && tiles * (2 * S) <= slots && K % (2 * S * 128) == 0 && K / (2 * S) >= 1024) S *= 2;
+    return S;
+}
+
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int S = splitk_splits(M, N, K);
+    if (S == 1) return 0;
+    return 4 * (int64_t)kSplitkCounters + (4 * S * M * N + 255) / 256 * 256;
+}
+
+namespace {
+template <Out O, bool PACKED>
+hipError_t splitk_out(const int8_t* xq, const float* sx, const int8_t* w, const float* sw, int M,
+                      int N, int K, void* y, int S, int32_t* ws, hipStream_t s) {
+    Epi epi;
+    epi.ws = ws;
+    epi.splits = S;
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2, false, false, true>),
+                       dim3(tiles, S), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_splitk(const int8_t* xq, const float* x_scale, const int8_t* w,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                              Out out, bool packed, int32_t* ws, hipStream_t s) {
+    const int S = splitk_splits(M, N, K);
+    if (S == 1)
+        return packed ? launch_gemm_packed(xq, x_scale, w, w_scale, M, N, K, y, out, s)
+                      : launch_gemm(xq, x_scale, w, w_scale, M, N, K, y, out, s);
+    const int m = (int)M, n = (int)N, k = (int)K;
+#define SQ_SK(O) return packed ? splitk_out<O, true>(xq, x_scale, w, w_scale, m, n, k, y, S, ws, s) \
+                               : splitk_out<O, false>(xq, x_scale, w, w_scale, m, n, k, y, S, ws, s)
+    switch (out) {
+        case Out::F16: SQ_SK(Out::F16);
+        case Out::BF16: SQ_SK(Out::BF16);
+        case Out::F32: SQ_SK(Out::F32);
+        default: break;
+    }
+#undef SQ_SK
     return hipErrorInvalidValue;
 }
 

@@ -7,6 +7,10 @@
 
 namespace sq {
 
+// Tile counters at the start of a split-K workspace (the split form is taken
+// only while the output has at most this many tiles).
+constexpr int kSplitkCounters = 4096;
+
 // Entry blockIdx.y of a batched product whose operands, scales and outputs
 // lie back to back (entry z: A + z*M*K, B + z*b_stride, sx + z*M, sw + z*N,
 // Y + z*M*N elements).  Entry 0 is the unbatched call.

@@ -17,6 +17,10 @@ struct Epi {
     const float* bias = nullptr;  // fp32 [N] or null
     int relu = 0;
     bool on() const { return bias != nullptr || relu != 0; }
+    // split-K launches only: int32 workspace (splits slices of [M x N], then
+    // one counter per output tile) and the number of splits of K
+    int32_t* ws = nullptr;
+    int splits = 1;
 };
 
 hipError_t launch_colmax(const void* x, Dt dt, int64_t R, int64_t C, float* out, bool zero_first,
@@ -59,6 +63,17 @@ hipError_t launch_pack_weight(const int8_t* wq, int64_t N, int64_t K, int8_t* wp
 hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8_t* wp,
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                               Out out, hipStream_t s, Epi epi = Epi());
+
+// Split-K form of the GEMM with scale back (packed or row-major weights) for
+// shapes whose output tiles alone would leave most CUs idle.  splitk_splits
+// gives the number of splits the library takes for a shape (1: none; the
+// call then runs the plain GEMM), splitk_workspace_bytes the workspace it
+// needs (0 when there is no split).
+int splitk_splits(int64_t M, int64_t N, int64_t K);
+int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_splitk(const int8_t* xq, const float* x_scale, const int8_t* w,
+                              const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
+                              Out out, bool packed, int32_t* ws, hipStream_t s);
 
 // Few-token GEMM (M <= 64): row-major or fragment-packed weights.
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
