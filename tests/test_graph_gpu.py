@@ -4,9 +4,10 @@ One graph records the whole run-time path: the per-token quantiser and the
 packed GEMM of a prefill layer, the one-call decode layer (2 tokens), the
 quantiser and the 4-block packed GEMM at 16 tokens, the fused LayerNorm +
 quantisation, the dynamic per-tensor quantiser (partial maxima, reduction,
-codes), both attention products (the one-stage K = 128 product and P V) and
+codes), both attention products (the one-stage K = 128 product and P V),
 both forms of the batched per-channel quantiser (the one-pass kernel, and
-zero fill + atomic column maxima + transposing quantiser).  The graph is
+zero fill + atomic column maxima + transposing quantiser) and the split-K
+GEMM (its tile counters reset by the last split of each tile).  The graph is
 replayed four times, each time on new inputs copied into its buffers, with
 eager calls and synchronisations in between; every replay must give, bit for
 bit, what the same calls give eagerly on the same inputs.  The library
@@ -58,6 +59,15 @@ def test_graph_replay_matches_eager(dev):
         "v": torch.empty(H, S, 64, dtype=f16, device=dev),
         "v_odd": torch.empty(3, 100, 40, dtype=f16, device=dev),
     }
+    # a deep, narrow layer at 128 tokens: the split-K form (8 splits), whose
+    # tile counters must be back at zero for every replay
+    Ks, Ns, Ms = 8192, 1024, 128
+    wsk = sq.pack_weight(_i8(11, Ns, Ks).to(dev))
+    sx_sk = torch.from_numpy(np.random.default_rng(12).uniform(1e-3, 2e-2, Ms).astype(np.float32)).to(dev)
+    sw_sk = torch.from_numpy(np.random.default_rng(13).uniform(1e-4, 1e-3, Ns).astype(np.float32)).to(dev)
+    assert sq.sq_gemm_workspace_bytes(Ms, Ns, Ks) > 0
+    workspace = sq.gemm_workspace(Ms, Ns, Ks, dev)
+    ins["xsk"] = torch.empty(Ms, Ks, dtype=torch.int8, device=dev)
     sxa = torch.from_numpy(np.random.default_rng(8).uniform(1e-3, 2e-2, (H, S)).astype(np.float32)).to(dev)
     vq_scores = torch.from_numpy(np.random.default_rng(9).uniform(1e-3, 2e-2, (H, D)).astype(np.float32)).to(dev)
     vq_pv = _i8(10, H, D, S).to(dev)
@@ -84,6 +94,7 @@ def test_graph_replay_matches_eager(dev):
             "vs": torch.empty(H, 64, dtype=torch.float32, device=dev),
             "vq_odd": torch.empty(3, 40, 100, dtype=torch.int8, device=dev),
             "vs_odd": torch.empty(3, 40, dtype=torch.float32, device=dev),
+            "ysk": torch.empty(Ms, Ns, dtype=f16, device=dev),
         }
 
     def run(o):
@@ -98,12 +109,13 @@ def test_graph_replay_matches_eager(dev):
         sq.sq_w8a8_bmm_dequant(ins["pq"], sxa, vq_pv, vq_scores, o["o"])
         sq.sq_quant_weight_perchannel_batched(ins["v"], o["vq"], o["vs"])
         sq.sq_quant_weight_perchannel_batched(ins["v_odd"], o["vq_odd"], o["vs_odd"])
+        sq.sq_w8a8_gemm_dequant_packed_ws(ins["xsk"], sx_sk, wsk, sw_sk, Ns, o["ysk"], workspace)
 
     def refill(seed):
         r = np.random.default_rng([55, seed])
         for name, t in ins.items():
             if t.dtype == torch.int8:
-                t.copy_(_i8(seed * 31 + len(name), *t.shape))
+                t.copy_(_i8(seed * 997 + sum(map(ord, name)), *t.shape))
             else:
                 z = r.standard_normal(tuple(t.shape), dtype=np.float32)
                 if name in ("x", "x2", "x16"):
@@ -139,6 +151,7 @@ def test_graph_replay_matches_eager(dev):
             elif a.dtype == torch.float32:
                 a, b = a.view(torch.int32), b.view(torch.int32)
             assert torch.equal(a, b), "replay %d: %s differs from the eager call" % (rep, k)
+        assert int(workspace[:4 * 4096].count_nonzero()) == 0, "split-K tile counters not reset"
         # each replay computed from its own inputs, not the previous ones
         if prev is not None:
             assert not torch.equal(snap["y"], prev["y"]) and not torch.equal(snap["vq"], prev["vq"])
