@@ -128,9 +128,15 @@ class Bufs:
         self.packed = packed
         self.mode = mode
         self.steps = []
+        # split-K entry point ("ws"): one zero-filled workspace per set, the
+        # size of its largest layer's need (the calls run one after another)
+        self.ws = None
+        if mode == "ws":
+            need = max(sq.sq_gemm_workspace_bytes(M, ly.N, ly.K) for ly in layers)
+            self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
         for ly in layers:
             x_hat = ly.x_hat[:M].clone()
-            if mode == "o1":
+            if mode in ("o1", "ws"):
                 w = (ly.wp if packed else ly.wq).clone()
                 sw = ly.sw.clone()
             else:  # per-tensor weights
@@ -155,6 +161,9 @@ class Bufs:
             elif self.mode == "o2":
                 sq.sq_quant_act_pertensor(x_hat, xq, sx)
                 self._gemm(xq, sx, w, sw, y, N)
+            elif self.mode == "ws":
+                sq.sq_quant_act_pertoken(x_hat, xq, sx)
+                sq.sq_w8a8_gemm_dequant_packed_ws(xq, sx, w, sw, N, y, self.ws)
             elif self.packed:  # one call per layer; one kernel for few tokens
                 sq.sq_w8a8_linear_packed(x_hat, w, sw, xq, sx, y)
             else:
@@ -481,6 +490,27 @@ def main():
                       "gbs": round(quant_bytes / quant_ms / 1e6, 1),
                       "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
     }
+    # ---- the same layers at 512 tokens (the configuration's smaller prefill):
+    # the plain packed path, and the split-K entry point, which splits K for
+    # the deep, narrow FC2 (its 128 output tiles would leave most CUs idle)
+    M5 = 512
+    ops5 = sum(2.0 * M5 * ly.N * ly.K for ly in layers)
+    p512 = {"tokens": M5,
+            "split_layers": [ly.name for ly in layers
+                             if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0]}
+    for mode in ("o1", "ws"):
+        sets = [Bufs(layers, M5, dev, True, mode) for _ in range(2)]
+        ms5 = time_rotation([b.step for b in sets], args.steps, args.warmup)
+        p512["split_k" if mode == "ws" else "plain"] = {
+            "ms_per_step": round(ms5, 4), "tops": round(ops5 / ms5 / 1e9, 1)}
+        log("prefill at %d tokens (%s): step %.3f ms, %.1f TOPS"
+            % (M5, "split-K entry point" if mode == "ws" else "plain", ms5, ops5 / ms5 / 1e9))
+        del sets
+        torch.cuda.synchronize()
+    p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
+                    "split_k: sq_w8a8_gemm_dequant_packed_ws")
+    out["prefill_512"] = p512
+
     # ---- the LayerNorm in front of QKV and FC1 (it carries the folded
     # smoothing) fused with the per-token quantisation: reads the residual
     # stream once and writes only codes and steps
