@@ -399,6 +399,8 @@ def main():
     ap.add_argument("--no-offline", action="store_true")
     ap.add_argument("--no-levels", action="store_true", help="skip the O2/O3 measurements")
     ap.add_argument("--no-attention", action="store_true", help="skip the INT8 attention products")
+    ap.add_argument("--no-prefill-512", action="store_true",
+                    help="skip the 512-token prefill (plain and split-K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -498,7 +500,7 @@ def main():
     p512 = {"tokens": M5,
             "split_layers": [ly.name for ly in layers
                              if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0]}
-    for mode in ("o1", "ws"):
+    for mode in (() if args.no_prefill_512 else ("o1", "ws")):
         sets = [Bufs(layers, M5, dev, True, mode) for _ in range(2)]
         ms5 = time_rotation([b.step for b in sets], args.steps, args.warmup)
         p512["split_k" if mode == "ws" else "plain"] = {
@@ -509,7 +511,8 @@ def main():
         torch.cuda.synchronize()
     p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
                     "split_k: sq_w8a8_gemm_dequant_packed_ws")
-    out["prefill_512"] = p512
+    if not args.no_prefill_512:
+        out["prefill_512"] = p512
 
     # ---- the LayerNorm in front of QKV and FC1 (it carries the folded
     # smoothing) fused with the per-token quantisation: reads the residual
