@@ -164,6 +164,8 @@ GEMM_SHAPES = [
     (2048, 12288, 256), (1999, 4100, 384),                       # 256 x 192 DMA tiles
     (2047, 16380, 640),                                          # 256 x 256 DMA tiles
     (300, 130, 128), (2000, 12300, 128), (65, 64, 128),          # K = 128: one operand stage
+    (100, 4100, 4096), (128, 1000, 384), (65, 63, 16384),        # <= 128 rows: 128 x 64 tiles, BK 64
+    (200, 1000, 2048), (256, 4100, 640), (129, 64, 256),         # <= 256 rows: 128 x 64 tiles, BK 128
 ]
 
 
