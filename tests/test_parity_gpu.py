@@ -166,6 +166,8 @@ GEMM_SHAPES = [
     (300, 130, 128), (2000, 12300, 128), (65, 64, 128),          # K = 128: one operand stage
     (100, 4100, 4096), (128, 1000, 384), (65, 63, 16384),        # <= 128 rows: 128 x 64 tiles, BK 64
     (200, 1000, 2048), (256, 4100, 640), (129, 64, 256),         # <= 256 rows: 128 x 64 tiles, BK 128
+    (40, 12288, 256), (33, 16384, 384), (64, 12300, 128),        # 17-64 rows on wide layers: tiles
+    (32, 12288, 512), (17, 28672, 256), (31, 12288, 256),        # the edge of that rule (31: few-token)
 ]
 
 

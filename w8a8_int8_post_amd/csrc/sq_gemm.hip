@@ -13,7 +13,7 @@
 // matrix cores: every lane's 16-byte fragment is one contiguous load.
 //
 // Kernels, chosen by the shape (M <= 64 tokens go to the few-token kernels of
-// sq_decode.hip):
+// sq_decode.hip, except 17-64 tokens on layers at least 12288 channels wide):
 //  * dma (M > 64, K % 128 == 0): workgroup tile BM x BN; 128-byte K slices go
 //    from global memory straight into LDS (global_load_lds_dwordx4, no
 //    register staging), double-buffered, as XOR-swizzled 16-byte chunks
@@ -688,18 +688,30 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const int8_t* __restri
     }
 }
 
+// 17-64 tokens: the few-token kernels read every activation fragment once per
+// 16-channel block, so on wide layers (N >= 12288) the activation traffic
+// outgrows the weights; there the 128 x 64 tiles win from about M * N >=
+// 32 x 12288 (measured: 12288 x 4096 at 32 tokens 20.1 -> 18.5 us, at 64
+// tokens 32.7 -> 18.5 us; 16384 x 4096 at 64 tokens 42.7 -> 23.0 us; 28672 x
+// 8192 at 32 tokens 76.4 -> 56.1 us; narrow, deep layers such as 4096 x 16384
+// keep the few-token kernels at every M <= 64).
+bool few_tokens_to_tiles(int M, int N) {
+    return M > 16 && N >= 12288 && (int64_t)M * N >= 32 * 12288;
+}
+
 template <Out O, bool EXT>
 hipError_t gemm_packed_dispatch(const int8_t* xq, const float* sx, const int8_t* wp,
                                 const float* sw, int M, int N, int K, void* y, Epi epi,
                                 hipStream_t s) {
-    if (M <= 64) return launch_skinny(xq, sx, wp, sw, M, N, K, y, O, true, s, epi);
+    if (M <= 64 && !few_tokens_to_tiles(M, N))
+        return launch_skinny(xq, sx, wp, sw, M, N, K, y, O, true, s, epi);
     return launch_dma<O, true, EXT>(xq, sx, wp, sw, M, N, K, y, epi, s);
 }
 
 template <Out O, bool KVEC, bool EXT>
 hipError_t gemm_dispatch(const int8_t* xq, const float* sx, const int8_t* wq, const float* sw,
                          int M, int N, int K, void* y, Epi epi, hipStream_t s, int batch) {
-    if (M <= 64) {
+    if (M <= 64 && !(KVEC && K % 128 == 0 && few_tokens_to_tiles(M, N))) {
         return launch_skinny(xq, sx, wq, sw, M, N, K, y, O, false, s, epi, batch);
     } else if (KVEC && K % 128 == 0) {
         return launch_dma<O, false, EXT>(xq, sx, wq, sw, M, N, K, y, epi, s, batch);
