@@ -12,7 +12,9 @@ alpha = 0.5, all resident in HBM before timing starts.
 
 The same layers at 1 and 16 tokens (decode) are timed as well and reported
 under "decode" in GB/s.  Buffer sets rotate so that weights are streamed from
-HBM rather than served by the 256 MB Infinity Cache.
+HBM rather than served by the 256 MB Infinity Cache.  The OPT-13B-like
+(4096 tokens, fp16) and OPT-175B-like (2048 and 8192 tokens, bf16) layer sets
+are timed the same way and reported under "larger_prefill".
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: the benchmark measures
 one GPU (one GPU's share of a layer at its real shape).
@@ -354,6 +356,80 @@ def decode_llama70b(dev, args):
     return res
 
 
+LARGER = ((3, (4096,)), (4, (2048, 8192)))  # OPT-13B-like, OPT-175B-like (config, tokens)
+
+
+def larger_prefill(dev, args):
+    """Prefill steps of the larger layer sets: OPT-13B-like (fp16, 4096 tokens)
+    and OPT-175B-like (bf16, 2048 and 8192 tokens).  Each layer goes through
+    the offline path (calibration on 512 tokens, smoothing and fold, per-channel
+    weight quantisation, packing); a step is, per layer, the per-token
+    quantiser and the packed GEMM with the scale back, output in the layer's
+    dtype.  Two buffer sets, weights included, alternate (each step moves far
+    more than the 256 MB last-level cache)."""
+    res = {}
+    for cid, Ms in LARGER:
+        cfg = synth.CONFIGS[cid]
+        ydt = synth.DTYPES[cfg.ydt]
+        prep = []
+        for ly in cfg.layers:
+            w = synth.weight(cfg, ly.name).to(dev)
+            xc = synth.activations(cfg, ly.name, cfg.T, calibration=True).to(dev)
+            s, w_hat = sq.smooth_fold(sq.calibrate_absmax(xc), w, ALPHA)
+            del w, xc
+            wq, sw = sq.quant_weight_perchannel(w_hat)
+            del w_hat
+            wp = sq.pack_weight(wq)
+            del wq
+            x = synth.activations(cfg, ly.name, max(Ms)).to(dev)
+            prep.append((ly, wp, sw, sq.smooth_activation(x, s)))
+            del x
+            torch.cuda.synchronize()
+        ent = {"layers": [[ly.name, ly.K, ly.N] for ly in cfg.layers], "dtype": cfg.act}
+        for M in Ms:
+            ops = sum(2.0 * M * ly.N * ly.K for ly in cfg.layers)
+            sets = []
+            for _ in range(2):
+                sets.append([(x_hat[:M].clone(), wp.clone(), sw.clone(),
+                              torch.empty(M, ly.K, dtype=torch.int8, device=dev),
+                              torch.empty(M, dtype=torch.float32, device=dev),
+                              torch.empty(M, ly.N, dtype=ydt, device=dev), ly.N)
+                             for (ly, wp, sw, x_hat) in prep])
+
+            def step(bs):
+                for (x_hat, wp, sw, xq, sx, y, N) in bs:
+                    sq.sq_quant_act_pertoken(x_hat, xq, sx)
+                    sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y)
+
+            def gemm(bs, i):
+                x_hat, wp, sw, xq, sx, y, N = bs[i]
+                sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y)
+
+            iters = max(4, args.steps // 4)
+            ms = time_rotation([lambda bs=bs: step(bs) for bs in sets], iters, 2)
+            per_layer = {}
+            for i, (ly, _, _, _) in enumerate(prep):
+                ms_g = time_rotation([lambda bs=bs, i=i: gemm(bs, i) for bs in sets], iters, 2)
+                tops_g = 2.0 * M * ly.N * ly.K / ms_g / 1e9
+                per_layer[ly.name] = {"gemm_us": round(ms_g * 1e3, 1), "gemm_tops": round(tops_g, 1),
+                                      "frac_of_int8_peak": round(tops_g / PEAK_I8_TOPS, 4)}
+            tops = ops / ms / 1e9
+            ent["M=%d" % M] = {"ms_per_step": round(ms, 4), "tops": round(tops, 1),
+                               "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
+                               "layers": per_layer}
+            log("%s prefill at %d tokens: step %.3f ms, %.1f TOPS (%.1f%% of peak); gemm %s"
+                % (cfg.name, M, ms, tops, 100 * tops / PEAK_I8_TOPS,
+                   ", ".join("%s %.1f us" % (k, v["gemm_us"]) for k, v in per_layer.items())))
+            del sets
+            torch.cuda.synchronize()
+        res[cfg.name] = ent
+        del prep
+        torch.cuda.synchronize()
+    res["step"] = ("per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant_packed, output in the "
+                   "layer dtype; gemm: the packed GEMM alone")
+    return res
+
+
 def n_sets(footprint_bytes):
     return max(2, math.ceil((1 << 30) / footprint_bytes))
 
@@ -401,6 +477,8 @@ def main():
     ap.add_argument("--no-attention", action="store_true", help="skip the INT8 attention products")
     ap.add_argument("--no-prefill-512", action="store_true",
                     help="skip the 512-token prefill (plain and split-K)")
+    ap.add_argument("--no-larger", action="store_true",
+                    help="skip the OPT-13B-like and OPT-175B-like prefill layers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -553,6 +631,10 @@ def main():
     # token, P V with P per row and V per head-dim channel; codes resident
     if not args.no_attention:
         out["attention"] = attention_time(dev, args)
+
+    # ---- the larger prefill layer sets (OPT-13B-like, OPT-175B-like)
+    if not args.no_larger:
+        out["larger_prefill"] = larger_prefill(dev, args)
 
     # ---- decode shapes
     if not args.no_decode:
