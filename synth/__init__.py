@@ -143,3 +143,26 @@ def random_int8(seed: int, rows: int, cols: int) -> np.ndarray:
     """Uniform int8 codes in [-127, 127] (the quantiser's code range)."""
     return np.random.default_rng([98, seed]).integers(-127, 128, size=(rows, cols),
                                                       dtype=np.int16).astype(np.int8)
+
+
+def device_matrix(seed: int, rows: int, cols: int, dt: str, device, scale: float = 1.0,
+                  outlier_cols=None, factor: float = 1.0) -> torch.Tensor:
+    """Seeded N(0, scale) matrix drawn on the device (torch's generator), for
+    tensors too large to draw on the host in a test's time; the values a test
+    checks are copied back, so both sides still see identical bits."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    z = torch.randn(rows, cols, generator=g, device=device, dtype=DTYPES[dt])
+    if scale != 1.0:
+        z.mul_(scale)
+    if outlier_cols is not None and len(outlier_cols):
+        idx = torch.as_tensor(np.asarray(outlier_cols, dtype=np.int64), device=device)
+        z[:, idx] *= factor
+    return z
+
+
+def device_int8(seed: int, rows: int, cols: int, device) -> torch.Tensor:
+    """Seeded uniform int8 codes in [-127, 127] drawn on the device."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randint(-127, 128, (rows, cols), generator=g, device=device, dtype=torch.int8)
