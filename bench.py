@@ -571,8 +571,8 @@ def main():
                       "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
     }
     # ---- the same layers at 512 tokens (the configuration's smaller prefill):
-    # the plain packed path, and the split-K entry point, which splits K for
-    # the deep, narrow FC2 (its 128 output tiles would leave most CUs idle)
+    # the plain packed path, and the split-K entry point (which splits K only
+    # where that beats the plain kernels; "split_layers" names those layers)
     M5 = 512
     ops5 = sum(2.0 * M5 * ly.N * ly.K for ly in layers)
     p512 = {"tokens": M5,

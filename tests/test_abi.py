@@ -165,18 +165,21 @@ def test_splitk_workspace_query_and_validation(lib):
     # no split for few tokens (the few-token kernels) or a wide layer at many tokens
     assert sq.sq_gemm_workspace_bytes(16, 4096, 16384) == 0
     assert sq.sq_gemm_workspace_bytes(4096, 16384, 4096) == 0
-    # 512 tokens through a 16384 x 4096 layer: K split, int32 slices plus counters
-    need = sq.sq_gemm_workspace_bytes(512, 4096, 16384)
-    assert need >= 2 * 4 * 512 * 4096 and need % 256 == 0
+    # 128 tokens through a 16384 x 4096 layer: K split, int32 slices plus counters;
+    # 512 tokens: the plain kernel keeps up there, no split
+    need = sq.sq_gemm_workspace_bytes(128, 4096, 16384)
+    assert need >= 2 * 4 * 128 * 4096 and need % 256 == 0
+    assert sq.sq_gemm_workspace_bytes(512, 4096, 16384) == 0
+    assert sq.sq_gemm_workspace_bytes(512, 4096, 28672) > 0
     assert lib.sq_gemm_workspace_bytes(0, 4, 4) == -1
     B = 1 << 32  # fake, far-apart, aligned addresses: validation never dereferences
-    args = (B, 2 * B, 3 * B, 4 * B, 512, 4096, 16384, 5 * B, 1)
+    args = (B, 2 * B, 3 * B, 4 * B, 128, 4096, 16384, 5 * B, 1)
     f = lib.sq_w8a8_gemm_dequant_packed_ws
     assert f(*args, None, need, None) == 11           # workspace needed, none given
     assert f(*args, 6 * B + 8, need, None) == 11      # misaligned
     assert f(*args, 6 * B, need - 16, None) == 11     # too small
     assert f(*args, 5 * B + 4096, need, None) == 8    # overlaps y
-    assert f(B, 2 * B, 3 * B, 4 * B, 512, 4096, 16064, 5 * B, 1, 6 * B, need, None) == 2
+    assert f(B, 2 * B, 3 * B, 4 * B, 128, 4096, 16064, 5 * B, 1, 6 * B, need, None) == 2
     g = lib.sq_w8a8_gemm_dequant_ws
     assert g(*args, None, need, None) == 11
     assert g(None, *args[1:], 6 * B, need, None) == 1

@@ -168,6 +168,7 @@ GEMM_SHAPES = [
     (200, 1000, 2048), (256, 4100, 640), (129, 64, 256),         # <= 256 rows: 128 x 64 tiles, BK 128
     (40, 12288, 256), (33, 16384, 384), (64, 12300, 128),        # 17-64 rows on wide layers: tiles
     (32, 12288, 512), (17, 28672, 256), (31, 12288, 256),        # the edge of that rule (31: few-token)
+    (70, 200, 16384), (130, 260, 16384),                         # deep: 64-deep k-tiles, four stages
 ]
 
 

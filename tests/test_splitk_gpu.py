@@ -38,7 +38,9 @@ CASES = [
     (65, 4096, 16384, "f16"),     # 32 tiles: 8 splits
     (128, 1000, 8192, "bf16"),    # 8 tiles: 8 splits of 1024
     (300, 4100, 8192, "f32"),     # ragged M and N tiles: 4 splits
-    (512, 4096, 16384, "f16"),    # 128 tiles: 4 splits
+    (512, 4096, 16384, "f16"),    # > 128 tokens, K < 24576: no split (the plain kernel)
+    (128, 4096, 16384, "bf16"),   # 32 tiles: 8 splits
+    (512, 4096, 28672, "f16"),    # 128 tiles, K = 28672: 4 splits
     (100, 8192, 28672, "bf16"),   # 64 tiles: 8 splits
     (129, 2048, 9216, "f16"),     # 32 tiles; K = 72 x 128: 8 splits of 1152
     (1000, 4096, 8192, "f16"),    # 256 tiles: no split
@@ -46,6 +48,12 @@ CASES = [
     (2048, 4096, 16384, "f16"),   # 512 tiles: no split (the plain GEMM)
     (16, 4096, 16384, "f16"),     # few tokens: no split
     (200, 1002, 16384, "f16"),    # N % 4 != 0: no split
+    # the plain entry points on deep layers: 128 x 64 tiles (at most one per
+    # CU) or 128 x 128 tiles, 64-deep k-tiles in a four-stage ring
+    (129, 8320, 16384, "f16"),    # 260 narrow tiles, 130 wide: the 128 x 128 form
+    (700, 4096, 16384, "bf16"),   # 192 wide tiles: the 128 x 128 form
+    (300, 5120, 20480, "f16"),    # 240 narrow tiles
+    (65, 12288, 49152, "bf16"),   # 192 narrow tiles, K = 49152
 ]
 
 
@@ -101,7 +109,7 @@ def test_splitk_gemm_dequant(ref, dev, workspace, M, N, K, ydt, packed):
 
 
 def test_splitk_workspace_errors(dev):
-    M, N, K = 512, 4096, 16384
+    M, N, K = 128, 4096, 16384
     xq = torch.zeros(M, K, dtype=torch.int8, device=dev)
     wp = sq.pack_weight(torch.zeros(N, K, dtype=torch.int8, device=dev))
     sx = torch.ones(M, device=dev)

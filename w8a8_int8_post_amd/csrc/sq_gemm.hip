@@ -630,6 +630,31 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                            epi);
         return hipGetLastError();
     }
+    if (K >= 16384) {
+        // Deep layers whose tiles number at most one per CU: each workgroup
+        // runs a long K loop bound by the latency of its operand loads, so
+        // 64-deep k-tiles go in a four-stage ring (more bytes in flight per
+        // workgroup); 128 x 64 tiles while they are few enough, else 128 x
+        // 128.  Measured (packed weights): 4096 x 16384 at 65 tokens 82.5 ->
+        // 62.1 us, at 200 tokens 95.0 -> 62.4, at 768 tokens 106 -> 85;
+        // 8192 x 28672 at 65 tokens 147 -> 109 us, at 384 tokens 190 -> 152;
+        // 12288 x 49152 at 65 tokens 260 -> 198 us, at 200 tokens 299 -> 253.
+        // With more tiles than CUs the deeper ring loses (8192 x 28672 at 768
+        // tokens 233 -> 274 us).
+        const int64_t cus = cu_count();
+        if ((int64_t)tiles(128, 64) * batch <= cus) {
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 3, 4, EXT>),
+                               dim3(tiles(128, 64), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N,
+                               K, epi);
+            return hipGetLastError();
+        }
+        if ((int64_t)tiles(128, 128) * batch <= cus) {
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, 64, O, PACKED, 2, 4, EXT>),
+                               dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N,
+                               K, epi);
+            return hipGetLastError();
+        }
+    }
     if (M <= 256) {
         // Few token rows: 128-row tiles leave most CUs idle on all but the
         // widest layers, so the tiles are narrower (128 x 64, four per CU).
@@ -769,11 +794,16 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
 // most a quarter of the slots (few tokens against a narrow layer: 512 x 4096
 // x 16384 has 128 tiles for 512 slots), in 2, 4 or 8 ranges of at least 1024
 // (a multiple of 128) so that tiles x splits fills at most all slots.
-// Measured on 4096 x 16384 (N x K) layers: 65 tokens 99 -> 50 us, 512 tokens
-// 105 -> 78 us; 8192 x 28672 at 65 tokens 190 -> 80 us.  Layers with K = 4096
-// lose (the partial sums cost more than the idle CUs), so they are not split.
+// Measured against the plain entry point (packed weights): 4096 x 16384 (N x
+// K) at 65 tokens 61 -> 50 us, 128 tokens 66 -> 52 us; 8192 x 28672 at 65
+// tokens 109 -> 80 us, at 256 tokens 126 -> 104 us; 12288 x 49152 at 65
+// tokens 192 -> 151 us.  Layers with K = 4096 lose (the partial sums cost
+// more than the idle CUs), and so do layers with 16384 <= K < 24576 above 128
+// tokens, where the plain kernel's four-stage ring keeps up (4096 x 16384 at
+// 512 tokens: split 73 us, plain 68 us); those are not split.
 int splitk_splits(int64_t M, int64_t N, int64_t K) {
     if (M <= 64 || N % 4 != 0 || K % 128 != 0 || K < 8192) return 1;
+    if (M > 128 && K >= 16384 && K < 24576) return 1;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int64_t slots = 2 * (int64_t)cu_count();
     if (tiles > kSplitkCounters || 4 * tiles > slots) return 1;
