@@ -71,6 +71,7 @@ EX_SHAPES = [
     (512, 2048, 4096), (300, 130, 128),                              # 128 x 128 DMA tiles
     (2048, 12288, 256), (1999, 4100, 384),                           # 256 x 192 DMA tiles
     (2000, 12300, 128), (2047, 16380, 640),                          # 256 x 256
+    (100, 300, 16384), (40, 12288, 256),                             # deep four-stage; wide 17-64
 ]
 
 
@@ -90,7 +91,8 @@ def test_gemm_dequant_ex(ref, dev, M, N, K, ydt, mode):
 
 
 PACKED_EX_SHAPES = [(1, 4096, 16384), (16, 300, 128), (33, 200, 1280), (64, 1000, 2048),
-                    (300, 130, 128), (512, 2048, 4096), (2048, 12288, 256), (2000, 12300, 128)]
+                    (300, 130, 128), (512, 2048, 4096), (2048, 12288, 256), (2000, 12300, 128),
+                    (40, 12288, 256), (100, 300, 16384), (129, 8320, 16384)]  # wide 17-64; deep
 
 
 @pytest.mark.parametrize("M,N,K", PACKED_EX_SHAPES)
