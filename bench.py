@@ -356,6 +356,28 @@ def decode_llama70b(dev, args):
     return res
 
 
+def prefill_512(layers, dev, args, M5=512):
+    """The OPT-6.7B-like layers at 512 tokens: the plain packed path and the
+    split-K entry point (which splits K only where that beats the plain
+    kernels; "split_layers" names those layers)."""
+    ops5 = sum(2.0 * M5 * ly.N * ly.K for ly in layers)
+    p512 = {"tokens": M5,
+            "split_layers": [ly.name for ly in layers
+                             if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0]}
+    for mode in ("o1", "ws"):
+        sets = [Bufs(layers, M5, dev, True, mode) for _ in range(2)]
+        ms5 = time_rotation([b.step for b in sets], args.steps, args.warmup)
+        p512["split_k" if mode == "ws" else "plain"] = {
+            "ms_per_step": round(ms5, 4), "tops": round(ops5 / ms5 / 1e9, 1)}
+        log("prefill at %d tokens (%s): step %.3f ms, %.1f TOPS"
+            % (M5, "split-K entry point" if mode == "ws" else "plain", ms5, ops5 / ms5 / 1e9))
+        del sets
+        torch.cuda.synchronize()
+    p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
+                    "split_k: sq_w8a8_gemm_dequant_packed_ws")
+    return p512
+
+
 LARGER = ((3, (4096,)), (4, (2048, 8192)))  # OPT-13B-like, OPT-175B-like (config, tokens)
 
 
@@ -479,6 +501,8 @@ def main():
                     help="skip the 512-token prefill (plain and split-K)")
     ap.add_argument("--no-larger", action="store_true",
                     help="skip the OPT-13B-like and OPT-175B-like prefill layers")
+    ap.add_argument("--prefill-512-only", action="store_true",
+                    help="only the 512-token prefill (prints {\"prefill_512\": ...}; for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -503,6 +527,9 @@ def main():
 
     log("setting up layers", [(ly.name, ly.K, ly.N) for ly in CFG.layers])
     layers = [Layer(ly.name, dev) for ly in CFG.layers]
+    if args.prefill_512_only:
+        print(json.dumps({"prefill_512": prefill_512(layers, dev, args)}), flush=True)
+        return
 
     # ---- prefill: the headline step, with row-major and with packed weights
     M = PREFILL_M
@@ -570,27 +597,9 @@ def main():
                       "gbs": round(quant_bytes / quant_ms / 1e6, 1),
                       "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
     }
-    # ---- the same layers at 512 tokens (the configuration's smaller prefill):
-    # the plain packed path, and the split-K entry point (which splits K only
-    # where that beats the plain kernels; "split_layers" names those layers)
-    M5 = 512
-    ops5 = sum(2.0 * M5 * ly.N * ly.K for ly in layers)
-    p512 = {"tokens": M5,
-            "split_layers": [ly.name for ly in layers
-                             if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0]}
-    for mode in (() if args.no_prefill_512 else ("o1", "ws")):
-        sets = [Bufs(layers, M5, dev, True, mode) for _ in range(2)]
-        ms5 = time_rotation([b.step for b in sets], args.steps, args.warmup)
-        p512["split_k" if mode == "ws" else "plain"] = {
-            "ms_per_step": round(ms5, 4), "tops": round(ops5 / ms5 / 1e9, 1)}
-        log("prefill at %d tokens (%s): step %.3f ms, %.1f TOPS"
-            % (M5, "split-K entry point" if mode == "ws" else "plain", ms5, ops5 / ms5 / 1e9))
-        del sets
-        torch.cuda.synchronize()
-    p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
-                    "split_k: sq_w8a8_gemm_dequant_packed_ws")
+    # ---- the same layers at 512 tokens (the configuration's smaller prefill)
     if not args.no_prefill_512:
-        out["prefill_512"] = p512
+        out["prefill_512"] = prefill_512(layers, dev, args)
 
     # ---- the LayerNorm in front of QKV and FC1 (it carries the folded
     # smoothing) fused with the per-token quantisation: reads the residual
