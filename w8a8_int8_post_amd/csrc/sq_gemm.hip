@@ -194,7 +194,12 @@ template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
-    constexpr int SWS = 1, GM = 8;
+    // XOR swizzle of the 16-byte chunks: chunk c of row r sits at c ^ ((r >>
+    // SWS) & (CPR - 1)).  A fragment read takes 16 consecutive rows, one chunk,
+    // in each 256-byte LDS cycle; with 128-byte rows the bank base repeats every
+    // 2 rows (shift 1), with 64-byte rows every 4 (shift 2), so that the 16 rows
+    // land on 16 distinct bank groups.
+    constexpr int SWS = BK == 64 ? 2 : 1, GM = 8;
     constexpr int KGT = BK / 64;  // packed k-groups per K tile
     static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
     constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NT = NW * 64;
