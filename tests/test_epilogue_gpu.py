@@ -71,7 +71,7 @@ EX_SHAPES = [
     (512, 2048, 4096), (300, 130, 128),                              # 128 x 128 DMA tiles
     (2048, 12288, 256), (1999, 4100, 384),                           # 256 x 192 DMA tiles
     (2000, 12300, 128), (2047, 16380, 640),                          # 256 x 256
-    (100, 300, 16384), (40, 12288, 256),                             # deep four-stage; wide 17-64
+    (100, 300, 16384), (40, 12288, 256),                             # few-tile four-stage; wide 17-64
 ]
 
 

@@ -635,17 +635,18 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                            epi);
         return hipGetLastError();
     }
-    if (K >= 16384) {
-        // Deep layers whose tiles number at most one per CU: each workgroup
-        // runs a long K loop bound by the latency of its operand loads, so
-        // 64-deep k-tiles go in a four-stage ring (more bytes in flight per
-        // workgroup); 128 x 64 tiles while they are few enough, else 128 x
-        // 128.  Measured (packed weights): 4096 x 16384 at 65 tokens 82.5 ->
-        // 62.1 us, at 200 tokens 95.0 -> 62.4, at 768 tokens 106 -> 85;
-        // 8192 x 28672 at 65 tokens 147 -> 109 us, at 384 tokens 190 -> 152;
-        // 12288 x 49152 at 65 tokens 260 -> 198 us, at 200 tokens 299 -> 253.
-        // With more tiles than CUs the deeper ring loses (8192 x 28672 at 768
-        // tokens 233 -> 274 us).
+    {
+        // Tiles numbering at most one per CU: each workgroup runs its whole K
+        // loop alone on its CU, bound by the latency of its operand loads, so
+        // 64-deep k-tiles go in a four-stage ring (twice the bytes in flight
+        // per workgroup); 128 x 64 tiles while they are few enough, else 128
+        // x 128.  Measured (packed weights, weights streamed from HBM):
+        // 12288 x 4096 at 65 tokens 23.7 -> 19.1 us, at 200 tokens 27.2 ->
+        // 24.0; 4096 x 8192 at 200 tokens 49.2 -> 33.8; 5120 x 5120 at 256
+        // tokens 32.7 -> 25.6; 4096 x 16384 at 65 tokens 82.5 -> 62.1, at 768
+        // tokens 106 -> 85; 8192 x 28672 at 384 tokens 190 -> 152; 12288 x
+        // 49152 at 200 tokens 299 -> 253.  With more tiles than CUs the
+        // deeper ring loses (8192 x 28672 at 768 tokens 233 -> 274 us).
         const int64_t cus = cu_count();
         if ((int64_t)tiles(128, 64) * batch <= cus) {
             hipLaunchKernelGGL((gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 3, 4, EXT>),
@@ -661,8 +662,9 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         }
     }
     if (M <= 256) {
-        // Few token rows: 128-row tiles leave most CUs idle on all but the
-        // widest layers, so the tiles are narrower (128 x 64, four per CU).
+        // Few token rows and more tiles than CUs: 128-row tiles still leave
+        // CUs idle on all but the widest layers, so the tiles are narrower
+        // (128 x 64, four per CU).
         // Up to 128 rows: 64-deep k-tiles in a three-stage ring (measured
         // 12288 x 4096 at 65 tokens 23.1 -> 18.3 us, 4096 x 16384 98 -> 77);
         // up to 256 rows: 128-deep, two stages (25.3 -> 22.7 us).
