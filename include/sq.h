@@ -299,9 +299,10 @@ sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int
 
 /* Split-K forms of sq_w8a8_gemm_dequant and sq_w8a8_gemm_dequant_packed
  * (identical results), for few tokens against a narrow, deep layer, where the
- * output tiles alone leave most compute units idle (e.g. 512 tokens through a
- * 16384 x 4096 layer; the split is taken for K >= 8192 when the 128 x 128
- * output tiles fill at most a quarter of the GPU's workgroup slots).  K is
+ * output tiles alone leave most compute units idle (e.g. 128 tokens through a
+ * 16384 x 4096 layer; the split is taken for K >= 12288 up to 128 tokens and
+ * for K >= 24576 above, when the 128 x 128 output tiles fill at most a
+ * quarter of the GPU's workgroup slots).  K is
  * split into 2, 4 or 8 ranges; each range's int32
  * partial products go to the workspace, and the scale back runs once the
  * ranges of an output tile are summed (integer sums, so the result does not

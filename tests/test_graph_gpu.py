@@ -61,7 +61,7 @@ def test_graph_replay_matches_eager(dev):
     }
     # a deep, narrow layer at 128 tokens: the split-K form (8 splits), whose
     # tile counters must be back at zero for every replay
-    Ks, Ns, Ms = 8192, 1024, 128
+    Ks, Ns, Ms = 16384, 1024, 128
     wsk = sq.pack_weight(_i8(11, Ns, Ks).to(dev))
     sx_sk = torch.from_numpy(np.random.default_rng(12).uniform(1e-3, 2e-2, Ms).astype(np.float32)).to(dev)
     sw_sk = torch.from_numpy(np.random.default_rng(13).uniform(1e-4, 1e-3, Ns).astype(np.float32)).to(dev)

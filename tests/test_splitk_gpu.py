@@ -36,15 +36,19 @@ def workspace(dev):
 
 CASES = [
     (65, 4096, 16384, "f16"),     # 32 tiles: 8 splits
-    (128, 1000, 8192, "bf16"),    # 8 tiles: 8 splits of 1024
-    (300, 4100, 8192, "f32"),     # ragged M and N tiles: 4 splits
+    (128, 1000, 8192, "bf16"),    # K < 12288: no split
+    (128, 1000, 12288, "bf16"),   # 8 tiles: 8 splits of 1536
+    (300, 4100, 8192, "f32"),     # K < 12288: no split
+    (100, 4100, 12288, "f32"),    # ragged M and N tiles: 8 splits
+    (300, 1000, 28672, "f32"),    # ragged M and N tiles above 128 tokens, K = 28672: 8 splits
     (512, 4096, 16384, "f16"),    # > 128 tokens, K < 24576: no split (the plain kernel)
     (128, 4096, 16384, "bf16"),   # 32 tiles: 8 splits
     (512, 4096, 28672, "f16"),    # 128 tiles, K = 28672: 4 splits
     (100, 8192, 28672, "bf16"),   # 64 tiles: 8 splits
-    (129, 2048, 9216, "f16"),     # 32 tiles; K = 72 x 128: 8 splits of 1152
+    (129, 2048, 9216, "f16"),     # K < 12288: no split
+    (120, 2048, 13824, "f16"),    # 16 tiles; K = 108 x 128: 4 splits of 3456
     (1000, 4096, 8192, "f16"),    # 256 tiles: no split
-    (100, 12288, 4096, "bf16"),   # K < 8192: no split
+    (100, 12288, 4096, "bf16"),   # K < 12288: no split
     (2048, 4096, 16384, "f16"),   # 512 tiles: no split (the plain GEMM)
     (16, 4096, 16384, "f16"),     # few tokens: no split
     (200, 1002, 16384, "f16"),    # N % 4 != 0: no split

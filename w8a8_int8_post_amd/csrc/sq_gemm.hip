@@ -797,20 +797,21 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
 // Split-K: 128 x 128 tiles, two workgroups per CU.  Workspace layout: a
 // fixed block of kSplitkCounters tile counters (only ever zero between
 // calls, whatever the shape), then the splits' int32 slices [S][M][N].
-// K is split only for deep layers (K >= 8192) whose output tiles fill at
-// most a quarter of the slots (few tokens against a narrow layer: 512 x 4096
-// x 16384 has 128 tiles for 512 slots), in 2, 4 or 8 ranges of at least 1024
+// K is split only for deep layers (K >= 12288) whose output tiles fill at
+// most a quarter of the slots (few tokens against a narrow layer: 128 x 4096
+// x 16384 has 32 tiles for 512 slots), in 2, 4 or 8 ranges of at least 1024
 // (a multiple of 128) so that tiles x splits fills at most all slots.
-// Measured against the plain entry point (packed weights): 4096 x 16384 (N x
-// K) at 65 tokens 61 -> 50 us, 128 tokens 66 -> 52 us; 8192 x 28672 at 65
-// tokens 109 -> 80 us, at 256 tokens 126 -> 104 us; 12288 x 49152 at 65
-// tokens 192 -> 151 us.  Layers with K = 4096 lose (the partial sums cost
-// more than the idle CUs), and so do layers with 16384 <= K < 24576 above 128
-// tokens, where the plain kernel's four-stage ring keeps up (4096 x 16384 at
-// 512 tokens: split 73 us, plain 68 us); those are not split.
+// Measured against the plain entry point (packed weights, its few-tile
+// forms): 4096 x 16384 (N x K) at 65 tokens 61 -> 50 us, 128 tokens 66 ->
+// 52 us; 4096 x 12288 at 128 tokens 55 -> 46 us; 8192 x 28672 at 65 tokens
+// 109 -> 80 us, at 256 tokens 126 -> 104 us; 12288 x 49152 at 65 tokens 192
+// -> 151 us.  Shallower layers lose (the partial sums cost more than the
+// plain kernel's idle time: 4096 x 8192 at 65 tokens 32 -> 40 us), and so do
+// layers with K < 24576 above 128 tokens (4096 x 16384 at 512 tokens: 68
+// plain, 73 split); those are not split.
 int splitk_splits(int64_t M, int64_t N, int64_t K) {
-    if (M <= 64 || N % 4 != 0 || K % 128 != 0 || K < 8192) return 1;
-    if (M > 128 && K >= 16384 && K < 24576) return 1;
+    if (M <= 64 || N % 4 != 0 || K % 128 != 0 || K < 12288) return 1;
+    if (M > 128 && K < 24576) return 1;
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int64_t slots = 2 * (int64_t)cu_count();
     if (tiles > kSplitkCounters || 4 * tiles > slots) return 1;
