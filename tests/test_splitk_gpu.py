@@ -58,6 +58,8 @@ CASES = [
     (700, 4096, 16384, "bf16"),   # 192 wide tiles: the 128 x 128 form
     (300, 5120, 20480, "f16"),    # 240 narrow tiles
     (65, 12288, 49152, "bf16"),   # 192 narrow tiles, K = 49152
+    (200, 28672, 8192, "f16"),    # 129-256 rows, wide and deep: 224 tiles of 256 x 128
+    (160, 36864, 12288, "bf16"),  # 129-256 rows: 144 tiles of 256 x 256
 ]
 
 

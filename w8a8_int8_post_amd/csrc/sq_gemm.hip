@@ -660,6 +660,27 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                                K, epi);
             return hipGetLastError();
         }
+        // 129-256 rows on wide, deep layers (K >= 8192, more 128-row tiles
+        // than CUs): one row of 256-row tiles, 256 x 128 or else 256 x 256,
+        // in the same four-stage ring.  Measured: 28672 x 8192 at 129 / 256
+        // tokens 113 / 124 -> 78 / 90 us; 49152 x 12288 213 / 245 -> 191 /
+        // 212 us; 36864 x 12288 176 -> 163 us.  Not for more rows or K = 4096
+        // (there it loses: 12288 x 4096 at 512 tokens 39 -> 43 us, 4096 x
+        // 16384 at 1024 tokens 94 -> 141 us).
+        if (K >= 8192 && M > 128 && M <= 256) {
+            if ((int64_t)tiles(256, 128) * batch <= cus) {
+                hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 64, 128, 64, O, PACKED, 1, 4, EXT>),
+                                   dim3(tiles(256, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y,
+                                   M, N, K, epi);
+                return hipGetLastError();
+            }
+            if ((int64_t)tiles(256, 256) * batch <= cus) {
+                hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 64, 128, 128, O, PACKED, 1, 4, EXT>),
+                                   dim3(tiles(256, 256), batch), dim3(256), 0, s, xq, w, sx, sw, y,
+                                   M, N, K, epi);
+                return hipGetLastError();
+            }
+        }
     }
     if (M <= 256) {
         // Few token rows and more tiles than CUs: 128-row tiles still leave
