@@ -29,8 +29,10 @@ codes downstream depend on them):
 
 A GPU that sums in double in another order reaches the same fp32 mu and
 rstd unless the exact statistic lies within that summation's error bound of
-an fp32 rounding boundary; ``ambiguous_rows`` reports such rows so that a
-test can treat them as having two correct answers.
+an fp32 rounding boundary; ``ambiguous_rows`` reports such rows, and
+``admissible_stats`` / ``row_alternatives`` enumerate every fp32 (mu, rstd)
+such a summation may give and the row's results under each, so that a test
+can require the GPU's row to equal one of them.
 """
 from __future__ import annotations
 
@@ -61,10 +63,13 @@ def layernorm_stats(x, eps: float):
     return mu, rstd
 
 
-def layernorm_f32(x, gamma, beta, eps: float):
-    """fp32 LayerNorm output [M x K] (before the store in the activation dtype)."""
+def layernorm_f32(x, gamma, beta, eps: float, stats=None):
+    """fp32 LayerNorm output [M x K] (before the store in the activation
+    dtype); ``stats`` = (mu, rstd) fp32 [M] replaces the row statistics."""
     x32 = np.asarray(x, np.float32)
-    mu, rstd = layernorm_stats(x32, eps)
+    mu, rstd = layernorm_stats(x32, eps) if stats is None else stats
+    mu = np.asarray(mu, np.float32)
+    rstd = np.asarray(rstd, np.float32)
     g = np.asarray(gamma, np.float32)[None, :]
     b = np.asarray(beta, np.float32)[None, :]
     t = (x32 - mu[:, None]).astype(np.float32)
@@ -101,32 +106,69 @@ def sum_exact_in_any_order(row) -> bool:
     return math.fsum(np.abs(v).tolist()) < math.ldexp(1.0, 52 + q)
 
 
+def _stat_error_bounds(row: np.ndarray, eps: float):
+    """(mu_d, rstd_d, e_mu, e_rstd, exact) for one row of exact float64 values.
+
+    A double sum of K terms in any order is within K * 2^-53 * sum|terms| of
+    the exact sum (zero when the sum is exact in any order,
+    ``sum_exact_in_any_order``); the bounds carry that through mu_d, var_d and
+    rstd_d with margin (a factor of 4) and add two double ulps for each
+    correctly rounded operation."""
+    K = row.shape[0]
+    u = 2.0 ** -53
+    mu_d, var_d, rstd_d = _row_stats(row, eps)
+    # an exact sum makes mu_d the same correctly rounded quotient on both
+    # sides, so fp32(mu_d) is then decided even on a midpoint
+    exact = sum_exact_in_any_order(row)
+    e_mu = 0.0 if exact else 4 * (u * float(np.abs(row).sum()) + 2 * u * abs(mu_d))
+    d = np.abs(row - mu_d)
+    e_var = 4 * (K * u * float((d * d).sum()) / K + 2 * e_mu * float(d.sum()) / K
+                 + e_mu * e_mu + 2 * u * var_d)
+    # rstd = (var + eps)^-1/2: relative error half that of var + eps
+    e_rstd = 4 * (0.5 * e_var / (var_d + eps) * rstd_d + 4 * u * rstd_d)
+    return mu_d, rstd_d, e_mu, e_rstd, exact
+
+
 def ambiguous_rows(x, eps: float):
     """Rows whose fp32 mu or rstd may differ by one unit when the double sums
-    are taken in another order.  A double sum of K terms in any order is
-    within K * 2^-53 * sum|terms| of the exact sum (zero when the sum is
-    exact in any order, ``sum_exact_in_any_order``); the bound below carries
-    that through mu_d, var_d and rstd_d with margin (a factor of 4) and adds
-    two double ulps for each correctly rounded operation."""
+    are taken in another order (the error bounds of ``_stat_error_bounds``
+    reach an fp32 rounding boundary)."""
     x = np.asarray(x, np.float32).astype(np.float64)
-    M, K = x.shape
-    u = 2.0 ** -53
     out = []
-    for m in range(M):
-        row = x[m]
-        mu_d, var_d, rstd_d = _row_stats(row, eps)
-        # an exact sum makes mu_d the same correctly rounded quotient on both
-        # sides, so fp32(mu_d) is then decided even on a midpoint
-        exact = sum_exact_in_any_order(row)
-        e_mu = 0.0 if exact else 4 * (u * float(np.abs(row).sum()) + 2 * u * abs(mu_d))
-        d = np.abs(row - mu_d)
-        e_var = 4 * (K * u * float((d * d).sum()) / K + 2 * e_mu * float(d.sum()) / K
-                     + e_mu * e_mu + 2 * u * var_d)
-        # rstd = (var + eps)^-1/2: relative error half that of var + eps
-        e_rstd = 4 * (0.5 * e_var / (var_d + eps) * rstd_d + 4 * u * rstd_d)
+    for m in range(x.shape[0]):
+        mu_d, rstd_d, e_mu, e_rstd, exact = _stat_error_bounds(x[m], eps)
         if (not exact and _near_f32_boundary(mu_d, e_mu)) or _near_f32_boundary(rstd_d, e_rstd):
             out.append(m)
     return out
+
+
+def _f32_candidates(v: float, err: float, limit: int = 64):
+    """Every fp32 value that a double within err of v rounds to: rounding is
+    monotone, so they are the values between fp32(v - err) and fp32(v + err).
+    More than `limit` of them means the row is not a useful test case."""
+    lo, hi = np.float32(v - err), np.float32(v + err)
+    out = [lo]
+    while out[-1] < hi:
+        out.append(np.nextafter(out[-1], np.float32(np.inf)))
+        if len(out) > limit:
+            raise ValueError("statistic %r +- %r spans more than %d fp32 values" % (v, err, limit))
+    return out
+
+
+def admissible_stats(row, eps: float):
+    """All (mu, rstd) fp32 pairs that a double summation of the row in some
+    order may produce, within the bounds of ``_stat_error_bounds``; the first
+    pair is the one ``layernorm_stats`` gives (the correctly rounded sums).
+    A row that ``ambiguous_rows`` does not flag has exactly that one pair."""
+    r = np.asarray(row, np.float32).astype(np.float64)
+    mu_d, rstd_d, e_mu, e_rstd, _ = _stat_error_bounds(r, eps)
+    first = (np.float32(mu_d), np.float32(rstd_d))
+    pairs = [first]
+    for mu in _f32_candidates(mu_d, e_mu):
+        for rs in _f32_candidates(rstd_d, e_rstd):
+            if (mu, rs) != first:
+                pairs.append((mu, rs))
+    return pairs
 
 
 def store_dtype(y32: np.ndarray, dtype: str) -> np.ndarray:
@@ -141,11 +183,25 @@ def store_dtype(y32: np.ndarray, dtype: str) -> np.ndarray:
     return t.float().numpy()
 
 
-def layernorm_quant_pertoken(x, gamma, beta, eps: float, dtype: str):
+def layernorm_quant_pertoken(x, gamma, beta, eps: float, dtype: str, stats=None):
     """(xq int8 [M x K], x_scale fp32 [M], x_hat [M x K] as stored in `dtype`,
     widened to fp32): LayerNorm with the folded (gamma, beta), stored in the
-    activation dtype, then per-token quantisation of the stored values."""
+    activation dtype, then per-token quantisation of the stored values.
+    ``stats`` = (mu, rstd) replaces the row statistics (see
+    ``admissible_stats``)."""
     from . import quant_act_pertoken
-    y = store_dtype(layernorm_f32(x, gamma, beta, eps), dtype)
+    y = store_dtype(layernorm_f32(x, gamma, beta, eps, stats), dtype)
     xq, sx = quant_act_pertoken(y)
     return xq, sx, y
+
+
+def row_alternatives(row, gamma, beta, eps: float, dtype: str):
+    """The results (xq [K], x_scale, x_hat [K]) of one row under each of its
+    admissible statistics (``admissible_stats``), the standard one first."""
+    x = np.asarray(row, np.float32)[None, :]
+    out = []
+    for mu, rs in admissible_stats(row, eps):
+        xq, sx, y = layernorm_quant_pertoken(x, gamma, beta, eps, dtype,
+                                             (np.array([mu]), np.array([rs])))
+        out.append((xq[0], sx[0], y[0]))
+    return out

@@ -4,9 +4,10 @@ oracle (oracle/layernorm.py).
 
 Bar: codes, steps and the stored LayerNorm output bit-exact on every row the
 oracle does not flag as ambiguous (an exact statistic within the double
-summation's error bound of an fp32 rounding boundary: two fp32 results are
-correct there); flagged rows may differ by one unit of the stored dtype and
-one code.
+summation's error bound of an fp32 rounding boundary: more than one fp32
+(mean, rstd) is correct there); a flagged row must equal, codes, step and
+stored output together, the oracle's row under one of its admissible
+statistics (``admissible_stats``).
 """
 import numpy as np
 import pytest
@@ -60,11 +61,12 @@ def _check(dev, x, g, b, eps, dt):
     assert_equal(g_xh[ok], xh_r[ok], "stored LayerNorm output")
     assert_equal(g_xq[ok], xq_r[ok], "codes")
     assert_equal(g_sx[ok], sx_r[ok], "steps")
-    if amb:
-        d = np.abs(g_xh[amb].astype(np.float64) - xh_r[amb])
-        assert (d <= 2 * np.spacing(np.abs(xh_r[amb]).astype(np.float32)) * (
-            8192 if dt == "f16" else 65536 if dt == "bf16" else 1)).all()
-        assert (np.abs(g_xq[amb].astype(int) - xq_r[amb].astype(int)) <= 1).all()
+    for m in amb:
+        alts = lnref.row_alternatives(x32[m], g, b, eps, dt)
+        hit = [i for i, (q, st, h) in enumerate(alts)
+               if np.array_equal(g_xq[m], q) and g_sx[m] == st and np.array_equal(g_xh[m], h)]
+        log("  row %d: %d admissible statistics, the GPU's is #%s" % (m, len(alts), hit))
+        assert hit, "row %d equals none of its %d admissible results" % (m, len(alts))
 
 
 CASES = [(1, 512, "f32"), (16, 4096, "f16"), (37, 1000, "f16"), (5, 1001, "bf16"),

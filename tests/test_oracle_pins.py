@@ -651,3 +651,34 @@ def test_batched_weight_quant_is_per_entry(ref):
         q1, s1 = ref.quant_weight_perchannel(w[b])
         assert np.array_equal(wq[b], q1) and np.array_equal(sw[b], s1)
     assert sw[2, 3] == 0.0 and not wq[2, 3].any()
+
+
+def test_layernorm_admissible_stats_cover_every_summation_order():
+    """The admissible (mu, rstd) of a row are the fp32 roundings reachable by
+    double sums in any order: brute force over random permutations of rows
+    whose sums depend on the order (sequential double adds, the mean and the
+    centred sum of squares as the oracle forms them) lands in the set; an
+    unflagged row has only its standard pair; a flagged one has more."""
+    import math
+    from oracle import layernorm as ln
+    r = np.random.default_rng(35)
+    eps = 1e-5
+    rows = [np.array([2.0 ** 30, -2.0 ** 30, 1.0, 1.0 + 2.0 ** -23], np.float32),
+            (r.standard_normal(64) * np.exp2(r.integers(-20, 24, 64))).astype(np.float32)]
+    for row in rows:
+        pairs = ln.admissible_stats(row, eps)
+        assert pairs[0] == tuple(np.float32(v[0]) for v in ln.layernorm_stats(row[None], eps))
+        v = row.astype(np.float64)
+        K = v.size
+        for _ in range(300):
+            p = v[r.permutation(K)]
+            mu_d = float(np.cumsum(p)[-1]) / K
+            d = p - mu_d
+            var_d = float(np.cumsum(d * d)[-1]) / K
+            got = (np.float32(mu_d), np.float32(1.0 / math.sqrt(var_d + eps)))
+            assert got in pairs, (got, pairs[:3])
+    assert len(ln.admissible_stats(rows[0], eps)) > 1
+    plain = r.standard_normal(256).astype(np.float16).astype(np.float32)
+    assert ln.ambiguous_rows(plain[None], eps) == []
+    assert ln.admissible_stats(plain, eps) == [tuple(np.float32(v[0]) for v in
+                                                     ln.layernorm_stats(plain[None], eps))]

@@ -72,8 +72,15 @@ def test_smooth_fold(ref, dev, K, N, dt, alpha):
     assert_equal(to_np(w_hat)[same], w_hat_ref[same], "W_hat rows with equal s")
     assert_equal(to_np(g_gpu)[same], g_ref[same], "gamma'")
     assert_equal(to_np(b_gpu)[same], b_ref[same], "beta'")
-    if (~same).any():  # the rows of an ulp-different s are one fp32 multiply away
-        np.testing.assert_allclose(to_np(w_hat)[~same], w_hat_ref[~same], rtol=2.5e-7)
+    if (~same).any():
+        # an ulp-different s_j (the two double pow results straddle an fp32
+        # rounding boundary) is the other admissible factor: the row is then
+        # the oracle's fold with the GPU's s_j, bit for bit
+        w_hat_alt = ref.fold_weight(w, s_g)
+        g_alt, b_alt = ref.fold_norm(s_g, gamma, beta)
+        assert_equal(to_np(w_hat)[~same], w_hat_alt[~same], "W_hat rows with the other s")
+        assert_equal(to_np(g_gpu)[~same], g_alt[~same], "gamma' with the other s")
+        assert_equal(to_np(b_gpu)[~same], b_alt[~same], "beta' with the other s")
 
 
 # --------------------------------------------------------------- weight quant
@@ -169,7 +176,8 @@ GEMM_SHAPES = [
     (40, 12288, 256), (33, 16384, 384), (64, 12300, 128),        # 17-64 rows on wide layers: tiles
     (32, 12288, 512), (17, 28672, 256), (31, 12288, 256),        # the edge of that rule (31: few-token)
     (70, 200, 16384), (130, 260, 16384),                         # deep: 64-deep k-tiles, four stages
-]
+    (130, 16400, 8192), (129, 32896, 8192),                      # 129-256 rows, wide and deep:
+]                                                                # 256 x 128 / 256 x 256, four stages
 
 
 def _codes(M, N, K, seed):

@@ -232,3 +232,62 @@ def test_linear_packed_static_alias(dev):
     with pytest.raises(sq.SQError) as ei:
         sq.sq_w8a8_linear_packed_static(x, wp, sw, sx[1:], xq, sx, y)
     assert ei.value.code == 8
+
+
+# Values whose quotient v / step overflows fp32 under steps inside the
+# reciprocal fast path [2^-96, 2^96]: they must saturate to +-127 with their
+# own sign (P1 推論方法 O3: a static step clamps values past the calibrated
+# range).  fp16 cannot reach such quotients (|v| <= 65504).
+OVERFLOW_STEPS = [2.0 ** -96, 1e-20, 0.05]
+
+
+def _overflow_input(rng, M, K, step, dt):
+    x = (rng.standard_normal((M, K)) * 90.0 * step).astype(np.float32)
+    big = np.array([1e10, 1e19, 3e37, 3.3e38], np.float32)
+    idx = rng.integers(0, M * K, 64)
+    x.ravel()[idx] = big[rng.integers(0, 4, 64)] * np.where(rng.random(64) < 0.5, -1.0, 1.0)
+    x.ravel()[idx[:2]] = [3e37, -3e37]
+    t = torch.from_numpy(x)
+    if dt == "bf16":
+        t = t.to(torch.bfloat16)
+    return t, idx[:2]
+
+
+@pytest.mark.parametrize("step_val", OVERFLOW_STEPS)
+@pytest.mark.parametrize("M,K,dt", [(6, 1024, "f32"), (5, 1001, "f32"), (7, 13, "f32"),
+                                    (6, 1024, "bf16"), (3, 4104, "bf16"), (1, 9, "bf16")])
+def test_quant_act_static_overflow(ref, dev, M, K, dt, step_val):
+    rng = np.random.default_rng([17, M, K])
+    x, planted = _overflow_input(rng, M, K, step_val, dt)
+    st = torch.tensor([step_val], dtype=torch.float32, device=dev)
+    xq, sx = sq.quant_act_pertensor(_gpu(x, dev), None, st)
+    torch.cuda.synchronize()
+    xq_r, sx_r = ref.quant_act_pertensor(x.float().numpy(), np.float32(step_val))
+    assert list(xq_r.ravel()[planted]) == [127, -127]
+    assert_equal(sx, sx_r, "x_scale (given step %g)" % step_val)
+    assert_equal(xq, xq_r, "xq (given step %g, quotients past fp32)" % step_val)
+
+
+# one kernel (M <= 2, M * K <= 16384) and the codes kernel + packed GEMM
+@pytest.mark.parametrize("M,N,K,xdt", [(1, 4096, 4096, "bf16"), (2, 700, 8192, "f32"),
+                                       (16, 1000, 2048, "f32"), (300, 1000, 1024, "bf16")])
+def test_linear_packed_static_overflow(ref, dev, M, N, K, xdt):
+    rng = np.random.default_rng([19, M, N, K])
+    # calibration maxima that give the step 2^-90 (inside the fast path)
+    a_r = np.full(K, np.float32(127.0 * 2.0 ** -90), np.float32)
+    ones = np.ones(K, np.float32)
+    step_r = ref.static_act_step(a_r, ones)
+    x, planted = _overflow_input(rng, M, K, float(step_r), xdt)
+    w = synth.random_matrix(N + 43 * K, K, N, "f32", scale=0.02)
+    step = sq.static_act_step(_gpu(torch.from_numpy(a_r), dev), _gpu(torch.from_numpy(ones), dev))
+    wq, sw = sq.quant_weight_pertensor(_gpu(w, dev))
+    y, xq, sx = sq.linear_w8a8_packed_static(_gpu(x, dev), sq.pack_weight(wq), sw, step,
+                                              torch.float32)
+    torch.cuda.synchronize()
+    wq_r, sw_r = ref.quant_weight_pertensor(w)
+    xq_r, sx_r = ref.quant_act_pertensor(x.float().numpy(), step_r)
+    assert list(xq_r.ravel()[planted]) == [127, -127]
+    assert_equal(step, np.array([step_r], np.float32), "static step")
+    assert_equal(xq, xq_r, "xq (one-call O3, quotients past fp32)")
+    assert_equal(sx, sx_r, "x_scale (one-call O3)")
+    _y_check(ref, dev, y, xq_r, sx_r, wq_r, sw_r, "y (one-call O3, quotients past fp32)")

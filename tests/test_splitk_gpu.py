@@ -122,7 +122,7 @@ def test_splitk_workspace_errors(dev):
     sw = torch.ones(N, device=dev)
     y = torch.empty(M, N, dtype=torch.float16, device=dev)
     small = torch.zeros(1024, dtype=torch.uint8, device=dev)
-    with pytest.raises(sq.SQError):
-        sq.sq_w8a8_gemm_dequant_packed_ws(xq, sx, wp, sw, N, y, small)
-    with pytest.raises(sq.SQError):
-        sq.sq_w8a8_gemm_dequant_packed_ws(xq, sx, wp, sw, N, y, None)
+    for ws in (small, None):
+        with pytest.raises(sq.SQError) as ei:
+            sq.sq_w8a8_gemm_dequant_packed_ws(xq, sx, wp, sw, N, y, ws)
+        assert ei.value.code == 11 and "SQ_ERR_WORKSPACE" in str(ei.value)

@@ -42,7 +42,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsq.so")
 
 STATUS = {0: "SQ_OK", 1: "SQ_ERR_NULL", 2: "SQ_ERR_SHAPE", 3: "SQ_ERR_DTYPE",
           4: "SQ_ERR_K_OVERFLOW", 5: "SQ_ERR_ALIGN", 6: "SQ_ERR_ALPHA", 7: "SQ_ERR_HIP",
-          8: "SQ_ERR_ALIAS", 9: "SQ_ERR_ACT", 10: "SQ_ERR_EPS"}
+          8: "SQ_ERR_ALIAS", 9: "SQ_ERR_ACT", 10: "SQ_ERR_EPS",
+          11: "SQ_ERR_WORKSPACE"}
 SQ_F32, SQ_F16, SQ_BF16 = 0, 1, 2
 SQ_ACT_NONE, SQ_ACT_RELU = 0, 1
 _DT = {torch.float32: SQ_F32, torch.float16: SQ_F16, torch.bfloat16: SQ_BF16}

@@ -36,19 +36,19 @@ __device__ inline void load_smoothed(const typename D::T* p, const float* smooth
     }
 }
 
-template <bool FAST, int V>
+template <bool FAST, int V, bool SAT = false>
 __device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowStep& step) {
     if constexpr (V == 8) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lo |= (uint32_t)(uint8_t)quant_code<FAST>(v[e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) lo |= (uint32_t)(uint8_t)quant_code<FAST, SAT>(v[e], step) << (8 * e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code<FAST>(v[4 + e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code<FAST, SAT>(v[4 + e], step) << (8 * e);
         *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
     } else {
         uint32_t w = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code<FAST>(v[e], step) << (8 * e);
+        for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code<FAST, SAT>(v[e], step) << (8 * e);
         *reinterpret_cast<uint32_t*>(dst) = w;
     }
 }
@@ -379,10 +379,12 @@ __global__ __launch_bounds__(kTensorThreads) void tensor_quant_kernel(
         for (int u = 0; u < kTensorUnroll; ++u) {
             const int64_t i = i0 + u * stride;
             if (i >= total) continue;
+            // the step may be a static one: values beyond 128 steps saturate
             if constexpr (V == 1) {
-                xq[i] = (int8_t)(q.fast ? quant_code<true>(v[u][0], q) : quant_code<false>(v[u][0], q));
+                xq[i] = (int8_t)(q.fast ? quant_code<true, true>(v[u][0], q)
+                                        : quant_code<false>(v[u][0], q));
             } else if (q.fast) {
-                store_codes<true, V>(xq + i * V, v[u], q);
+                store_codes<true, V, true>(xq + i * V, v[u], q);
             } else {
                 store_codes<false, V>(xq + i * V, v[u], q);
             }

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
             int8_t q[V];
             if (st.fast) {
 #pragma unroll
-                for (int k = 0; k < V; ++k) q[k] = (int8_t)quant_code<true>(D::to_f32(e[k]), st);
+                for (int k = 0; k < V; ++k) q[k] = (int8_t)quant_code<true, STATIC>(D::to_f32(e[k]), st);
             } else {
 #pragma unroll
                 for (int k = 0; k < V; ++k) q[k] = (int8_t)quant_code<false>(D::to_f32(e[k]), st);

@@ -57,16 +57,18 @@ __device__ inline void pin_f32(float& v) { __asm__("" : "+v"(v)); }
 
 // ------------------------------------------------------------- quantiser
 // step = absmax / 127 (fp32 IEEE division); code = clamp(round half away
-// from zero (v / step), -127, 127); a zero step gives code 0.
-__device__ inline float quant_step(float absmax) { return absmax / 127.0f; }
+// from zero (v / step), -127, 127); a zero step gives code 0.  These helpers
+// are also built for the host, where a CPU test replays them against the
+// IEEE quotient.
+__host__ __device__ inline float quant_step(float absmax) { return absmax / 127.0f; }
 
-__device__ inline int code_from_quotient(float t) {
+__host__ __device__ inline int code_from_quotient(float t) {
     float r = __builtin_roundf(t);  // halves away from zero
     r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
     return (int)r;
 }
 
-__device__ inline int quant_code(float v, float step) {
+__host__ __device__ inline int quant_code(float v, float step) {
     if (step == 0.0f) return 0;
     return code_from_quotient(v / step);
 }
@@ -81,29 +83,39 @@ __device__ inline int quant_code(float v, float step) {
 // Dev. 34(1), 1990; correctness proofs by Cornea-Hasegan, Golliver and
 // Markstein, ARITH-14, 1999).  Steps outside [2^-96, 2^96] use the plain
 // IEEE division instead.
+//
+// A step fixed in advance (the static per-tensor step) meets values far
+// beyond 127 steps, and v * y may then overflow to infinity, which turns the
+// correction into inf - inf = NaN.  Such callers saturate v to +-128 steps
+// first (lim = 128 * step, exact: a power-of-two multiple of a step in
+// [2^-96, 2^96]): a value beyond it has the code +-127 either way, and the
+// quotient of the saturated value is exactly +-128, so the sign survives.
 struct RowStep {
-    float step, rcp;
+    float step, rcp, lim;
     bool fast;
 };
 
 // Quantiser parameters for a given step.
-__device__ inline RowStep given_step(float step) {
+__host__ __device__ inline RowStep given_step(float step) {
     RowStep q;
     q.step = step;
     q.fast = step >= 0x1p-96f && step <= 0x1p96f;
     q.rcp = q.fast ? 1.0f / step : 0.0f;
+    q.lim = q.fast ? 128.0f * step : 0.0f;
     return q;
 }
 
 // ... and for the step absmax / 127 of a row's maximum.
-__device__ inline RowStep row_step(float absmax) { return given_step(quant_step(absmax)); }
+__host__ __device__ inline RowStep row_step(float absmax) { return given_step(quant_step(absmax)); }
 
 // FAST: the caller has checked q.fast (a row-uniform branch taken once).
-template <bool FAST>
-__device__ inline int quant_code(float v, const RowStep& q) {
+// SAT: v may lie beyond 128 steps (a step not taken from v's own row).
+template <bool FAST, bool SAT = false>
+__host__ __device__ inline int quant_code(float v, const RowStep& q) {
     if (q.step == 0.0f) return 0;
     float t;
     if constexpr (FAST) {
+        if constexpr (SAT) v = __builtin_fminf(__builtin_fmaxf(v, -q.lim), q.lim);
         const float q0 = v * q.rcp;
         const float r = __builtin_fmaf(-q0, q.step, v);
         t = __builtin_fmaf(r, q.rcp, q0);

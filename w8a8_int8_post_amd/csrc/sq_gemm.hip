@@ -663,8 +663,8 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         // 129-256 rows on wide, deep layers (K >= 8192, more 128-row tiles
         // than CUs): one row of 256-row tiles, 256 x 128 or else 256 x 256,
         // in the same four-stage ring.  Measured: 28672 x 8192 at 129 / 256
-        // tokens 113 / 124 -> 78 / 90 us; 49152 x 12288 213 / 245 -> 191 /
-        // 212 us; 36864 x 12288 176 -> 163 us.  Not for more rows or K = 4096
+        // tokens 113 / 124 -> 92 / 88 us; 49152 x 12288 213 / 245 -> 186 /
+        // 208 us; 36864 x 12288 at 129 tokens 176 -> 163 us.  Not for more rows or K = 4096
         // (there it loses: 12288 x 4096 at 512 tokens 39 -> 43 us, 4096 x
         // 16384 at 1024 tokens 94 -> 141 us).
         if (K >= 8192 && M > 128 && M <= 256) {
