@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the SmoothQuant W8A8 linear-layer hot path on one MI355X.
 
-Workload (one step): the three linear layers of an OPT-6.7B-like block --
-QKV [4096 x 12288], FC1 [4096 x 16384], FC2 [16384 x 4096], fp16 -- each
-called on 2048 tokens: per-token INT8 activation quantisation followed by the
-INT8 GEMM with fused scale back (the run-time part of the method; the offline
-calibration / smoothing / weight quantisation is timed once, separately, and
-reported under "offline").  Inputs are seeded synthetic activations with 0.5%
-persistent outlier channels x60 and N(0, 0.02) weights, smoothed with
-alpha = 0.5, all resident in HBM before timing starts.
+Headline workload (one step): the three linear layers of an OPT-175B-like
+block -- QKV [12288 x 36864], FC1 [12288 x 49152], FC2 [49152 x 12288],
+bf16 -- each called on 8192 tokens: per-token INT8 activation quantisation
+followed by the INT8 GEMM with fused scale back (the run-time part of the
+method; the offline calibration / smoothing / weight quantisation runs once,
+untimed for the headline).  Inputs are seeded synthetic activations with 0.1%
+persistent outlier channels x100 and N(0, 0.02) weights, smoothed with
+alpha = 0.5, all resident in HBM before timing starts.  The step is timed as
+W warm-up steps, then 5 repeats of K steps between HIP events, the median
+reported; two buffer sets (weights included) alternate.
 
-The same layers at 1 and 16 tokens (decode) are timed as well and reported
-under "decode" in GB/s.  Buffer sets rotate so that weights are streamed from
-HBM rather than served by the 256 MB Infinity Cache.  The OPT-13B-like
-(4096 tokens, fp16) and OPT-175B-like (2048 and 8192 tokens, bf16) layer sets
-are timed the same way and reported under "larger_prefill".
+Also reported: the OPT-6.7B-like layers (fp16) at 2048 and 512 tokens, the
+OPT-13B-like layers at 4096 tokens and the OPT-175B-like ones at 2048, decode
+shapes (1 and 16 tokens; the Llama-70B-like layers at 1-16 tokens) in GB/s
+with weights streamed from HBM, the fused LayerNorm + quantiser, the INT8
+attention products, the per-tensor levels, the offline transform, and the CPU
+oracle on slices of the headline layers.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: the benchmark measures
 one GPU (one GPU's share of a layer at its real shape).
@@ -44,6 +47,9 @@ CFG = synth.CONFIGS[2]  # OPT-6.7B-like layers
 ALPHA = 0.5
 PREFILL_M = 2048
 DECODE_M = (1, 16)
+HEAD_CFG = synth.CONFIGS[4]  # OPT-175B-like layers (bf16): the headline
+HEAD_M = 8192
+REPEATS = 5
 
 
 def log(*a):
@@ -225,11 +231,31 @@ def time_rotation(fns, iters, warmup, min_calls=4):
     return time_graphs([g], reps, wreps) / len(seq)
 
 
-def profiled_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 summary, if it
-    was taken on the current GEMM source (else None)."""
+def time_steps(fns, steps, warmup, repeats=REPEATS):
+    """Median ms per call of fns (one graph each, replayed in rotation):
+    `warmup` untimed calls, then `repeats` timed runs of exactly `steps`
+    calls between HIP events on the current stream.  Returns (median, runs)."""
+    graphs = [capture(f) for f in fns]
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(e0.elapsed_time(e1) / steps)
+    return float(np.median(runs)), runs
+
+
+def profiled_traffic(summary):
+    """HBM bytes per GEMM launch from a committed rocprofv3 summary under
+    profiles/, if it was taken on the current GEMM source (else None)."""
     import hashlib
-    prof = os.path.join(ROOT, "profiles", "gemm_prefill_opt6.7b.md")
+    prof = os.path.join(ROOT, "profiles", summary)
     csrc = os.path.join(ROOT, "w8a8_int8_post_amd", "csrc")
     try:
         fields = dict(ln.split(": ", 1) for ln in open(prof).read().splitlines()
@@ -359,18 +385,30 @@ def decode_llama70b(dev, args):
 def prefill_512(layers, dev, args, M5=512):
     """The OPT-6.7B-like layers at 512 tokens: the plain packed path and the
     split-K entry point (which splits K only where that beats the plain
-    kernels; "split_layers" names those layers)."""
+    kernels; "split_layers" names those layers).  Besides TOPS, the step is
+    given as a fraction of its roofline floor, sum over layers of
+    max(ops / INT8 peak, algorithmic bytes / HBM bandwidth): at 512 tokens
+    these layers sit just right of the ridge point (about 770 ops/byte)."""
     ops5 = sum(2.0 * M5 * ly.N * ly.K for ly in layers)
+    floor_ms = 0.0
+    for ly in layers:
+        nbytes = ly.N * ly.K + 4 * ly.N + 2 * M5 * ly.K + 2 * M5 * ly.N + 4 * M5
+        floor_ms += max(2.0 * M5 * ly.N * ly.K / (PEAK_I8_TOPS * 1e9),
+                        nbytes / (PEAK_HBM_GBS * 1e6))
     p512 = {"tokens": M5,
             "split_layers": [ly.name for ly in layers
-                             if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0]}
+                             if sq.sq_gemm_workspace_bytes(M5, ly.N, ly.K) > 0],
+            "roofline_floor_ms": round(floor_ms, 4)}
     for mode in ("o1", "ws"):
         sets = [Bufs(layers, M5, dev, True, mode) for _ in range(2)]
         ms5 = time_rotation([b.step for b in sets], args.steps, args.warmup)
         p512["split_k" if mode == "ws" else "plain"] = {
-            "ms_per_step": round(ms5, 4), "tops": round(ops5 / ms5 / 1e9, 1)}
-        log("prefill at %d tokens (%s): step %.3f ms, %.1f TOPS"
-            % (M5, "split-K entry point" if mode == "ws" else "plain", ms5, ops5 / ms5 / 1e9))
+            "ms_per_step": round(ms5, 4), "tops": round(ops5 / ms5 / 1e9, 1),
+            "frac_of_int8_peak": round(ops5 / ms5 / 1e9 / PEAK_I8_TOPS, 4),
+            "frac_of_roofline": round(floor_ms / ms5, 4)}
+        log("prefill at %d tokens (%s): step %.3f ms, %.1f TOPS, %.1f%% of the roofline floor"
+            % (M5, "split-K entry point" if mode == "ws" else "plain", ms5, ops5 / ms5 / 1e9,
+               100 * floor_ms / ms5))
         del sets
         torch.cuda.synchronize()
     p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
@@ -378,7 +416,102 @@ def prefill_512(layers, dev, args, M5=512):
     return p512
 
 
-LARGER = ((3, (4096,)), (4, (2048, 8192)))  # OPT-13B-like, OPT-175B-like (config, tokens)
+def prepare_layers(cfg, M, dev, keep_host_rows=0):
+    """Each layer of cfg through the library's offline path (calibration on
+    the config's calibration tokens, smoothing factors and fold, per-channel
+    weight quantisation, packing) plus its smoothed evaluation activations
+    (M tokens), as a folded LayerNorm would emit them.  With keep_host_rows,
+    host copies of the row-major codes, steps and the first rows of X_hat are
+    kept for the CPU oracle."""
+    prep, host = [], []
+    for ly in cfg.layers:
+        w = synth.weight(cfg, ly.name).to(dev)
+        xc = synth.activations(cfg, ly.name, cfg.T, calibration=True).to(dev)
+        s_, w_hat = sq.smooth_fold(sq.calibrate_absmax(xc), w, ALPHA)
+        del w, xc
+        wq, sw = sq.quant_weight_perchannel(w_hat)
+        del w_hat
+        wp = sq.pack_weight(wq)
+        x = synth.activations(cfg, ly.name, M).to(dev)
+        x_hat = sq.smooth_activation(x, s_)
+        del x
+        torch.cuda.synchronize()
+        if keep_host_rows:
+            host.append((x_hat[:keep_host_rows].float().cpu().numpy(), wq.cpu().numpy(),
+                         sw.cpu().numpy(), ly.N, ly.K))
+        del wq
+        prep.append((ly, wp, sw, x_hat))
+        torch.cuda.synchronize()
+    return prep, host
+
+
+def layer_sets(prep, M, ydt, dev, R=2):
+    """R independent run-time buffer sets (weights included) for M tokens."""
+    sets = []
+    for _ in range(R):
+        sets.append([(x_hat[:M].clone(), wp.clone(), sw.clone(),
+                      torch.empty(M, ly.K, dtype=torch.int8, device=dev),
+                      torch.empty(M, dtype=torch.float32, device=dev),
+                      torch.empty(M, ly.N, dtype=ydt, device=dev), ly.N)
+                     for (ly, wp, sw, x_hat) in prep])
+    return sets
+
+
+def headline(dev, args):
+    """The OPT-175B-like block at 8192 tokens: step = per layer the per-token
+    quantiser and the packed GEMM with the scale back (bf16 out); each GEMM
+    and each quantiser also alone.  Returns (result dict, host data for the
+    CPU baseline)."""
+    cfg, M = HEAD_CFG, HEAD_M
+    ydt = synth.DTYPES[cfg.ydt]
+    log("setting up the headline layers", [(ly.name, ly.K, ly.N) for ly in cfg.layers])
+    prep, host = prepare_layers(cfg, M, dev, keep_host_rows=CPU_SLICE_ROWS)
+    sets = layer_sets(prep, M, ydt, dev)
+    del prep
+    torch.cuda.synchronize()
+
+    def step(bs):
+        for (x_hat, wp, sw, xq, sx, y, N) in bs:
+            sq.sq_quant_act_pertoken(x_hat, xq, sx)
+            sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y)
+
+    ops = sum(2.0 * M * ly.N * ly.K for ly in cfg.layers)
+    ms, runs = time_steps([lambda bs=bs: step(bs) for bs in sets], args.steps, args.warmup)
+    log("headline %s at %d tokens: step %.3f ms (runs %s), %.1f TOPS"
+        % (cfg.name, M, ms, ", ".join("%.3f" % r for r in runs), ops / ms / 1e9))
+    layers = {}
+    gemm_us, quant_us = [], []
+    for i, ly in enumerate(cfg.layers):
+        def gemm(bs, i=i):
+            x_hat, wp, sw, xq, sx, y, N = bs[i]
+            sq.sq_w8a8_gemm_dequant_packed(xq, sx, wp, sw, N, y)
+
+        def quant(bs, i=i):
+            x_hat, wp, sw, xq, sx, y, N = bs[i]
+            sq.sq_quant_act_pertoken(x_hat, xq, sx)
+        ms_g, _ = time_steps([lambda bs=bs: gemm(bs) for bs in sets], args.steps, args.warmup)
+        ms_q, _ = time_steps([lambda bs=bs: quant(bs) for bs in sets], args.steps, args.warmup)
+        lops = 2.0 * M * ly.N * ly.K
+        qbytes = M * ly.K * 2 + M * ly.K + 4 * M
+        layers[ly.name] = {"gemm_us": round(ms_g * 1e3, 1),
+                           "gemm_tops": round(lops / ms_g / 1e9, 1),
+                           "frac_of_int8_peak": round(lops / ms_g / 1e9 / PEAK_I8_TOPS, 4),
+                           "act_quant_us": round(ms_q * 1e3, 2),
+                           "act_quant_gbs": round(qbytes / ms_q / 1e6, 1)}
+        gemm_us.append(ms_g * 1e3)
+        quant_us.append(ms_q * 1e3)
+        log("  %s: gemm %.1f us (%.1f TOP/s), quantiser %.1f us"
+            % (ly.name, ms_g * 1e3, lops / ms_g / 1e9, ms_q * 1e3))
+    del sets
+    torch.cuda.synchronize()
+    return {"cfg": cfg, "M": M, "ms": ms, "runs": runs, "ops": ops, "layers": layers,
+            "gemm_avg_us": float(np.mean(gemm_us)), "quant_avg_us": float(np.mean(quant_us)),
+            "per_launch_ops": ops / len(cfg.layers),
+            "quant_bytes": sum(M * ly.K * 2 + M * ly.K + 4 * M for ly in cfg.layers)
+            / len(cfg.layers)}, host
+
+
+LARGER = ((3, (4096,)), (4, (2048,)))  # OPT-13B-like, OPT-175B-like (config, tokens)
 
 
 def larger_prefill(dev, args):
@@ -458,31 +591,44 @@ def n_sets(footprint_bytes):
 
 # ---------------------------------------------------------------- cpu baseline
 
-def cpu_baseline(layers, target_s=12.0):
-    """The CPU oracle (per-token quant + INT8 GEMM + scale back) on a bounded
-    sample of the prefill workload: the first r tokens of every layer."""
+CPU_SLICE_ROWS = 256     # all host cores: 256-token slice of every headline layer
+CPU_SLICE_ROWS_1T = 16   # one thread: 16-token slice
+
+
+def cpu_baseline(host, M, cfg):
+    """The CPU oracle (per-token quant + INT8 GEMM + scale back, OpenMP over
+    token rows) on slices of the headline layers: the first CPU_SLICE_ROWS
+    tokens of each layer on all host cores and the first CPU_SLICE_ROWS_1T on
+    one thread, each the median of 3 runs.  GEMM work is linear in the token
+    count, so the rate is the full step's, extrapolated."""
     import oracle
-    wq_h = [ly.wq.cpu().numpy() for ly in layers]
-    sw_h = [ly.sw.cpu().numpy() for ly in layers]
-    xh_h = [ly.x_hat.cpu().float().numpy() for ly in layers]
 
     def run(rows):
         t0 = time.perf_counter()
-        for x, wq, sw in zip(xh_h, wq_h, sw_h):
-            oracle.linear_w8a8(x[:rows], wq, sw)
+        for (xh, wq, sw, N, K) in host:
+            oracle.linear_w8a8(xh[:rows], wq, sw)
         return time.perf_counter() - t0
 
-    rows = 2
-    run(rows)  # warm the thread pool
-    t = run(rows)
-    while t < 0.5 * target_s and rows < PREFILL_M:
-        rows = max(rows + 1, min(PREFILL_M, int(rows * target_s / max(t, 1e-3))))
-        t = run(rows)
-    ops = sum(2.0 * rows * ly.N * ly.K for ly in layers)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(ops / t / 1e12, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
-            "sample": "first %d of %d tokens of each of the 3 layers (quant + INT8 GEMM + scale "
-                      "back), %.1f s wall" % (rows, PREFILL_M, t)}
+    def ops(rows):
+        return sum(2.0 * rows * N * K for (_, _, _, N, K) in host)
+
+    cores = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    run(2)  # start the thread pool
+    t_all = float(np.median([run(CPU_SLICE_ROWS) for _ in range(3)]))
+    oracle.set_threads(1)
+    t_one = float(np.median([run(CPU_SLICE_ROWS_1T) for _ in range(3)]))
+    oracle.set_threads(cores)
+    tops_all = ops(CPU_SLICE_ROWS) / t_all / 1e12
+    tops_one = ops(CPU_SLICE_ROWS_1T) / t_one / 1e12
+    return {"value": round(tops_all, 6), "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": "first %d of %d tokens of each of the 3 %s layers (quant + INT8 GEMM + scale "
+                      "back), median of 3 runs of %.1f s; extrapolated linearly in tokens"
+                      % (CPU_SLICE_ROWS, M, cfg.name, t_all),
+            "extrapolated_step_s": round(t_all * M / CPU_SLICE_ROWS, 1),
+            "one_thread": {"value": round(tops_one, 6), "unit": "TOPS", "cores": 1,
+                           "sample": "first %d tokens of each layer, median of 3 runs of %.1f s"
+                                     % (CPU_SLICE_ROWS_1T, t_one),
+                           "extrapolated_step_s": round(t_one * M / CPU_SLICE_ROWS_1T, 1)}}
 
 
 # ---------------------------------------------------------------- main
@@ -500,7 +646,11 @@ def main():
     ap.add_argument("--no-prefill-512", action="store_true",
                     help="skip the 512-token prefill (plain and split-K)")
     ap.add_argument("--no-larger", action="store_true",
-                    help="skip the OPT-13B-like and OPT-175B-like prefill layers")
+                    help="skip the OPT-13B-like (4096 tokens) and OPT-175B-like (2048 tokens) layers")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline step (OPT-175B-like, 8192 tokens; for profiling)")
+    ap.add_argument("--opt67b-only", action="store_true",
+                    help="only the OPT-6.7B-like layers at 2048 tokens (for profiling)")
     ap.add_argument("--prefill-512-only", action="store_true",
                     help="only the 512-token prefill (prints {\"prefill_512\": ...}; for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -525,78 +675,109 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
         return
 
-    log("setting up layers", [(ly.name, ly.K, ly.N) for ly in CFG.layers])
+    out = {}
+    host = None
+    if not (args.opt67b_only or args.prefill_512_only):
+        # ---- the headline: OPT-175B-like block, 8192 tokens, bf16
+        hd, host = headline(dev, args)
+        cfg = hd["cfg"]
+        tops = hd["ops"] / (hd["ms"] * 1e-3) / 1e12
+        gemm_tops = hd["per_launch_ops"] / (hd["gemm_avg_us"] * 1e-6) / 1e12
+        out = {
+            "metric": METRIC,
+            "value": round(tops, 2),
+            "unit": "TOPS",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(hd["ms"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "i8",
+            "data": "synthetic",
+            "config": {
+                "workload": "OPT-175B-like linear layers QKV 12288x36864, FC1 12288x49152, FC2 "
+                            "49152x12288; bf16 activations/weights/output; 8192 tokens per layer "
+                            "call; 0.1% persistent outlier channels x100; alpha 0.5",
+                "tokens": hd["M"],
+                "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant_packed (3 layers)",
+                "weights": "fragment-packed",
+                "timing": "median of %d runs of %d steps (HIP events; two buffer sets alternate); "
+                          "runs ms/step %s" % (REPEATS, args.steps,
+                                              ", ".join("%.4f" % r for r in hd["runs"])),
+                "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
+                "layers": hd["layers"],
+                "parallelism": "single GPU",
+            },
+            "roofline": {
+                "kernel": "gemm_dma_kernel (i8 MFMA GEMM + fused scale back), 256x256 tiles",
+                "bound": "mfma",
+                "achieved": round(gemm_tops * 1e3, 2),
+                "peak": PEAK_I8_TOPS,
+                "unit": "TOP/s",
+                "frac": round(gemm_tops * 1e3 / PEAK_I8_TOPS, 4),
+                "traffic": profiled_traffic("gemm_prefill_opt175b.md"),
+                "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
+                                "profiles/gemm_prefill_opt175b.md)",
+                "avg_launch_us": round(hd["gemm_avg_us"], 2),
+                "per_launch_ops": hd["per_launch_ops"],
+            },
+            "act_quant": {"avg_launch_us": round(hd["quant_avg_us"], 2),
+                          "gbs": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3, 1),
+                          "hbm_frac": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3
+                                            / PEAK_HBM_GBS, 3)},
+        }
+        if args.headline_only:
+            print(json.dumps(out), flush=True)
+            return
+
+    log("setting up the OPT-6.7B-like layers", [(ly.name, ly.K, ly.N) for ly in CFG.layers])
     layers = [Layer(ly.name, dev) for ly in CFG.layers]
     if args.prefill_512_only:
         print(json.dumps({"prefill_512": prefill_512(layers, dev, args)}), flush=True)
         return
 
-    # ---- prefill: the headline step, with row-major and with packed weights
+    # ---- the OPT-6.7B-like layers at 2048 tokens, row-major and packed weights
     M = PREFILL_M
     ops_step = sum(2.0 * M * ly.N * ly.K for ly in layers)
     quant_bytes = sum(M * ly.K * 2 + M * ly.K + 4 * M for ly in layers) / len(layers)
     res = {}
     for packed in (False, True):
         sets = [Bufs(layers, M, dev, packed) for _ in range(2)]
-        ms = time_rotation([b.step for b in sets], args.steps, args.warmup)
+        ms, runs = time_steps([b.step for b in sets], args.steps, args.warmup)
         gemm_ms = time_rotation([b.gemm_only for b in sets], args.steps, args.warmup) / len(layers)
         quant_ms = time_rotation([b.quant_only for b in sets], args.steps,
                                  args.warmup) / len(layers)
         res[packed] = (ms, gemm_ms, quant_ms)
-        log("prefill (%s weights): step %.3f ms  %.1f TOPS; gemm avg %.1f us (%.1f TOPS); "
+        log("opt-6.7b prefill (%s weights): step %.3f ms  %.1f TOPS; gemm avg %.1f us (%.1f TOPS); "
             "quant avg %.1f us (%.0f GB/s)" % ("packed" if packed else "row-major", ms,
                                                ops_step / ms / 1e9, gemm_ms * 1e3,
                                                ops_step / len(layers) / gemm_ms / 1e9,
                                                quant_ms * 1e3, quant_bytes / quant_ms / 1e6))
         del sets
         torch.cuda.synchronize()
-    packed_best = res[True][0] < res[False][0]
-    ms, gemm_ms, quant_ms = res[packed_best]
-    tops = ops_step / (ms * 1e-3) / 1e12
-    gemm_tops = ops_step / len(layers) / (gemm_ms * 1e-3) / 1e12
-
-    out = {
-        "metric": METRIC,
-        "value": round(tops, 2),
-        "unit": "TOPS",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8",
-        "data": "synthetic",
-        "config": {
-            "workload": "OPT-6.7B-like linear layers QKV 4096x12288, FC1 4096x16384, FC2 "
-                        "16384x4096; fp16 activations/weights/output; 2048 tokens per layer "
-                        "call; 0.5% persistent outlier channels x60; alpha 0.5",
-            "tokens": M,
-            "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant%s (3 layers)"
-                    % ("_packed" if packed_best else ""),
-            "weights": "fragment-packed" if packed_best else "row-major",
-            "other_weight_layout_ms_per_step": round(res[not packed_best][0], 4),
-            "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "kernel": "gemm_dma_kernel (i8 MFMA GEMM + fused scale back)",
-            "bound": "mfma",
-            "achieved": round(gemm_tops, 2),
-            "peak": PEAK_I8_TOPS,
-            "unit": "TOP/s",
-            "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
-            "traffic": profiled_traffic() if packed_best else None,
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
-                            "profiles/gemm_prefill_opt6.7b.md)",
-            "avg_launch_us": round(gemm_ms * 1e3, 2),
-            "per_launch_ops": ops_step / len(layers),
-        },
-        "act_quant": {"avg_launch_us": round(quant_ms * 1e3, 2),
-                      "gbs": round(quant_bytes / quant_ms / 1e6, 1),
-                      "hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3)},
+    ms, gemm_ms, quant_ms = res[True]
+    tops67 = ops_step / (ms * 1e-3) / 1e12
+    gemm67 = ops_step / len(layers) / (gemm_ms * 1e-3) / 1e12
+    out["opt6.7b_2048"] = {
+        "workload": "OPT-6.7B-like linear layers QKV 4096x12288, FC1 4096x16384, FC2 16384x4096; "
+                    "fp16; 2048 tokens; 0.5% persistent outlier channels x60; alpha 0.5",
+        "step": "per layer: sq_w8a8_linear_packed (quantiser + packed GEMM)",
+        "ms_per_step": round(ms, 4), "tops": round(tops67, 2),
+        "frac_of_int8_peak": round(tops67 / PEAK_I8_TOPS, 4),
+        "row_major_ms_per_step": round(res[False][0], 4),
+        "gemm_avg_launch_us": round(gemm_ms * 1e3, 2), "gemm_tops": round(gemm67 * 1e3, 1),
+        "gemm_frac_of_int8_peak": round(gemm67 * 1e3 / PEAK_I8_TOPS, 4),
+        "gemm_traffic": profiled_traffic("gemm_prefill_opt6.7b.md"),
+        "act_quant_avg_launch_us": round(quant_ms * 1e3, 2),
+        "act_quant_gbs": round(quant_bytes / quant_ms / 1e6, 1),
+        "act_quant_hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3),
     }
+    if args.opt67b_only:
+        print(json.dumps(out), flush=True)
+        return
+
     # ---- the same layers at 512 tokens (the configuration's smaller prefill)
     if not args.no_prefill_512:
         out["prefill_512"] = prefill_512(layers, dev, args)
@@ -718,8 +899,8 @@ def main():
         out["offline"] = offline_time(dev)
         log("offline", out["offline"])
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(layers)
+    if not args.no_cpu_baseline and host is not None:
+        out["cpu_baseline"] = cpu_baseline(host, HEAD_M, HEAD_CFG)
         log("cpu baseline", out["cpu_baseline"])
     else:
         out["cpu_baseline"] = None

@@ -348,3 +348,14 @@ def linear_w8a8(x_hat, wq, sw):
     if rc != 0:
         raise ValueError("oracle linear failed (%d)" % rc)
     return y
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads for the oracle's parallel loops (over token rows); returns
+    the number now in effect.  Timing plumbing only: no arithmetic changes."""
+    _load()
+    gomp = ctypes.CDLL("libgomp.so.1")
+    gomp.omp_set_num_threads.argtypes = [ctypes.c_int]
+    gomp.omp_set_num_threads(int(n))
+    gomp.omp_get_max_threads.restype = ctypes.c_int
+    return int(gomp.omp_get_max_threads())

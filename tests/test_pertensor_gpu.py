@@ -246,11 +246,12 @@ def _overflow_input(rng, M, K, step, dt):
     big = np.array([1e10, 1e19, 3e37, 3.3e38], np.float32)
     idx = rng.integers(0, M * K, 64)
     x.ravel()[idx] = big[rng.integers(0, 4, 64)] * np.where(rng.random(64) < 0.5, -1.0, 1.0)
-    x.ravel()[idx[:2]] = [3e37, -3e37]
+    planted = rng.choice(M * K, 2, replace=False)  # two distinct elements
+    x.ravel()[planted] = [3e37, -3e37]
     t = torch.from_numpy(x)
     if dt == "bf16":
         t = t.to(torch.bfloat16)
-    return t, idx[:2]
+    return t, planted
 
 
 @pytest.mark.parametrize("step_val", OVERFLOW_STEPS)
