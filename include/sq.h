@@ -328,6 +328,28 @@ sq_status sq_w8a8_gemm_dequant_packed_ws(const int8_t* xq, const float* x_scale,
                                          int64_t N, int64_t K, void* y, sq_dtype ydt,
                                          void* workspace, int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the split-K
+ * form of sq_w8a8_gemm_dequant_packed (results identical to it and to
+ * sq_w8a8_gemm_dequant_packed_ws) with the int32 partial sums and tile
+ * counters in a scratch array inside the library instead of a caller
+ * workspace.  Nothing is allocated: the array is a static device array of
+ * sq_noalloc_scratch_bytes() bytes (32 MiB + 16 KiB), one copy per GPU the
+ * library runs on, held until the process ends.  It fits every split the
+ * library takes on a 256-CU MI355X; a shape whose split would need more
+ * returns SQ_ERR_WORKSPACE (sq_gemm_workspace_bytes(M, N, K) gives the need).
+ * Shapes the library does not split run the plain packed GEMM and do not
+ * touch the scratch.  Each call clears the tile counters it uses (a small
+ * kernel on `stream`) before the split product.  All calls on one GPU share
+ * its array: calls that can run at the same time on one GPU (on different
+ * streams) race and must not overlap.  Other errors as
+ * sq_w8a8_gemm_dequant_packed (K % 128 == 0). */
+sq_status sq_w8a8_gemm_dequant_packed_noalloc(const int8_t* xq, const float* x_scale,
+                                              const int8_t* wq_packed, const float* w_scale,
+                                              int64_t M, int64_t N, int64_t K, void* y,
+                                              sq_dtype ydt, void* stream);
+int64_t sq_noalloc_scratch_bytes(void);
+
 /* sq_w8a8_gemm_dequant_ex with the weights in the packed layout; identical
  * results.  K % 128 == 0. */
 sq_status sq_w8a8_gemm_dequant_packed_ex(const int8_t* xq, const float* x_scale,

@@ -183,3 +183,25 @@ def test_splitk_workspace_query_and_validation(lib):
     g = lib.sq_w8a8_gemm_dequant_ws
     assert g(*args, None, need, None) == 11
     assert g(None, *args[1:], 6 * B, need, None) == 1
+
+
+def test_noalloc_validation_and_scratch_bound(lib):
+    """The allocation-free split-K entry point validates like the workspace
+    form, and its static scratch holds the workspace of every split the
+    library takes (tiles x splits <= the workgroup slots of a 256-CU GPU)."""
+    B = 1 << 32
+    f = lib.sq_w8a8_gemm_dequant_packed_noalloc
+    assert f(None, 2 * B, 3 * B, 4 * B, 128, 4096, 16384, 5 * B, 1, None) == 1
+    assert f(B, 2 * B, 3 * B, 4 * B, 128, 4096, 16064, 5 * B, 1, None) == 2   # K % 128
+    assert f(B, 2 * B, 3 * B, 4 * B, 0, 4096, 16384, 5 * B, 1, None) == 2
+    assert f(B, 2 * B, 3 * B, 4 * B, 128, 4096, 133248, 5 * B, 1, None) == 4
+    assert f(B, 2 * B, 3 * B, 4 * B, 128, 4096, 16384, 5 * B, 7, None) == 3
+    assert f(B, 2 * B, 3 * B + 8, 4 * B, 128, 4096, 16384, 5 * B, 1, None) == 5
+    cap = sq.sq_noalloc_scratch_bytes()
+    assert cap == 4 * 4096 + (32 << 20)
+    worst = 0
+    for M in list(range(65, 1025, 7)) + [128, 256, 512, 1024]:
+        for N in (128, 1000, 2048, 4096, 4100, 5120, 8192, 12288, 16384, 28672):
+            for K in (12288, 16384, 24576, 28672, 49152, 131072):
+                worst = max(worst, sq.sq_gemm_workspace_bytes(M, N, K))
+    assert 0 < worst <= cap, (worst, cap)

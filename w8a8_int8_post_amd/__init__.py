@@ -33,7 +33,8 @@ __all__ = [
     "w8a8_gemm_dequant_packed_ex", "fold_prev_linear", "SQ_ACT_NONE", "SQ_ACT_RELU",
     "sq_layernorm_quant_pertoken", "layernorm_quant_pertoken", "sq_w8a8_bmm_dequant",
     "sq_w8a8_bmm_i32", "sq_quant_weight_perchannel_batched", "w8a8_bmm_dequant", "w8a8_bmm_i32",
-    "quant_weight_perchannel_batched",
+    "quant_weight_perchannel_batched", "sq_w8a8_gemm_dequant_packed_noalloc",
+    "sq_noalloc_scratch_bytes",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -92,6 +93,7 @@ def load_library() -> ctypes.CDLL:
             "sq_quant_weight_pertensor": [P, E, I64, I64, P, P, P],
             "sq_w8a8_gemm_dequant_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
             "sq_w8a8_gemm_dequant_packed_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
+            "sq_w8a8_gemm_dequant_packed_noalloc": [P, P, P, P, I64, I64, I64, P, E, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -101,6 +103,8 @@ def load_library() -> ctypes.CDLL:
         lib.sq_packed_weight_bytes.restype = I64
         lib.sq_gemm_workspace_bytes.argtypes = [I64, I64, I64]
         lib.sq_gemm_workspace_bytes.restype = I64
+        lib.sq_noalloc_scratch_bytes.argtypes = []
+        lib.sq_noalloc_scratch_bytes.restype = I64
         lib.sq_version.argtypes = []
         lib.sq_version.restype = ctypes.c_char_p
         _lib = lib
@@ -334,6 +338,22 @@ def sq_w8a8_gemm_dequant_packed_ws(xq, x_scale, wq_packed, w_scale, N, y, worksp
           _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
           _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype], wp, wb,
           _stream(xq, stream))
+
+
+def sq_w8a8_gemm_dequant_packed_noalloc(xq, x_scale, wq_packed, w_scale, N, y, stream=None):
+    """Split-K packed GEMM with the library's static scratch (allocates nothing)."""
+    M, K = xq.shape
+    if tuple(y.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    _call("sq_w8a8_gemm_dequant_packed_noalloc", _dev(xq, "xq", torch.int8),
+          _dev(x_scale, "x_scale", torch.float32), _dev(wq_packed, "wq_packed", torch.int8),
+          _dev(w_scale, "w_scale", torch.float32), M, N, K, _dev(y, "y"), _DT[y.dtype],
+          _stream(xq, stream))
+
+
+def sq_noalloc_scratch_bytes() -> int:
+    return int(load_library().sq_noalloc_scratch_bytes())
 
 
 def sq_w8a8_gemm_dequant_packed_ex(xq, x_scale, wq_packed, w_scale, bias, act, N, y,

@@ -259,6 +259,25 @@ sq_status sq_w8a8_gemm_dequant_packed_ws(const int8_t* xq, const float* x_scale,
                    true, stream);
 }
 
+sq_status sq_w8a8_gemm_dequant_packed_noalloc(const int8_t* xq, const float* x_scale,
+                                              const int8_t* wq_packed, const float* w_scale,
+                                              int64_t M, int64_t N, int64_t K, void* y,
+                                              sq_dtype ydt, void* stream) {
+    if (!xq || !x_scale || !wq_packed || !w_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || K < 1 || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq_packed) || !aligned16(w_scale) ||
+        !aligned16(y))
+        return SQ_ERR_ALIGN;
+    if (sq::splitk_workspace_bytes(M, N, K) > sq::noalloc_scratch_bytes()) return SQ_ERR_WORKSPACE;
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_gemm_splitk_noalloc(xq, x_scale, wq_packed, w_scale, M, N, K, y,
+                                                     out, as_stream(stream)));
+}
+
+int64_t sq_noalloc_scratch_bytes(void) { return sq::noalloc_scratch_bytes(); }
+
 sq_status sq_w8a8_gemm_dequant_ex(const int8_t* xq, const float* x_scale, const int8_t* wq,
                                   const float* w_scale, const float* bias, int act, int64_t M,
                                   int64_t N, int64_t K, void* y, sq_dtype ydt, void* stream) {

@@ -33,6 +33,8 @@
 // order yields the same integer sum.
 #include "sq_gemm_common.h"
 
+#include <mutex>
+
 namespace sq {
 namespace {
 
@@ -879,6 +881,62 @@ hipError_t launch_gemm_splitk(const int8_t* xq, const float* x_scale, const int8
     }
 #undef SQ_SK
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K with the library's own scratch, for callers that cannot allocate a
+// workspace (graph capture, serving loops).  The scratch is one static device
+// array per GPU, sized for every split the library takes on a 256-CU device:
+// the tiles x splits of a split launch number at most the workgroup slots
+// (tiles * S <= 2 * CUs), and a tile holds 128 x 128 int32 sums, so the
+// slices take at most 2 * CUs * 16384 * 4 bytes = 32 MiB there.  The array's
+// name is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr int64_t kNoallocSlices = 32 << 20;
+constexpr int64_t kNoallocBytes = 4 * (int64_t)kSplitkCounters + kNoallocSlices;
+static __device__ __align__(256) int32_t scratch[kNoallocBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+__global__ __launch_bounds__(256) void zero_counters_kernel(int32_t* c, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) c[i] = 0;
+}
+}  // namespace
+
+int64_t noalloc_scratch_bytes() { return kNoallocBytes; }
+
+hipError_t launch_gemm_splitk_noalloc(const int8_t* xq, const float* x_scale, const int8_t* wp,
+                                      const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                      void* y, Out out, hipStream_t s) {
+    const int S = splitk_splits(M, N, K);
+    if (S == 1) return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int32_t* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+        }
+        ws = g_scratch_ptr[dev];
+    }
+    // the tile counters must start at zero: every split launch leaves them so,
+    // but the array keeps whatever the last call on this GPU left, so they are
+    // cleared by a small kernel (not a memset node, which graph capture would
+    // record) ahead of every split launch
+    const int tiles = (int)(((M + 127) / 128) * ((N + 127) / 128));
+    hipLaunchKernelGGL(zero_counters_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s, ws, tiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gemm_splitk(xq, x_scale, wp, w_scale, M, N, K, y, out, true, ws, s);
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int8_t* wq,

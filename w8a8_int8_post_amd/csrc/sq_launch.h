@@ -71,6 +71,13 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
 // needs (0 when there is no split).
 int splitk_splits(int64_t M, int64_t N, int64_t K);
 int64_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The split-K form on packed weights with the library's static scratch
+// instead of a caller workspace (noalloc_scratch_bytes: its size; shapes
+// whose split needs more are rejected by the entry point).
+int64_t noalloc_scratch_bytes();
+hipError_t launch_gemm_splitk_noalloc(const int8_t* xq, const float* x_scale, const int8_t* wp,
+                                      const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                      void* y, Out out, hipStream_t s);
 hipError_t launch_gemm_splitk(const int8_t* xq, const float* x_scale, const int8_t* w,
                               const float* w_scale, int64_t M, int64_t N, int64_t K, void* y,
                               Out out, bool packed, int32_t* ws, hipStream_t s);
