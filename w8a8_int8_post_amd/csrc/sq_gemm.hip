@@ -577,18 +577,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 // shape is chosen to minimise
 //     rounds * (tile area * workgroups per CU) / efficiency,
 // the time of the rounds in units of one CU's work on a 256 x 256 tile.
-// Candidates: 256 x 256 (four waves, one per SIMD, each a 128 x 128
-// register tile: a third fewer LDS fragment bytes per MFMA than eight waves
-// of 128 x 64), 256 x 192 (eight waves of 64 x 96; 512 tiles make exactly
-// two rounds of the 2048 x 12288 QKV shape that 256 x 256 covers in one and
-// a half), 128 x 128 (two per CU).  All use BK 128 and two operand stages.
-// The efficiencies are measured relative throughputs per unit of tile area
-// on whole rounds.  (K <= 128 bypasses the model: see launch_dma.)
+// Candidates: 256 x 256 (eight waves, two per SIMD, each a 64-token x
+// 128-channel register tile: while one wave of a SIMD waits at its k-tile's
+// barrier or for its fragments, the other keeps the matrix core busy; four
+// waves of 128 x 128, a third fewer LDS fragment bytes per MFMA but one wave
+// per SIMD, measured 3-10% slower: 8192 x 12288 x 49152 4654 -> 4239 us,
+// 8192 x 49152 x 12288 4418 -> 4243 us, 2048 x 16384 x 4096 141 -> 132 us),
+// 256 x 192 (eight waves of 64 x 96; 512 tiles make exactly two rounds of
+// the 2048 x 12288 QKV shape that 256 x 256 covers in one and a half),
+// 128 x 128 (two per CU).  All use BK 128 and two operand stages.  The
+// efficiencies are measured relative throughputs per unit of tile area on
+// whole rounds.  (K <= 128 bypasses the model: see launch_dma.)
 struct TileCfg {
     int bm, bn, per_cu;
     double eff;
 };
-constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.85}, {128, 128, 2, 0.82}};
+constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.81}, {128, 128, 2, 0.78}};
 
 int cu_count() {
     static int cached[64] = {0};
@@ -703,8 +707,8 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
     }
     switch (pick_tile(M, N, batch)) {
         case 0:
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 128, 128, O, PACKED, 1, 2, EXT>),
-                               dim3(tiles(256, 256), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 128, 64, 128, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(256, 256), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
         case 1:
