@@ -72,8 +72,9 @@ EX_SHAPES = [
     (2048, 12288, 256), (1999, 4100, 384),                           # 256 x 192 DMA tiles
     (2000, 12300, 128), (2047, 16380, 640),                          # 256 x 256
     (100, 300, 16384), (40, 12288, 256),                             # few-tile four-stage; wide 17-64
-    (130, 16400, 8192), (129, 32896, 8192),                          # 129-256 rows, wide and deep:
-]                                                                    # 256 x 128 / 256 x 256, four stages
+    (130, 16400, 8192), (200, 20000, 8192), (160, 33000, 8192),      # 129-256 rows, wide and deep
+    (500, 12200, 384), (500, 16300, 256),                            # 128 x 192; 256 x 128 (8 waves)
+]
 
 
 @pytest.mark.parametrize("M,N,K", EX_SHAPES)

@@ -176,8 +176,11 @@ GEMM_SHAPES = [
     (40, 12288, 256), (33, 16384, 384), (64, 12300, 128),        # 17-64 rows on wide layers: tiles
     (32, 12288, 512), (17, 28672, 256), (31, 12288, 256),        # the edge of that rule (31: few-token)
     (70, 200, 16384), (130, 260, 16384),                         # deep: 64-deep k-tiles, four stages
-    (130, 16400, 8192), (129, 32896, 8192),                      # 129-256 rows, wide and deep:
-]                                                                # 256 x 128 / 256 x 256, four stages
+    (130, 16400, 8192), (200, 20000, 8192), (160, 33000, 8192),  # 129-256 rows, wide and deep:
+                                                                 # 256 x 128 ring, 256 x 128 (8 waves), 128 x 192
+    (500, 12200, 384), (512, 12288, 256),                        # 128 x 192 tiles (one round)
+    (500, 16300, 256), (2048, 4096, 512),                        # 256 x 128 tiles, eight waves
+]
 
 
 def _codes(M, N, K, seed):

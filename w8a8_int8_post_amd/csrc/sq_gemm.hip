@@ -585,14 +585,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
 // 8192 x 49152 x 12288 4418 -> 4243 us, 2048 x 16384 x 4096 141 -> 132 us),
 // 256 x 192 (eight waves of 64 x 96; 512 tiles make exactly two rounds of
 // the 2048 x 12288 QKV shape that 256 x 256 covers in one and a half),
-// 128 x 128 (two per CU).  All use BK 128 and two operand stages.  The
-// efficiencies are measured relative throughputs per unit of tile area on
-// whole rounds.  (K <= 128 bypasses the model: see launch_dma.)
+// 128 x 128 (two per CU), 256 x 128 (eight waves of 64 x 64) and 128 x 192
+// (four waves of 64 x 96), the last two for shapes of about one round, where
+// a tile per CU with fewer operand bytes per tile beats two 128 x 128 tiles
+// (same-box sweep, 512 tokens: 512 x 12288 x 4096 38.1 -> 35.1 us with
+// 128 x 192, 512 x 16384 x 4096 44.3 -> 41.2 us with 256 x 128; 2048 x 4096 x
+// 16384 150.4 -> 138.8 us with 256 x 128).  All use BK 128 and two operand
+// stages.  The efficiencies are relative throughputs per unit of tile area
+// fitted to those measurements.  (K <= 128 bypasses the model: see
+// launch_dma.)
 struct TileCfg {
     int bm, bn, per_cu;
     double eff;
 };
-constexpr TileCfg kTiles[3] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.81}, {128, 128, 2, 0.78}};
+constexpr int kNumTiles = 5;
+constexpr TileCfg kTiles[kNumTiles] = {{256, 256, 1, 1.0}, {256, 192, 1, 0.81}, {128, 128, 2, 0.78},
+                                       {256, 128, 1, 0.80}, {128, 192, 1, 0.70}};
 
 int cu_count() {
     static int cached[64] = {0};
@@ -611,7 +619,7 @@ int pick_tile(int M, int N, int batch) {
     const int cus = cu_count();
     int best = 0;
     double best_cost = 0.0;
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < kNumTiles; ++c) {
         const TileCfg& t = kTiles[c];
         const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn) * batch;
         const int64_t slots = (int64_t)cus * t.per_cu;
@@ -667,25 +675,32 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
             return hipGetLastError();
         }
         // 129-256 rows on wide, deep layers (K >= 8192, more 128-row tiles
-        // than CUs): one row of 256-row tiles, 256 x 128 or else 256 x 256,
-        // in the same four-stage ring.  Measured: 28672 x 8192 at 129 / 256
-        // tokens 113 / 124 -> 92 / 88 us; 49152 x 12288 213 / 245 -> 186 /
-        // 208 us; 36864 x 12288 at 129 tokens 176 -> 163 us.  Not for more rows or K = 4096
-        // (there it loses: 12288 x 4096 at 512 tokens 39 -> 43 us, 4096 x
-        // 16384 at 1024 tokens 94 -> 141 us).
+        // than CUs): one row of 256 x 128 tiles when they number at most one
+        // per CU -- up to 191 rows in the four-stage ring, from 192 rows as
+        // eight waves of 64 x 64 with BK 128 in two stages -- else 128 x 192
+        // tiles (four waves of 64 x 96, BK 128, two stages).  Same-box sweep
+        // (packed weights): 28672 x 8192 at 130 / 200 / 256 tokens 72.5 /
+        // 79.3 / 80.4 us (the ring 72.5 / 80.8 / 87.2); 49152 x 12288 at 130
+        // / 200 / 256 tokens 153.8 / 164.8 / 166.5 us and 36864 x 12288 at
+        // 256 tokens 148.9 us with 128 x 192, where a row of 256 x 256 tiles
+        // in the ring took 175.3 / 191.6 / 204.7 and 188.6 us.  Not for more
+        // rows or K = 4096 (12288 x 4096 at 512 tokens: the ring 39 -> 43 us).
         if (K >= 8192 && M > 128 && M <= 256) {
             if ((int64_t)tiles(256, 128) * batch <= cus) {
-                hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 64, 128, 64, O, PACKED, 1, 4, EXT>),
-                                   dim3(tiles(256, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y,
-                                   M, N, K, epi);
+                if (M >= 192)
+                    hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 128, 64, 64, O, PACKED, 1, 2, EXT>),
+                                       dim3(tiles(256, 128), batch), dim3(512), 0, s, xq, w, sx, sw,
+                                       y, M, N, K, epi);
+                else
+                    hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 64, 128, 64, O, PACKED, 1, 4, EXT>),
+                                       dim3(tiles(256, 128), batch), dim3(256), 0, s, xq, w, sx, sw,
+                                       y, M, N, K, epi);
                 return hipGetLastError();
             }
-            if ((int64_t)tiles(256, 256) * batch <= cus) {
-                hipLaunchKernelGGL((gemm_dma_kernel<256, 256, 64, 128, 128, O, PACKED, 1, 4, EXT>),
-                                   dim3(tiles(256, 256), batch), dim3(256), 0, s, xq, w, sx, sw, y,
-                                   M, N, K, epi);
-                return hipGetLastError();
-            }
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(128, 192), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N,
+                               K, epi);
+            return hipGetLastError();
         }
     }
     if (M <= 256) {
@@ -716,9 +731,19 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                                dim3(tiles(256, 192), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
-        default:
+        case 2:
             hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2, EXT>),
                                dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
+                               epi);
+            break;
+        case 3:
+            hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 128, 64, 64, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(256, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
+                               epi);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_dma_kernel<128, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
+                               dim3(tiles(128, 192), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
                                epi);
             break;
     }
