@@ -251,6 +251,75 @@ def time_steps(fns, steps, warmup, repeats=REPEATS):
     return float(np.median(runs)), runs
 
 
+def headline_record(hd, steps, warmup):
+    """The JSON line's common part from the headline measurement (hd as
+    headline() returns it: step ms, ops per step and per GEMM launch, average
+    GEMM and quantiser launch us)."""
+    tops = hd["ops"] / (hd["ms"] * 1e-3) / 1e12
+    gemm_tops = hd["per_launch_ops"] / (hd["gemm_avg_us"] * 1e-6) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(hd["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "OPT-175B-like linear layers QKV 12288x36864, FC1 12288x49152, FC2 "
+                        "49152x12288; bf16 activations/weights/output; 8192 tokens per layer "
+                        "call; 0.1% persistent outlier channels x100; alpha 0.5",
+            "tokens": hd["M"],
+            "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant_packed (3 layers)",
+            "weights": "fragment-packed",
+            "timing": "median of %d runs of %d steps (HIP events; two buffer sets alternate); "
+                      "runs ms/step %s" % (REPEATS, steps,
+                                          ", ".join("%.4f" % r for r in hd["runs"])),
+            "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
+            "layers": hd["layers"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "gemm_dma_kernel (i8 MFMA GEMM + fused scale back), 256x256 tiles",
+            "bound": "mfma",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_I8_TOPS,
+            "unit": "TOP/s",
+            "frac": round(gemm_tops / PEAK_I8_TOPS, 4),
+            "traffic": profiled_traffic("gemm_prefill_opt175b.md"),
+            "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
+                            "profiles/gemm_prefill_opt175b.md)",
+            "avg_launch_us": round(hd["gemm_avg_us"], 2),
+            "per_launch_ops": hd["per_launch_ops"],
+        },
+        "act_quant": {"avg_launch_us": round(hd["quant_avg_us"], 2),
+                      "gbs": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3, 1),
+                      "hbm_frac": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3
+                                        / PEAK_HBM_GBS, 3)},
+    }
+    return out
+
+
+def check_peak_fractions(obj, path="out"):
+    """Every fraction of the INT8 MFMA peak in the JSON line must lie in
+    (0, 1]: a value above 1 is a unit error, never a measurement."""
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            here = "%s.%s" % (path, k)
+            if isinstance(v, (int, float)) and (k.endswith("frac_of_int8_peak")
+                                                or (k == "frac" and obj.get("bound") == "mfma")):
+                if not 0.0 < v <= 1.0:
+                    raise RuntimeError("%s = %r is not a fraction of the peak" % (here, v))
+            else:
+                check_peak_fractions(v, here)
+    return obj
+
+
 def profiled_traffic(summary):
     """HBM bytes per GEMM launch from a committed rocprofv3 summary under
     profiles/, if it was taken on the current GEMM source (else None)."""
@@ -680,56 +749,9 @@ def main():
     if not (args.opt67b_only or args.prefill_512_only):
         # ---- the headline: OPT-175B-like block, 8192 tokens, bf16
         hd, host = headline(dev, args)
-        cfg = hd["cfg"]
-        tops = hd["ops"] / (hd["ms"] * 1e-3) / 1e12
-        gemm_tops = hd["per_launch_ops"] / (hd["gemm_avg_us"] * 1e-6) / 1e12
-        out = {
-            "metric": METRIC,
-            "value": round(tops, 2),
-            "unit": "TOPS",
-            "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
-            "ms_per_step": round(hd["ms"], 4),
-            "higher_is_better": True,
-            "scaling": "weak",
-            "vs_baseline": None,
-            "dtype": "i8",
-            "data": "synthetic",
-            "config": {
-                "workload": "OPT-175B-like linear layers QKV 12288x36864, FC1 12288x49152, FC2 "
-                            "49152x12288; bf16 activations/weights/output; 8192 tokens per layer "
-                            "call; 0.1% persistent outlier channels x100; alpha 0.5",
-                "tokens": hd["M"],
-                "step": "per layer: sq_quant_act_pertoken + sq_w8a8_gemm_dequant_packed (3 layers)",
-                "weights": "fragment-packed",
-                "timing": "median of %d runs of %d steps (HIP events; two buffer sets alternate); "
-                          "runs ms/step %s" % (REPEATS, args.steps,
-                                              ", ".join("%.4f" % r for r in hd["runs"])),
-                "frac_of_int8_peak": round(tops / PEAK_I8_TOPS, 4),
-                "layers": hd["layers"],
-                "parallelism": "single GPU",
-            },
-            "roofline": {
-                "kernel": "gemm_dma_kernel (i8 MFMA GEMM + fused scale back), 256x256 tiles",
-                "bound": "mfma",
-                "achieved": round(gemm_tops * 1e3, 2),
-                "peak": PEAK_I8_TOPS,
-                "unit": "TOP/s",
-                "frac": round(gemm_tops * 1e3 / PEAK_I8_TOPS, 4),
-                "traffic": profiled_traffic("gemm_prefill_opt175b.md"),
-                "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, "
-                                "profiles/gemm_prefill_opt175b.md)",
-                "avg_launch_us": round(hd["gemm_avg_us"], 2),
-                "per_launch_ops": hd["per_launch_ops"],
-            },
-            "act_quant": {"avg_launch_us": round(hd["quant_avg_us"], 2),
-                          "gbs": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3, 1),
-                          "hbm_frac": round(hd["quant_bytes"] / hd["quant_avg_us"] / 1e3
-                                            / PEAK_HBM_GBS, 3)},
-        }
+        out = headline_record(hd, args.steps, args.warmup)
         if args.headline_only:
-            print(json.dumps(out), flush=True)
+            print(json.dumps(check_peak_fractions(out)), flush=True)
             return
 
     log("setting up the OPT-6.7B-like layers", [(ly.name, ly.K, ly.N) for ly in CFG.layers])
@@ -767,15 +789,15 @@ def main():
         "ms_per_step": round(ms, 4), "tops": round(tops67, 2),
         "frac_of_int8_peak": round(tops67 / PEAK_I8_TOPS, 4),
         "row_major_ms_per_step": round(res[False][0], 4),
-        "gemm_avg_launch_us": round(gemm_ms * 1e3, 2), "gemm_tops": round(gemm67 * 1e3, 1),
-        "gemm_frac_of_int8_peak": round(gemm67 * 1e3 / PEAK_I8_TOPS, 4),
+        "gemm_avg_launch_us": round(gemm_ms * 1e3, 2), "gemm_tops": round(gemm67, 1),
+        "gemm_frac_of_int8_peak": round(gemm67 / PEAK_I8_TOPS, 4),
         "gemm_traffic": profiled_traffic("gemm_prefill_opt6.7b.md"),
         "act_quant_avg_launch_us": round(quant_ms * 1e3, 2),
         "act_quant_gbs": round(quant_bytes / quant_ms / 1e6, 1),
         "act_quant_hbm_frac": round(quant_bytes / quant_ms / 1e6 / PEAK_HBM_GBS, 3),
     }
     if args.opt67b_only:
-        print(json.dumps(out), flush=True)
+        print(json.dumps(check_peak_fractions(out)), flush=True)
         return
 
     # ---- the same layers at 512 tokens (the configuration's smaller prefill)
@@ -905,7 +927,7 @@ def main():
     else:
         out["cpu_baseline"] = None
 
-    print(json.dumps(out), flush=True)
+    print(json.dumps(check_peak_fractions(out)), flush=True)
 
 
 if __name__ == "__main__":
