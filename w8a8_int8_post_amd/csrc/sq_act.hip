@@ -14,6 +14,8 @@
 // are spread over up to 16 wavefronts.  Rows whose length is not a multiple of 16 bytes, or
 // longer than the register budget, take a two-pass variant (the second pass
 // re-reads the row).
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_launch.h"
 
@@ -506,6 +508,30 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
     typedef typename D::T T;
     constexpr int W = VECT ? D::VEC : 1;  // elements per piece
     constexpr int RPW = NT / (64 * WPR);  // rows per workgroup
+    // The row stays in registers from load to code store.  1024-thread
+    // workgroups (a register budget of 128 per lane) with 16-bit rows hold
+    // it packed, two elements per 32-bit register, and widen each element
+    // when it is used (exact), so that rows of up to 8 pieces per lane fit
+    // without spilling; the others hold it widened to fp32.
+    constexpr bool RAW = NT == 1024 && VECT && sizeof(T) == 2;
+    constexpr int WS = RAW ? W / 2 : W;  // storage slots per piece
+    typedef typename std::conditional<RAW, uint32_t, float>::type S;
+    auto get = [](const S (&p)[WS], int e) -> float {
+        if constexpr (RAW) {
+            const uint32_t h = (e & 1) ? (p[e >> 1] >> 16) : (p[e >> 1] & 0xFFFFu);
+            return D::to_f32(__builtin_bit_cast(T, (uint16_t)h));
+        } else {
+            return p[e];
+        }
+    };
+    auto put = [](S (&p)[WS], int e, float f) {  // f is exactly representable in T
+        if constexpr (RAW) {
+            const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, D::from_f32(f));
+            p[e >> 1] = (e & 1) ? ((p[e >> 1] & 0xFFFFu) | (h << 16)) : ((p[e >> 1] & 0xFFFF0000u) | h);
+        } else {
+            p[e] = f;
+        }
+    };
     __shared__ double dred[NT / 64];
     __shared__ float fred[NT / 64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -514,12 +540,14 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
     const bool live = m < M;
     const T* row = x + (live ? m : 0) * K;
     const int64_t npc = K / W;  // pieces in the row
-    float v[NCH][W];
+    S v[NCH][WS];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
         const int64_t pc = ((int64_t)c * WPR + part) * 64 + lane;
         const int64_t pcl = pc < npc ? pc : npc - 1;  // clamped: loads stay straight-line
-        if constexpr (VECT)
+        if constexpr (RAW)
+            *reinterpret_cast<uint4*>(v[c]) = *reinterpret_cast<const uint4*>(row + pcl * W);
+        else if constexpr (VECT)
             load_vec<D>(row + pcl * W, v[c]);
         else
             v[c][0] = D::to_f32(row[pcl]);
@@ -529,7 +557,7 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
     for (int c = 0; c < NCH; ++c)
         if (((int64_t)c * WPR + part) * 64 + lane < npc)
 #pragma unroll
-            for (int e = 0; e < W; ++e) s += (double)v[c][e];
+            for (int e = 0; e < W; ++e) s += (double)get(v[c], e);
     const double mu_d = row_sum<NT, WPR>(s, dred) / (double)K;
     double q = 0.0;
 #pragma unroll
@@ -537,7 +565,7 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
         if (((int64_t)c * WPR + part) * 64 + lane < npc)
 #pragma unroll
             for (int e = 0; e < W; ++e) {
-                const double d = (double)v[c][e] - mu_d;
+                const double d = (double)get(v[c], e) - mu_d;
                 q += d * d;
             }
     const double var_d = row_sum<NT, WPR>(q, dred) / (double)K;
@@ -566,16 +594,16 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
         }
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-            float t = v[c][e] - mu;
+            float t = get(v[c], e) - mu;
             t = t * rstd;
             t = t * g[e];
             t = t + b[e];
             pin_f32(t);
-            v[c][e] = D::to_f32(D::from_f32(t));  // the value as stored in the activation dtype
+            put(v[c], e, D::to_f32(D::from_f32(t)));  // the value as stored in the activation dtype
         }
         if (pc < npc)
 #pragma unroll
-            for (int e = 0; e < W; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[c][e]));
+            for (int e = 0; e < W; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(get(v[c], e)));
     }
     amax = row_max<NT, WPR>(amax, fred);
     if (!live) return;
@@ -590,20 +618,23 @@ __global__ __launch_bounds__(NT) void ln_quant_kernel(const typename D::T* __res
         if constexpr (HAT) {
             T h[W];
 #pragma unroll
-            for (int e = 0; e < W; ++e) h[e] = D::from_f32(v[c][e]);  // exact: already in T
+            for (int e = 0; e < W; ++e) h[e] = D::from_f32(get(v[c], e));  // exact: already in T
             if constexpr (VECT)
                 *reinterpret_cast<uint4*>(hrow + pc * W) = *reinterpret_cast<const uint4*>(h);
             else
                 hrow[pc] = h[0];
         }
+        float f[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) f[e] = get(v[c], e);
         if constexpr (VECT) {
             if (step.fast)
-                store_codes<true, W>(qrow + pc * W, v[c], step);
+                store_codes<true, W>(qrow + pc * W, f, step);
             else
-                store_codes<false, W>(qrow + pc * W, v[c], step);
+                store_codes<false, W>(qrow + pc * W, f, step);
         } else {
-            qrow[pc] = (int8_t)(step.fast ? quant_code<true>(v[c][0], step)
-                                          : quant_code<false>(v[c][0], step));
+            qrow[pc] = (int8_t)(step.fast ? quant_code<true>(f[0], step)
+                                          : quant_code<false>(f[0], step));
         }
     }
 }
