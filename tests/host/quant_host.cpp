@@ -23,6 +23,21 @@ void hq_codes(const float* v, const float* step, long n, int sat, signed char* c
     }
 }
 
+// Number of fp32 bit patterns u in [lo, hi) whose code differs from the
+// definition (roundf, halves away from zero, clamped to +-127).
+long hq_rounding_mismatches(unsigned lo, unsigned long hi) {
+    long bad = 0;
+    for (unsigned long u = lo; u < hi; ++u) {
+        float t;
+        const unsigned b = (unsigned)u;
+        __builtin_memcpy(&t, &b, 4);
+        float r = __builtin_roundf(t);
+        r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
+        bad += sq::code_from_quotient(t) != (int)r;
+    }
+    return bad;
+}
+
 // The row step absmax / 127 as the kernels compute it.
 float hq_row_step(float absmax) { return sq::quant_step(absmax); }
 

@@ -46,5 +46,7 @@ def load():
         lib.hq_codes.restype = None
         lib.hq_row_step.argtypes = [ctypes.c_float]
         lib.hq_row_step.restype = ctypes.c_float
+        lib.hq_rounding_mismatches.argtypes = [ctypes.c_uint, ctypes.c_ulong]
+        lib.hq_rounding_mismatches.restype = ctypes.c_long
         _lib = lib
     return _lib

@@ -113,7 +113,14 @@ def test_quant_weight_perchannel(ref, dev, K, N, dt):
                                     (513, 512, "f16"), (600, 1024, "f32"), (1000, 2048, "f16"),
                                     (3, 49152, "bf16"), (4, 50000, "f16"), (9, 1001, "f16"),
                                     (300, 28672, "f16"), (1, 8, "bf16"), (7, 13, "f32"),
-                                    (2, 24576, "f32"), (3, 24580, "f32")])
+                                    (2, 24576, "f32"), (3, 24580, "f32"),
+                                    # many rows: two waves of 4 pieces; 8 waves of 3
+                                    # or 4; 16 waves of 6 or 8 (full and partial rows)
+                                    (600, 4096, "bf16"), (513, 4000, "f16"),
+                                    (520, 12288, "bf16"), (512, 12000, "f16"),
+                                    (513, 16384, "f16"), (516, 12296, "bf16"),
+                                    (512, 49152, "bf16"), (514, 50000, "f16"),
+                                    (512, 6144, "f32"), (530, 24576, "f32")])
 @pytest.mark.parametrize("smooth", [False, True])
 def test_quant_act_pertoken(ref, dev, M, K, dt, smooth):
     log("act_quant", M, K, dt, smooth)

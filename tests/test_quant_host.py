@@ -99,3 +99,17 @@ def test_row_step_codes_match_oracle():
             assert np.float32(st) == sx_r[m]
             np.testing.assert_array_equal(host_codes(x[m], st, sat=False), xq_r[m])
             np.testing.assert_array_equal(host_codes(x[m], st, sat=True), xq_r[m])
+
+
+def test_code_rounding_every_fp32():
+    """The kernels' rounding of a quotient to a code (one addition of
+    copysign(0.5 - 2^-25, t) and the truncating conversion, then the clamp)
+    against its definition, roundf clamped to +-127, for all 2^32 fp32 bit
+    patterns (ties, the value just below 0.5, infinities and NaN included)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    lib = hostbuild.load()
+    chunks = [(i << 28, (i + 1) << 28) for i in range(16)]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        bad = list(ex.map(lambda c: lib.hq_rounding_mismatches(c[0], c[1]), chunks))
+    assert sum(bad) == 0, bad

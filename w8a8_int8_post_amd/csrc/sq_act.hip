@@ -58,9 +58,13 @@ __device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowSt
 // Max over aligned groups of G lanes (G a power of two, at most 64).
 template <int G>
 __device__ inline float group_max(float v) {
+    if constexpr (G == 64) {
+        return wave_max_dpp(v);
+    } else {
 #pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+        for (int off = G / 2; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+        return v;
+    }
 }
 
 // Register-resident variant: WPR waves per token row, each lane holding up to
@@ -192,8 +196,13 @@ hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* sm
     } else if (M >= 512) {
         // Many rows: short rows share a wave (4, 8 or 16 lanes per row, up to
         // 4 pieces per lane: 65536 rows of 128 fp16 take 6.0 us against 6.8 us
-        // at one piece per lane); otherwise as few waves per row as hold the
-        // row at up to 8 pieces per lane, and no more pieces per lane than it needs.
+        // at one piece per lane); rows of 257-512 pieces take two waves of
+        // 4 pieces (2048 x 4096 fp16: 8.6 -> 8.0 us); longer rows take
+        // 4, 8 or 16 waves with as few pieces per lane as cover the row, so
+        // that no lane idles on the common widths (8192 x 12288: 55.0 -> 53.7
+        // us with 8 waves x 3; 2048 x 16384: 21.7 -> 20.5 us with 8 x 4;
+        // 8192 x 49152: 233.7 -> 214.9 us with 16 x 6; rows rotated past the
+        // Infinity Cache, same box).
         if (nch <= 8)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 2, SMOOTH, 4>), grid(64), dim3(256),
                                0, s, x, smooth, M, K, xq, sx);
@@ -212,15 +221,21 @@ hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* sm
         else if (nch <= 64 * 4)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH>), grid(4), dim3(256), 0,
                                s, x, smooth, M, K, xq, sx);
-        else if (nch <= 64 * 8)
-            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 8, SMOOTH>), grid(4), dim3(256), 0,
+        else if (nch <= 128 * 4)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 2, 4, SMOOTH>), grid(2), dim3(256), 0,
                                s, x, smooth, M, K, xq, sx);
         else if (nch <= 128 * 8)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 2, 8, SMOOTH>), grid(2), dim3(256), 0,
                                s, x, smooth, M, K, xq, sx);
-        else if (nch <= 256 * 8)
-            hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, 8, SMOOTH>), grid(1), dim3(256), 0,
+        else if (nch <= 512 * 3)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 8, 3, SMOOTH>), grid(1), dim3(512), 0,
                                s, x, smooth, M, K, xq, sx);
+        else if (nch <= 512 * 4)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 8, 4, SMOOTH>), grid(1), dim3(512), 0,
+                               s, x, smooth, M, K, xq, sx);
+        else if (nch <= 1024 * 6)
+            hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 6, SMOOTH>), grid(1), dim3(1024),
+                               0, s, x, smooth, M, K, xq, sx);
         else
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 8, SMOOTH>), grid(1), dim3(1024),
                                0, s, x, smooth, M, K, xq, sx);

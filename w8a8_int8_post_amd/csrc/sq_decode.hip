@@ -346,25 +346,6 @@ constexpr int kXsPad = 16;  // bytes after each token row of codes in LDS
 constexpr int kFusedMaxCpt = 16;
 constexpr int kFusedU = 2;  // 256-byte K steps per stage in the one-call layer
 
-// Max over the 64 lanes (non-negative values): DPP rotations within each row
-// of 16 lanes, then the four row results through scalar registers.
-__device__ inline float wave_max_dpp(float v) {
-    int x = __float_as_int(v);
-    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false)));
-    x = __float_as_int(v);
-    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false)));
-    x = __float_as_int(v);
-    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false)));
-    x = __float_as_int(v);
-    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false)));
-    x = __float_as_int(v);
-    const float a = __int_as_float(__builtin_amdgcn_readlane(x, 0));
-    const float b = __int_as_float(__builtin_amdgcn_readlane(x, 16));
-    const float c = __int_as_float(__builtin_amdgcn_readlane(x, 32));
-    const float d = __int_as_float(__builtin_amdgcn_readlane(x, 48));
-    return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
-}
-
 template <class D, int NW, int U, Out O, int CPT, int MM, bool STATIC>
 __global__ __launch_bounds__(NW * 64) void linear_decode_fused_kernel(
     const typename D::T* __restrict__ X, const int8_t* __restrict__ Wp,

@@ -62,8 +62,15 @@ __device__ inline void pin_f32(float& v) { __asm__("" : "+v"(v)); }
 // IEEE quotient.
 __host__ __device__ inline float quant_step(float absmax) { return absmax / 127.0f; }
 
+// Rounding half away from zero as one addition and the truncating
+// conversion: t + copysign(0.5 - 2^-25, t), rounded to nearest in fp32, has
+// round(t) as its integer part for every fp32 t (the constant, not 0.5, keeps
+// t = 0.5 - 2^-25 from rounding up to 1; beyond 127 the clamp decides, and
+// NaN gives -127 as fmax(NaN, -127) does).  Four vector instructions
+// (bit-insert, add, med3, convert) against eight for roundf and the clamp;
+// the host test checks every fp32 bit pattern against roundf.
 __host__ __device__ inline int code_from_quotient(float t) {
-    float r = __builtin_roundf(t);  // halves away from zero
+    float r = t + __builtin_copysignf(0.5f - 0x1p-25f, t);
     r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
     return (int)r;
 }
@@ -126,6 +133,26 @@ __host__ __device__ inline int quant_code(float v, const RowStep& q) {
 }
 
 // ------------------------------------------------------------ reductions
+// Max over the 64 lanes, the same value in every lane: DPP rotations within
+// each row of 16 lanes, then the four row results through scalar registers
+// (no LDS round trips, unlike a shuffle).
+__device__ inline float wave_max_dpp(float v) {
+    int x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false)));
+    x = __float_as_int(v);
+    const float a = __int_as_float(__builtin_amdgcn_readlane(x, 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(x, 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(x, 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(x, 48));
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), __builtin_fmaxf(c, d));
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
