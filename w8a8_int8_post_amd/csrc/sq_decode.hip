@@ -209,6 +209,57 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
     reduce_store<TB, NW, O, decltype(sxf), EXT>(red, acc, wave, lane, n0, M, N, sw, Y, sxf, epi);
 }
 
+// Fragment-packed weights, up to 16 tokens, one 16-channel block per
+// workgroup, no double buffering: each iteration issues the wave's U steps
+// of weight fragments and their activation fragments together, waits once,
+// then runs the MFMAs.  With the next stage's loads issued only after the
+// current MFMAs the wave keeps U steps in flight, but the code has no
+// wait that counts a later load, fewer registers (44 at U = 1: eight waves
+// per SIMD, so up to four workgroups share a CU) and a shorter tail.
+// Measured on one box against the double-buffered kernel (1 token, packed
+// weights streamed from HBM): 12288 x 4096 11.35 -> 9.76 us, 4096 x 16384
+// 13.27 -> 11.93 us, 28672 x 8192 38.7 -> 35.9 us, 8192 x 28672 37.1 -> 36.2
+// us (U = 2); 4 tokens x 28672 x 8192 40.0 -> 35.5 us (against four blocks
+// per workgroup).
+template <int U, Out O, bool EXT>
+__global__ __launch_bounds__(kNW * 64) void gemm_skinny_lean_kernel(
+    const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
+    constexpr int NW = kNW;
+    __shared__ v4i red[NW][1][64];
+    batch_entry<O>(X, Wp, sx, sw, Y, M, N, K, (int64_t)((N + 15) / 16) * 16 * K);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int b0 = blockIdx.x, n0 = b0 * 16;
+    const int r = lane & 15, g = lane >> 4;
+    const int KG = K / 64, nsteps = (KG + 3) / 4;
+    const int8_t* wblk = Wp + (int64_t)b0 * KG * 1024 + lane * 16;
+    const int8_t* xrow = X + (int64_t)(r < M ? r : M - 1) * K + g * 16;
+    v4i acc[1] = {v4i{0, 0, 0, 0}};
+    for (int st = wave; st < nsteps; st += NW * U) {
+        v4i w[U][4], x[U][1][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st + u * NW) * 4 + t;
+                w[u][t] = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4i*>(wblk + (int64_t)(c < KG ? c : KG - 1) * 1024));
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = (st + u * NW) * 4 + t;
+                const v4i v = *reinterpret_cast<const v4i*>(xrow + (c < KG ? c : KG - 1) * 64);
+                x[u][0][t] = (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
+            }
+        mfma_stage<1, U>(acc, w, x);
+    }
+    auto sxf = [&](int tok) { return sx[tok]; };
+    reduce_store<1, NW, O, decltype(sxf), EXT>(red, acc, wave, lane, n0, M, N, sw, Y, sxf, epi);
+}
+
 // ---------------------------------------------------------------------------
 // Whole decode layer in one launch (M <= 16 tokens, packed weights).  Every
 // workgroup
@@ -525,17 +576,17 @@ hipError_t launch_fused_nw(const void* x, const int8_t* wp, const float* sw, con
 #undef SQ_FUSED
 }
 
-// Wide layers with long rows take 4-wave workgroups with 4 steps per stage
-// (the same 64 KB of weights in flight per workgroup, twice as many
-// workgroups resident per CU): measured on one box, 1 token x 8192 channels
-// x 28672 outputs 40.6 -> 38.0 us; 4096-channel rows and narrow layers keep
-// 8 waves x 2 steps (4096 x 12288: 10.7 against 11.0 us; 16384 x 4096: 15.3
-// against 16.9 us).
+// Wide layers (at least 768 channel blocks) take 4-wave workgroups with 2
+// steps per stage (twice as many workgroups resident per CU as with 8
+// waves); narrow layers keep 8 waves x 2 steps.  Measured on one box, medians
+// of interleaved rounds, 1 token: 12288 x 4096 10.82 -> 10.59 us, 16384 x
+// 4096 13.10 -> 12.96 us, 28672 x 8192 37.34 (4 waves x 4 steps) -> 37.09 us;
+// 4096 x 16384 stays at 14.25 us (4 waves: 16.17).
 template <class D, Out O, bool STATIC>
 hipError_t launch_fused(const void* x, const int8_t* wp, const float* sw, const float* step,
                         int8_t* xq, float* sx, void* y, int M, int N, int K, hipStream_t s) {
-    if ((N + 15) / 16 >= 1024 && K >= 8192)
-        return launch_fused_nw<D, O, 4, 4, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
+    if ((N + 15) / 16 >= 768)
+        return launch_fused_nw<D, O, 4, 2, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
     return launch_fused_nw<D, O, kNW, kFusedU, STATIC>(x, wp, sw, step, xq, sx, y, M, N, K, s);
 }
 
@@ -578,12 +629,25 @@ hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const f
                      int N, int K, void* y, bool packed, Epi epi, hipStream_t s, int batch) {
     const int nb = (N + 15) / 16;
     const dim3 grid((unsigned)nb, (unsigned)batch), block(kNW * 64);
-    // 4 to 16 tokens, packed weights: RB blocks per workgroup share each
-    // activation fragment, as long as the grid keeps >= 192 workgroups (fewer
-    // starve the HBM stream).  Measured on one box, 16 tokens: 28672 x 8192
-    // 48.6 -> 40.9 us (RB 4), 8192 x 28672 52.6 -> 40.9 us (RB 2), 12288 x
-    // 4096 14.7 -> 12.1 us (RB 4); 4096 x 16384 keeps RB 1.
-    if (packed && TB == 1 && M >= 4 && nb >= 512) {
+    // Packed weights, up to 16 tokens: the lean kernel (U = 2 for K >= 24576)
+    // at one or two tokens, and up to 8 tokens on wide layers (>= 768
+    // channel blocks: 8 tokens x 28672 x 8192 40.4 -> 38.4 us); else, from 4
+    // tokens on >= 512 blocks, RB blocks per workgroup share each activation
+    // fragment, as long as the grid keeps >= 192 workgroups (fewer starve the
+    // HBM stream).  Measured on one box, 16 tokens: 28672 x 8192 48.6 -> 40.9
+    // us (RB 4), 8192 x 28672 52.6 -> 40.9 us (RB 2), 12288 x 4096 14.7 ->
+    // 12.1 us (RB 4); narrower layers take the lean kernel (4096 x 16384 at 16
+    // tokens 15.3 us either way).
+    const bool lean = packed && TB == 1 &&
+                      (M <= 2 || (M <= 8 && nb >= 768) || nb < 512 || M < 4);
+    if (lean) {
+        if (M <= 2 && K >= 24576)
+            hipLaunchKernelGGL((gemm_skinny_lean_kernel<2, O, EXT>), grid, block, 0, s, xq, w, sx,
+                               sw, y, M, N, K, epi);
+        else
+            hipLaunchKernelGGL((gemm_skinny_lean_kernel<1, O, EXT>), grid, block, 0, s, xq, w, sx,
+                               sw, y, M, N, K, epi);
+    } else if (packed && TB == 1 && M >= 4 && nb >= 512) {
         if (nb >= 768)
             hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, kNW, kU, O, EXT>),
                                dim3((unsigned)((nb + 3) / 4), (unsigned)batch), block, 0, s, xq, w,
