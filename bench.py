@@ -700,6 +700,37 @@ def cpu_baseline(host, M, cfg):
                            "extrapolated_step_s": round(t_one * M / CPU_SLICE_ROWS_1T, 1)}}
 
 
+def decode_phase(layers, dev, args):
+    """The OPT-6.7B-like layers at DECODE_M tokens (packed and row-major
+    weights, rotated past the Infinity Cache), per step and per GEMM launch."""
+    dec = {}
+    for Md in DECODE_M:
+        foot = sum(ly.N * ly.K + Md * ly.K * 3 + Md * ly.N * 2 for ly in layers)
+        R = n_sets(foot)
+        nbytes = sum(ly.N * ly.K + 4 * ly.N + 2 * Md * ly.K + 2 * Md * ly.N + 4 * Md
+                     for ly in layers)
+        entry = {"buffer_sets": R}
+        for packed in (True, False):
+            sets = [Bufs(layers, Md, dev, packed) for _ in range(R)]
+            ms_d = time_rotation([b.step for b in sets], max(args.steps, 4 * R), args.warmup)
+            ms_g = time_rotation([b.gemm_only for b in sets], max(args.steps, 4 * R),
+                                 args.warmup) / len(layers)
+            gbs = nbytes / (ms_d * 1e-3) / 1e9
+            gbs_g = nbytes / len(layers) / (ms_g * 1e-3) / 1e9
+            key = "packed" if packed else "row_major"
+            entry[key] = {"us_per_step": round(ms_d * 1e3, 2), "gbs": round(gbs, 1),
+                          "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "gemm_avg_launch_us": round(ms_g * 1e3, 2),
+                          "gemm_gbs": round(gbs_g, 1),
+                          "gemm_hbm_frac": round(gbs_g / PEAK_HBM_GBS, 4)}
+            log("decode M=%d (%s): %.2f us/step, %.0f GB/s (%.1f%% HBM); gemm %.2f us, %.0f GB/s"
+                % (Md, key, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS, ms_g * 1e3, gbs_g))
+            del sets
+            torch.cuda.synchronize()
+        dec["M=%d" % Md] = entry
+    return dec
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -722,6 +753,11 @@ def main():
                     help="only the OPT-6.7B-like layers at 2048 tokens (for profiling)")
     ap.add_argument("--prefill-512-only", action="store_true",
                     help="only the 512-token prefill (prints {\"prefill_512\": ...}; for profiling)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode phases (OPT-6.7B-like and Llama-70B-like; for profiling)")
+    ap.add_argument("--larger-only", action="store_true",
+                    help="only the OPT-13B-like (4096 tokens) and OPT-175B-like (2048 tokens) layers "
+                         "(for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -742,6 +778,17 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 5}))
+        return
+
+    if args.decode_only or args.larger_only:
+        part = {}
+        if args.larger_only:
+            part["larger_prefill"] = larger_prefill(dev, args)
+        if args.decode_only:
+            layers = [Layer(ly.name, dev) for ly in CFG.layers]
+            part["decode"] = decode_phase(layers, dev, args)
+            part["decode_llama70b"] = decode_llama70b(dev, args)
+        print(json.dumps(check_peak_fractions(part)), flush=True)
         return
 
     out = {}
@@ -850,32 +897,7 @@ def main():
 
     # ---- decode shapes
     if not args.no_decode:
-        dec = {}
-        for Md in DECODE_M:
-            foot = sum(ly.N * ly.K + Md * ly.K * 3 + Md * ly.N * 2 for ly in layers)
-            R = n_sets(foot)
-            nbytes = sum(ly.N * ly.K + 4 * ly.N + 2 * Md * ly.K + 2 * Md * ly.N + 4 * Md
-                         for ly in layers)
-            entry = {"buffer_sets": R}
-            for packed in (True, False):
-                sets = [Bufs(layers, Md, dev, packed) for _ in range(R)]
-                ms_d = time_rotation([b.step for b in sets], max(args.steps, 4 * R), args.warmup)
-                ms_g = time_rotation([b.gemm_only for b in sets], max(args.steps, 4 * R),
-                                     args.warmup) / len(layers)
-                gbs = nbytes / (ms_d * 1e-3) / 1e9
-                gbs_g = nbytes / len(layers) / (ms_g * 1e-3) / 1e9
-                key = "packed" if packed else "row_major"
-                entry[key] = {"us_per_step": round(ms_d * 1e3, 2), "gbs": round(gbs, 1),
-                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                              "gemm_avg_launch_us": round(ms_g * 1e3, 2),
-                              "gemm_gbs": round(gbs_g, 1),
-                              "gemm_hbm_frac": round(gbs_g / PEAK_HBM_GBS, 4)}
-                log("decode M=%d (%s): %.2f us/step, %.0f GB/s (%.1f%% HBM); gemm %.2f us, %.0f GB/s"
-                    % (Md, key, ms_d * 1e3, gbs, 100 * gbs / PEAK_HBM_GBS, ms_g * 1e3, gbs_g))
-                del sets
-                torch.cuda.synchronize()
-            dec["M=%d" % Md] = entry
-        out["decode"] = dec
+        out["decode"] = decode_phase(layers, dev, args)
         out["decode_llama70b"] = decode_llama70b(dev, args)
 
     # ---- O2 (per-tensor dynamic) and O3 (per-tensor static) activations with
