@@ -192,8 +192,8 @@ __device__ inline void wait_vm() {
 
 template <int BM, int BN, int BK, int WM, int WN, Out O, bool PACKED_B, int MINB = 1,
           int NSTAGE = 2, bool EXT = false, bool NTS = false /* non-temporal output stores */,
-          bool SPLITK = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_kernel(
+          bool SPLITK = false, int KGR = 1 /* wave groups splitting K inside the workgroup */>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_dma_kernel(
     const int8_t* __restrict__ A, const int8_t* __restrict__ B, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
     // XOR swizzle of the 16-byte chunks: chunk c of row r sits at c ^ ((r >>
@@ -204,28 +204,39 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     constexpr int SWS = BK == 64 ? 2 : 1, GM = 8;
     constexpr int KGT = BK / 64;  // packed k-groups per K tile
     static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
-    constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NT = NW * 64;
+    // KGR > 1: KGR groups of NW waves, each multiplying the whole tile over
+    // its own contiguous K range K / KGR (a multiple of BK) through its own
+    // ring of stages; group 1 hands its accumulators to group 0 through LDS
+    // after the loop, and all threads share the output stores.  Twice the
+    // loads in flight per CU for a layer whose tiles number at most one per CU.
+    static_assert(KGR == 1 || KGR == 2, "one or two wave groups along K");
+    static_assert(KGR == 1 || !SPLITK, "wave groups or split-K, not both");
+    constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NTG = NW * 64, NT = NTG * KGR;
     constexpr int TM = WM / 32, TN = WN / 32, CPR = BK / 16, S = BK / 32;
-    constexpr int A_INS = BM * CPR / NT, B_INS = BN * CPR / NT;  // 1 KB wave loads per thread
-    static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile/thread mismatch");
+    constexpr int A_INS = BM * CPR / NTG, B_INS = BN * CPR / NTG;  // 1 KB wave loads per thread
+    static_assert(BM * CPR % NTG == 0 && BN * CPR % NTG == 0, "tile/thread mismatch");
     constexpr int STAGE = (BM + BN) * BK;
     constexpr bool HALF_OUT = (O == Out::F16 || O == Out::BF16);
     constexpr int EPI_LD = BN * 2 + 16;  // staged output row pitch (bytes): padded, 16-byte aligned
     constexpr int EPI = HALF_OUT ? BM * EPI_LD : 0;
-    constexpr int SMEM = NSTAGE * STAGE > EPI ? NSTAGE * STAGE : EPI;
+    constexpr int RED = KGR > 1 ? NW * TN * TM * 16 * 64 * 4 : 0;  // group 1's accumulators
+    constexpr int RING = KGR * NSTAGE * STAGE > RED ? KGR * NSTAGE * STAGE : RED;
+    constexpr int SMEM = RING > EPI ? RING : EPI;
     constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
     static_assert(NSTAGE >= 1 && NSTAGE <= 4, "1 to 4 operand stages");
     __shared__ __attribute__((aligned(16))) int8_t smem[SMEM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave group and wave within it
+    const int grp = KGR > 1 ? (tid >> 6) / NW : 0, wave = KGR > 1 ? (tid >> 6) % NW : tid >> 6;
     // SPLITK: blockIdx.y is the split (a contiguous range of K / epi.splits,
     // a multiple of BK); otherwise it is the batch entry
-    int koff = 0;
+    int koff = grp * (K / KGR);
     if constexpr (SPLITK)
         koff = (int)blockIdx.y * (K / epi.splits);
     else
         batch_entry<O>(A, B, sx, sw, Y, M, N, K,
                        PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
     const int nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN, total = nbm * nbn;
     const int bid = blockIdx.x;
@@ -272,7 +283,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
         }
     }
     auto issue = [&](int buf, int k0) {
-        int8_t* sA = smem + buf * STAGE;
+        int8_t* sA = smem + (grp * NSTAGE + buf) * STAGE;
         int8_t* sB = sA + BM * BK;
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
@@ -299,7 +310,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     // the stage that tile kt-1 used.  One stage (short K, where a small LDS
     // footprint lets more workgroups share a CU): tile kt+1 is issued once
     // every wave is done with tile kt.
-    const int nk = (SPLITK ? K / epi.splits : K) / BK;
+    const int nk = (SPLITK ? K / epi.splits : K / KGR) / BK;
     if constexpr (NSTAGE == 1) {
         if (nk > 0) issue(0, 0);
     } else {
@@ -320,7 +331,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
         else
             wait_vm<0>();
         asm volatile("s_barrier" ::: "memory");
-        const int8_t* sA = smem + cur * STAGE;
+        const int8_t* sA = smem + (grp * NSTAGE + cur) * STAGE;
         const int8_t* sB = sA + BM * BK;
         v4i af[2][TM], bf[2][TN];
 #pragma unroll
@@ -362,6 +373,34 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
             }
         }
         cur = cur + 1 == NSTAGE ? 0 : cur + 1;
+    }
+
+    if constexpr (KGR > 1) {
+        // Every wave is past its last tile (its loads landed, its fragment
+        // reads are in registers): group 1 stores its accumulators over the
+        // operand stages, group 0 adds them (integer sums, exact).  Lane-major
+        // layout: a wave's 64 lanes write 64 consecutive words.
+        int32_t* red = reinterpret_cast<int32_t*>(smem);
+        __syncthreads();
+        if (grp == 1) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        red[(((wave * TN + j) * TM + i) * 16 + r) * 64 + lane] = acc[j][i][r];
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[j][i][r] += red[(((wave * TN + j) * TM + i) * 16 + r) * 64 + lane];
+        }
     }
 
     if constexpr (SPLITK) {
@@ -441,6 +480,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
     if constexpr (!HALF_OUT) {
         // 32-bit outputs: a lane's four consecutive channels as one 16-byte
         // store where the row allows it (N % 4 == 0, Y 16-byte aligned)
+        if (KGR > 1 && grp != 0) return;  // group 0 holds the sums (no barrier follows)
         const bool vec = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(Y) & 15) == 0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
@@ -498,7 +538,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, MINB) void gemm_dma_ker
         // entry of a product whose N is not a multiple of 4 is not)
         const bool sw_al = (reinterpret_cast<uintptr_t>(sw) & 15) == 0;
         // One 32-channel column block at a time, so that only its scales
-        // (four float4) are live next to the accumulators.
+        // (four float4) are live next to the accumulators.  With wave groups
+        // only group 0 holds sums; every thread takes part in the write-out.
+        if (KGR == 1 || grp == 0)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             float4 swv[4], bv[4];
@@ -661,17 +703,35 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         // tokens 106 -> 85; 8192 x 28672 at 384 tokens 190 -> 152; 12288 x
         // 49152 at 200 tokens 299 -> 253.  With more tiles than CUs the
         // deeper ring loses (8192 x 28672 at 768 tokens 233 -> 274 us).
+        // From K = 8192 the workgroup holds two groups of four waves, each
+        // with its own ring over half of K (twice the loads in flight per CU,
+        // no partial sums leave the workgroup).  Same-box sweep (packed
+        // weights, weights streamed from HBM): 4096 x 16384 at 512 / 256 / 65
+        // tokens 70.2 / 64.3 / 64.3 -> 61.7 / 57.9 / 59.1 us; 4096 x 8192 at
+        // 512 tokens 35.1 -> 29.4; 8192 x 28672 at 130 tokens 112.0 -> 101.9;
+        // 12288 x 49152 at 65 tokens 194.2 -> 165.7; 128 x 128 tiles: 8192 x
+        // 8192 at 512 tokens 50.7 -> 46.7 us.
         const int64_t cus = cu_count();
         if ((int64_t)tiles(128, 64) * batch <= cus) {
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 3, 4, EXT>),
-                               dim3(tiles(128, 64), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N,
-                               K, epi);
+            if (K >= 8192)
+                hipLaunchKernelGGL(
+                    (gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 1, 4, EXT, false, false, 2>),
+                    dim3(tiles(128, 64), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+            else
+                hipLaunchKernelGGL((gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 3, 4, EXT>),
+                                   dim3(tiles(128, 64), batch), dim3(256), 0, s, xq, w, sx, sw, y,
+                                   M, N, K, epi);
             return hipGetLastError();
         }
         if ((int64_t)tiles(128, 128) * batch <= cus) {
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, 64, O, PACKED, 2, 4, EXT>),
-                               dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N,
-                               K, epi);
+            if (K >= 8192)
+                hipLaunchKernelGGL(
+                    (gemm_dma_kernel<128, 128, 64, 64, 64, O, PACKED, 1, 4, EXT, false, false, 2>),
+                    dim3(tiles(128, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+            else
+                hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 64, 64, 64, O, PACKED, 2, 4, EXT>),
+                                   dim3(tiles(128, 128), batch), dim3(256), 0, s, xq, w, sx, sw, y,
+                                   M, N, K, epi);
             return hipGetLastError();
         }
         // 129-256 rows on wide, deep layers (K >= 8192, more 128-row tiles
