@@ -703,17 +703,19 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         // tokens 106 -> 85; 8192 x 28672 at 384 tokens 190 -> 152; 12288 x
         // 49152 at 200 tokens 299 -> 253.  With more tiles than CUs the
         // deeper ring loses (8192 x 28672 at 768 tokens 233 -> 274 us).
-        // From K = 8192 the workgroup holds two groups of four waves, each
+        // From K = 2048 the workgroup holds two groups of four waves, each
         // with its own ring over half of K (twice the loads in flight per CU,
-        // no partial sums leave the workgroup).  Same-box sweep (packed
-        // weights, weights streamed from HBM): 4096 x 16384 at 512 / 256 / 65
-        // tokens 70.2 / 64.3 / 64.3 -> 61.7 / 57.9 / 59.1 us; 4096 x 8192 at
-        // 512 tokens 35.1 -> 29.4; 8192 x 28672 at 130 tokens 112.0 -> 101.9;
-        // 12288 x 49152 at 65 tokens 194.2 -> 165.7; 128 x 128 tiles: 8192 x
-        // 8192 at 512 tokens 50.7 -> 46.7 us.
+        // no partial sums leave the workgroup).  Same-box sweeps (packed
+        // weights): 4096 x 16384 at 512 / 256 / 65 tokens 70.2 / 64.3 / 64.3 ->
+        // 61.7 / 57.9 / 59.1 us; 4096 x 8192 at 512 tokens 35.1 -> 29.4; 8192 x
+        // 28672 at 130 tokens 112.0 -> 101.9; 12288 x 49152 at 65 tokens 194.2
+        // -> 165.7; 12288 x 4096 at 65 tokens 18.2 -> 14.7; 4096 x 4096 at 512
+        // tokens 19.5 -> 16.9; 4096 x 2048 at 100 tokens 10.1 -> 8.7; 128 x 128
+        // tiles: 8192 x 8192 at 512 tokens 50.7 -> 46.7, 8192 x 4096 29.1 ->
+        // 27.4 us.
         const int64_t cus = cu_count();
         if ((int64_t)tiles(128, 64) * batch <= cus) {
-            if (K >= 8192)
+            if (K >= 2048)
                 hipLaunchKernelGGL(
                     (gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 1, 4, EXT, false, false, 2>),
                     dim3(tiles(128, 64), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
@@ -724,7 +726,7 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
             return hipGetLastError();
         }
         if ((int64_t)tiles(128, 128) * batch <= cus) {
-            if (K >= 8192)
+            if (K >= 2048)
                 hipLaunchKernelGGL(
                     (gemm_dma_kernel<128, 128, 64, 64, 64, O, PACKED, 1, 4, EXT, false, false, 2>),
                     dim3(tiles(128, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
@@ -802,9 +804,19 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                                epi);
             break;
         default:
-            hipLaunchKernelGGL((gemm_dma_kernel<128, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
-                               dim3(tiles(128, 192), batch), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K,
-                               epi);
+            // 128 x 192 tiles in one round (at most one per CU) from K = 2048:
+            // two groups of four waves over the two halves of K, all 160 KB
+            // of LDS (12288 x 4096 at 512 / 400 tokens 35.8 / 33.8 -> 34.0 /
+            // 32.5 us in a same-box sweep; with more tiles, or for 256 x 128
+            // tiles, the groups lose)
+            if (K >= 2048 && (int64_t)tiles(128, 192) * batch <= cu_count())
+                hipLaunchKernelGGL(
+                    (gemm_dma_kernel<128, 192, 128, 64, 96, O, PACKED, 1, 2, EXT, false, false, 2>),
+                    dim3(tiles(128, 192), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+            else
+                hipLaunchKernelGGL((gemm_dma_kernel<128, 192, 128, 64, 96, O, PACKED, 1, 2, EXT>),
+                                   dim3(tiles(128, 192), batch), dim3(256), 0, s, xq, w, sx, sw, y,
+                                   M, N, K, epi);
             break;
     }
     return hipGetLastError();
