@@ -300,9 +300,9 @@ sq_status sq_w8a8_gemm_i32_packed(const int8_t* xq, const int8_t* wq_packed, int
 /* Split-K forms of sq_w8a8_gemm_dequant and sq_w8a8_gemm_dequant_packed
  * (identical results), for few tokens against a narrow, deep layer, where the
  * output tiles alone leave most compute units idle (e.g. 128 tokens through a
- * 16384 x 4096 layer; the split is taken for K >= 12288 up to 128 tokens and
- * for K >= 24576 above, when the 128 x 128 output tiles fill at most a
- * quarter of the GPU's workgroup slots).  K is
+ * 16384 x 4096 layer; the split is taken for K >= 8192 with K % 256 == 0
+ * when the 128 x 64 output tiles number at most half the compute units,
+ * from 65 tokens on).  K is
  * split into 2, 4 or 8 ranges; each range's int32
  * partial products go to the workspace, and the scale back runs once the
  * ranges of an output tile are summed (integer sums, so the result does not
@@ -334,7 +334,7 @@ sq_status sq_w8a8_gemm_dequant_packed_ws(const int8_t* xq, const float* x_scale,
  * sq_w8a8_gemm_dequant_packed_ws) with the int32 partial sums and tile
  * counters in a scratch array inside the library instead of a caller
  * workspace.  Nothing is allocated: the array is a static device array of
- * sq_noalloc_scratch_bytes() bytes (32 MiB + 16 KiB), one copy per GPU the
+ * sq_noalloc_scratch_bytes() bytes (8 MiB + 16 KiB), one copy per GPU the
  * library runs on, held until the process ends.  It fits every split the
  * library takes on a 256-CU MI355X; a shape whose split would need more
  * returns SQ_ERR_WORKSPACE (sq_gemm_workspace_bytes(M, N, K) gives the need).

@@ -165,12 +165,16 @@ def test_splitk_workspace_query_and_validation(lib):
     # no split for few tokens (the few-token kernels) or a wide layer at many tokens
     assert sq.sq_gemm_workspace_bytes(16, 4096, 16384) == 0
     assert sq.sq_gemm_workspace_bytes(4096, 16384, 4096) == 0
-    # 128 tokens through a 16384 x 4096 layer: K split, int32 slices plus counters;
-    # 512 tokens: the plain kernel keeps up there, no split
+    # 128 tokens through a 16384 x 4096 layer: K split (64 tiles of 128 x 64,
+    # 4 splits), int32 slices plus counters; 512 tokens (one tile per CU): the
+    # plain kernel keeps up there, no split; 256 tokens on K = 28672: 2 splits
     need = sq.sq_gemm_workspace_bytes(128, 4096, 16384)
-    assert need >= 2 * 4 * 128 * 4096 and need % 256 == 0
+    assert need == 4 * 4096 + 4 * 4 * 128 * 4096
     assert sq.sq_gemm_workspace_bytes(512, 4096, 16384) == 0
-    assert sq.sq_gemm_workspace_bytes(512, 4096, 28672) > 0
+    assert sq.sq_gemm_workspace_bytes(512, 4096, 28672) == 0
+    assert sq.sq_gemm_workspace_bytes(256, 4096, 28672) == 4 * 4096 + 4 * 2 * 256 * 4096
+    assert sq.sq_gemm_workspace_bytes(128, 4096, 8320) == 0    # K % 256 != 0
+    assert sq.sq_gemm_workspace_bytes(128, 4096, 4096) == 0    # K < 8192
     assert lib.sq_gemm_workspace_bytes(0, 4, 4) == -1
     B = 1 << 32  # fake, far-apart, aligned addresses: validation never dereferences
     args = (B, 2 * B, 3 * B, 4 * B, 128, 4096, 16384, 5 * B, 1)
@@ -183,6 +187,21 @@ def test_splitk_workspace_query_and_validation(lib):
     g = lib.sq_w8a8_gemm_dequant_ws
     assert g(*args, None, need, None) == 11
     assert g(None, *args[1:], 6 * B, need, None) == 1
+
+
+@pytest.mark.parametrize("M,N,K,splits", [
+    (65, 4096, 16384, 4), (128, 1000, 8192, 4), (128, 1000, 12288, 4), (300, 4100, 8192, 1),
+    (100, 4100, 12288, 2), (300, 1000, 28672, 4), (512, 4096, 16384, 1), (128, 4096, 16384, 4),
+    (512, 4096, 28672, 1), (100, 8192, 28672, 2), (129, 2048, 9216, 4), (120, 2048, 13824, 2),
+    (128, 1024, 16384, 8), (70, 300, 24576, 8), (128, 1000, 8320, 1), (100, 12288, 4096, 1),
+    (16, 4096, 16384, 1), (200, 1002, 16384, 1), (65, 12288, 49152, 1), (256, 4096, 28672, 2),
+    (65, 8192, 49152, 2), (65, 2048, 12288, 4)])
+def test_splitk_split_counts(lib, M, N, K, splits):
+    """The split the library takes on a 256-CU device (the count a host
+    without a GPU assumes): the workspace holds the tile counters and
+    `splits` int32 slices of M x N."""
+    want = 0 if splits == 1 else 4 * 4096 + (4 * splits * M * N + 255) // 256 * 256
+    assert sq.sq_gemm_workspace_bytes(M, N, K) == want
 
 
 def test_noalloc_validation_and_scratch_bound(lib):
@@ -198,7 +217,7 @@ def test_noalloc_validation_and_scratch_bound(lib):
     assert f(B, 2 * B, 3 * B, 4 * B, 128, 4096, 16384, 5 * B, 7, None) == 3
     assert f(B, 2 * B, 3 * B + 8, 4 * B, 128, 4096, 16384, 5 * B, 1, None) == 5
     cap = sq.sq_noalloc_scratch_bytes()
-    assert cap == 4 * 4096 + (32 << 20)
+    assert cap == 4 * 4096 + (8 << 20)
     worst = 0
     for M in list(range(65, 1025, 7)) + [128, 256, 512, 1024]:
         for N in (128, 1000, 2048, 4096, 4100, 5120, 8192, 12288, 16384, 28672):

@@ -75,6 +75,7 @@ EX_SHAPES = [
     (130, 16400, 8192), (200, 20000, 8192), (160, 33000, 8192),      # 129-256 rows, wide and deep
     (500, 12200, 384), (500, 16300, 256),                            # 128 x 192; 256 x 128 (8 waves)
     (200, 8010, 8192), (300, 8192, 8192), (400, 12100, 4096),        # two wave groups over K
+    (200, 4100, 8320),                                               # the same, K % 256 != 0
 ]
 
 

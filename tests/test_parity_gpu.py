@@ -186,6 +186,7 @@ GEMM_SHAPES = [
     (200, 8010, 8192), (256, 4100, 16384),                       # few tiles, K >= 8192: two wave
     (512, 8192, 8192), (300, 8192, 8192),                        # groups over K (128 x 64; 128 x 128)
     (400, 12100, 4096), (100, 4100, 2048),                       # (128 x 192 in one round; K = 2048)
+    (200, 4100, 8320), (65, 300, 2176),                          # few tiles, K % 256 != 0: 64-deep groups
     (130, 16400, 8192), (200, 20000, 8192), (160, 33000, 8192),  # 129-256 rows, wide and deep:
                                                                  # 256 x 128 ring, 256 x 128 (8 waves), 128 x 192
     (500, 12200, 384), (512, 12288, 256),                        # 128 x 192 tiles (one round)

@@ -1,7 +1,8 @@
 """GPU parity for the split-K entry points (sq_w8a8_gemm_dequant_ws and
 sq_w8a8_gemm_dequant_packed_ws): few tokens against narrow, deep layers,
 where K is split into 2, 4 or 8 ranges whose int32 partial products meet in
-a caller-owned workspace.
+a caller-owned workspace (128 x 64 output tiles, two wave groups per
+workgroup, each over half of its split's range).
 
 Bar: outputs bit-equal to the oracle's fp32 evaluation of the scale back
 (RN(RN(fp32(acc) * sx) * sw), one rounding to the output dtype) and to the
@@ -35,29 +36,34 @@ def workspace(dev):
 
 
 CASES = [
-    (65, 4096, 16384, "f16"),     # 32 tiles: 8 splits
-    (128, 1000, 8192, "bf16"),    # K < 12288: no split
-    (128, 1000, 12288, "bf16"),   # 8 tiles: 8 splits of 1536
-    (300, 4100, 8192, "f32"),     # K < 12288: no split
-    (100, 4100, 12288, "f32"),    # ragged M and N tiles: 8 splits
-    (300, 1000, 28672, "f32"),    # ragged M and N tiles above 128 tokens, K = 28672: 8 splits
-    (512, 4096, 16384, "f16"),    # > 128 tokens, K < 24576: no split (the plain kernel)
-    (128, 4096, 16384, "bf16"),   # 32 tiles: 8 splits
-    (512, 4096, 28672, "f16"),    # 128 tiles, K = 28672: 4 splits
-    (100, 8192, 28672, "bf16"),   # 64 tiles: 8 splits
-    (129, 2048, 9216, "f16"),     # K < 12288: no split
-    (120, 2048, 13824, "f16"),    # 16 tiles; K = 108 x 128: 4 splits of 3456
-    (1000, 4096, 8192, "f16"),    # 256 tiles: no split
-    (100, 12288, 4096, "bf16"),   # K < 12288: no split
-    (2048, 4096, 16384, "f16"),   # 512 tiles: no split (the plain GEMM)
+    # split: 128 x 64 output tiles at most half the CUs, K >= 8192, K % 256 == 0;
+    # 2, 4 or 8 splits with tiles x splits <= the CUs and K / splits >= 2048
+    (65, 4096, 16384, "f16"),     # 64 tiles: 4 splits
+    (128, 1000, 8192, "bf16"),    # 16 tiles: 4 splits of 2048
+    (128, 1000, 12288, "bf16"),   # 16 tiles: 4 splits of 3072
+    (300, 4100, 8192, "f32"),     # 195 tiles: no split
+    (100, 4100, 12288, "f32"),    # ragged M and N tiles, 65 tiles: 2 splits
+    (300, 1000, 28672, "f32"),    # ragged M and N tiles above 256 tokens, 48 tiles: 4 splits
+    (512, 4096, 16384, "f16"),    # 256 tiles, one per CU: no split (the plain kernel)
+    (128, 4096, 16384, "bf16"),   # 64 tiles: 4 splits
+    (512, 4096, 28672, "f16"),    # 256 tiles: no split
+    (100, 8192, 28672, "bf16"),   # 128 tiles: 2 splits
+    (129, 2048, 9216, "f16"),     # 64 tiles: 4 splits of 2304 (two groups of 9 k-tiles)
+    (120, 2048, 13824, "f16"),    # 32 tiles; K = 54 x 256: 2 splits of 6912
+    (128, 1024, 16384, "f16"),    # 16 tiles: 8 splits
+    (70, 300, 24576, "bf16"),     # 5 tiles, N % 64 != 0: 8 splits
+    (128, 1000, 8320, "f16"),     # K % 256 != 0: no split (the plain 64-deep two-group form)
+    (1000, 4096, 8192, "f16"),    # 512 tiles: no split
+    (100, 12288, 4096, "bf16"),   # K < 8192: no split
+    (2048, 4096, 16384, "f16"),   # 1024 tiles: no split (the plain GEMM)
     (16, 4096, 16384, "f16"),     # few tokens: no split
     (200, 1002, 16384, "f16"),    # N % 4 != 0: no split
     # the plain entry points on deep layers: 128 x 64 tiles (at most one per
-    # CU) or 128 x 128 tiles, 64-deep k-tiles in a four-stage ring
+    # CU) or 128 x 128 tiles, two wave groups over K
     (129, 8320, 16384, "f16"),    # 260 narrow tiles, 130 wide: the 128 x 128 form
     (700, 4096, 16384, "bf16"),   # 192 wide tiles: the 128 x 128 form
-    (300, 5120, 20480, "f16"),    # 240 narrow tiles
-    (65, 12288, 49152, "bf16"),   # 192 narrow tiles, K = 49152
+    (300, 5120, 20480, "f16"),    # 240 narrow tiles: no split
+    (65, 12288, 49152, "bf16"),   # 192 narrow tiles, K = 49152: no split
     (200, 28672, 8192, "f16"),    # 129-256 rows, wide and deep: 224 tiles of 256 x 128
     (160, 36864, 12288, "bf16"),  # 129-256 rows: 144 tiles of 256 x 256
 ]

@@ -34,9 +34,9 @@ def _layer(dev, M, N, K, seed):
 
 # (first call, second call): both split K (the second with fewer tiles,
 # splits or a different K range), then a shape the library does not split
-PAIRS = [((128, 4096, 16384), (65, 2048, 12288)),
-         ((256, 4096, 28672), (128, 4096, 16384)),
-         ((65, 12288, 49152), (70, 300, 24576))]
+PAIRS = [((128, 4096, 16384), (65, 2048, 12288)),    # 4 splits, then 4 of fewer tiles
+         ((256, 4096, 28672), (128, 4096, 16384)),   # 2 splits, then 4
+         ((65, 8192, 49152), (70, 300, 24576))]      # 2 splits, then 8 of 5 tiles
 
 
 @pytest.mark.parametrize("first,second", PAIRS)

@@ -206,11 +206,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
     static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
     // KGR > 1: KGR groups of NW waves, each multiplying the whole tile over
     // its own contiguous K range K / KGR (a multiple of BK) through its own
-    // ring of stages; group 1 hands its accumulators to group 0 through LDS
-    // after the loop, and all threads share the output stores.  Twice the
-    // loads in flight per CU for a layer whose tiles number at most one per CU.
-    static_assert(KGR == 1 || KGR == 2, "one or two wave groups along K");
-    static_assert(KGR == 1 || !SPLITK, "wave groups or split-K, not both");
+    // ring of stages; groups 1 .. KGR-1 hand their accumulators to group 0
+    // through LDS after the loop, and all threads share the output stores.
+    // KGR times the loads in flight per CU for a layer whose tiles number at
+    // most one per CU.
+    static_assert(KGR == 1 || KGR == 2 || KGR == 4, "one, two or four wave groups along K");
     constexpr int WAVES_N = BN / WN, NW = (BM / WM) * WAVES_N, NTG = NW * 64, NT = NTG * KGR;
     constexpr int TM = WM / 32, TN = WN / 32, CPR = BK / 16, S = BK / 32;
     constexpr int A_INS = BM * CPR / NTG, B_INS = BN * CPR / NTG;  // 1 KB wave loads per thread
@@ -219,7 +219,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
     constexpr bool HALF_OUT = (O == Out::F16 || O == Out::BF16);
     constexpr int EPI_LD = BN * 2 + 16;  // staged output row pitch (bytes): padded, 16-byte aligned
     constexpr int EPI = HALF_OUT ? BM * EPI_LD : 0;
-    constexpr int RED = KGR > 1 ? NW * TN * TM * 16 * 64 * 4 : 0;  // group 1's accumulators
+    constexpr int RED_G = NW * TN * TM * 16 * 64;  // accumulator words of one group
+    constexpr int RED = (KGR - 1) * RED_G * 4;     // groups 1 .. KGR-1
     constexpr int RING = KGR * NSTAGE * STAGE > RED ? KGR * NSTAGE * STAGE : RED;
     constexpr int SMEM = RING > EPI ? RING : EPI;
     constexpr int INS = A_INS + B_INS;  // loads per thread per K tile
@@ -229,10 +230,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
     // wave group and wave within it
     const int grp = KGR > 1 ? (tid >> 6) / NW : 0, wave = KGR > 1 ? (tid >> 6) % NW : tid >> 6;
     // SPLITK: blockIdx.y is the split (a contiguous range of K / epi.splits,
-    // a multiple of BK); otherwise it is the batch entry
+    // KGR multiples of BK); otherwise it is the batch entry.  Wave group grp
+    // takes the grp-th of KGR equal parts of the workgroup's K range.
     int koff = grp * (K / KGR);
     if constexpr (SPLITK)
-        koff = (int)blockIdx.y * (K / epi.splits);
+        koff = (int)blockIdx.y * (K / epi.splits) + grp * (K / epi.splits / KGR);
     else
         batch_entry<O>(A, B, sx, sw, Y, M, N, K,
                        PACKED_B ? (int64_t)((N + 15) / 16) * 16 * K : (int64_t)N * K);
@@ -310,7 +312,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
     // the stage that tile kt-1 used.  One stage (short K, where a small LDS
     // footprint lets more workgroups share a CU): tile kt+1 is issued once
     // every wave is done with tile kt.
-    const int nk = (SPLITK ? K / epi.splits : K / KGR) / BK;
+    const int nk = (SPLITK ? K / epi.splits : K) / KGR / BK;
     if constexpr (NSTAGE == 1) {
         if (nk > 0) issue(0, 0);
     } else {
@@ -377,29 +379,33 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
 
     if constexpr (KGR > 1) {
         // Every wave is past its last tile (its loads landed, its fragment
-        // reads are in registers): group 1 stores its accumulators over the
-        // operand stages, group 0 adds them (integer sums, exact).  Lane-major
-        // layout: a wave's 64 lanes write 64 consecutive words.
+        // reads are in registers): groups 1 .. KGR-1 store their accumulators
+        // over the operand stages, each in its own slice, and group 0 adds
+        // them (integer sums, exact in any order).  Lane-major layout: a
+        // wave's 64 lanes write 64 consecutive words.
         int32_t* red = reinterpret_cast<int32_t*>(smem);
         __syncthreads();
-        if (grp == 1) {
+        if (grp != 0) {
+            int32_t* mine = red + (grp - 1) * RED_G;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        red[(((wave * TN + j) * TM + i) * 16 + r) * 64 + lane] = acc[j][i][r];
+                        mine[(((wave * TN + j) * TM + i) * 16 + r) * 64 + lane] = acc[j][i][r];
         }
         __syncthreads();
         if (grp == 0) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int g = 0; g < KGR - 1; ++g)
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[j][i][r] += red[(((wave * TN + j) * TM + i) * 16 + r) * 64 + lane];
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc[j][i][r] += red[g * RED_G + (((wave * TN + j) * TM + i) * 16 + r) * 64 + lane];
         }
     }
 
@@ -425,7 +431,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
             return __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(slices + o * MN), (short)0,
                                                      (int)(MN * 4), 0x00020000);
         };
-        {
+        if (KGR == 1 || grp == 0) {  // with wave groups, group 0 holds the sums
             const __amdgpu_buffer_rsrc_t mine = slice(split);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -450,7 +456,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64 * KGR, MINB) void gemm_d
         if (tid == 0) sk_last = atomicAdd(cnt, 1) == S - 1;
         __syncthreads();
         if (!sk_last) return;
-        for (int o = 0; o < S; ++o) {
+        for (int o = 0; o < S && (KGR == 1 || grp == 0); ++o) {
             if (o == split) continue;
             const __amdgpu_buffer_rsrc_t theirs = slice(o);
 #pragma unroll
@@ -713,9 +719,22 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
         // tokens 19.5 -> 16.9; 4096 x 2048 at 100 tokens 10.1 -> 8.7; 128 x 128
         // tiles: 8192 x 8192 at 512 tokens 50.7 -> 46.7, 8192 x 4096 29.1 ->
         // 27.4 us.
+        // In the 128 x 64 form, 128-deep k-tiles in three stages per group
+        // (144 KB of LDS) where K % 256 == 0: whole 128-byte activation row
+        // pieces per load instead of halves, and more bytes in flight (same
+        // box, packed weights, 64-deep four-stage -> 128-deep three-stage
+        // rings): 4096 x 16384 at 512 / 256 / 65 tokens 62.9 / 58.0 / 45.4 ->
+        // 53.1 / 44.9 / 41.8 us; 12288 x 49152 at 65 tokens 167.6 -> 145.2;
+        // 4096 x 4096 at 512 tokens 17.3 -> 16.1; 12288 x 4096 at 65 tokens
+        // 14.8 -> 14.6.  Four groups of 64-deep rings measured no better than
+        // two (4096 x 16384 at 512 tokens 63.9 against 63.5 us).
         const int64_t cus = cu_count();
         if ((int64_t)tiles(128, 64) * batch <= cus) {
-            if (K >= 2048)
+            if (K >= 2048 && K % 256 == 0)
+                hipLaunchKernelGGL(
+                    (gemm_dma_kernel<128, 64, 128, 64, 32, O, PACKED, 1, 3, EXT, false, false, 2>),
+                    dim3(tiles(128, 64), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+            else if (K >= 2048)
                 hipLaunchKernelGGL(
                     (gemm_dma_kernel<128, 64, 64, 64, 32, O, PACKED, 1, 4, EXT, false, false, 2>),
                     dim3(tiles(128, 64), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
@@ -799,9 +818,18 @@ hipError_t launch_dma(const int8_t* xq, const float* sx, const int8_t* w, const 
                                epi);
             break;
         case 3:
-            hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 128, 64, 64, O, PACKED, 1, 2, EXT>),
-                               dim3(tiles(256, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K,
-                               epi);
+            // 256 x 128 tiles in one round (at most one per CU): a third
+            // 128-deep stage (144 KB of LDS) keeps more bytes in flight
+            // (16384 x 4096 at 512 tokens 40.0 -> 38.8 us in a same-box
+            // sweep); with more rounds the two-stage form
+            if ((int64_t)tiles(256, 128) * batch <= cu_count())
+                hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 128, 64, 64, O, PACKED, 1, 3, EXT>),
+                                   dim3(tiles(256, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N,
+                                   K, epi);
+            else
+                hipLaunchKernelGGL((gemm_dma_kernel<256, 128, 128, 64, 64, O, PACKED, 1, 2, EXT>),
+                                   dim3(tiles(256, 128), batch), dim3(512), 0, s, xq, w, sx, sw, y, M, N,
+                                   K, epi);
             break;
         default:
             // 128 x 192 tiles in one round (at most one per CU) from K = 2048:
@@ -918,29 +946,30 @@ hipError_t launch_gemm_packed(const int8_t* xq, const float* x_scale, const int8
     return hipErrorInvalidValue;
 }
 
-// Split-K: 128 x 128 tiles, two workgroups per CU.  Workspace layout: a
-// fixed block of kSplitkCounters tile counters (only ever zero between
-// calls, whatever the shape), then the splits' int32 slices [S][M][N].
-// K is split only for deep layers (K >= 12288) whose output tiles fill at
-// most a quarter of the slots (few tokens against a narrow layer: 128 x 4096
-// x 16384 has 32 tiles for 512 slots), in 2, 4 or 8 ranges of at least 1024
-// (a multiple of 128) so that tiles x splits fills at most all slots.
-// Measured against the plain entry point (packed weights, its few-tile
-// forms): 4096 x 16384 (N x K) at 65 tokens 61 -> 50 us, 128 tokens 66 ->
-// 52 us; 4096 x 12288 at 128 tokens 55 -> 46 us; 8192 x 28672 at 65 tokens
-// 109 -> 80 us, at 256 tokens 126 -> 104 us; 12288 x 49152 at 65 tokens 192
-// -> 151 us.  Shallower layers lose (the partial sums cost more than the
-// plain kernel's idle time: 4096 x 8192 at 65 tokens 32 -> 40 us), and so do
-// layers with K < 24576 above 128 tokens (4096 x 16384 at 512 tokens: 68
-// plain, 73 split); those are not split.
+// Split-K: 128 x 64 tiles, one workgroup of two wave groups per CU (each
+// group over half of its split's K range, 128-deep k-tiles in three stages,
+// as the plain few-tile form).  Workspace layout: a fixed block of
+// kSplitkCounters tile counters (only ever zero between calls, whatever the
+// shape), then the splits' int32 slices [S][M][N].  K is split for deep
+// layers (K >= 8192, K % 256 == 0) whose 128 x 64 output tiles number at
+// most half the CUs, in 2, 4 or 8 ranges of at least 2048, so that tiles x
+// splits fills at most one workgroup per CU.  Measured against the plain
+// entry point (packed weights, the 128 x 64 few-tile form; same box): 4096 x
+// 16384 (N x K) at 65 / 128 tokens 41.6 / 44.7 -> 28.8 / 32.7 us; 4096 x
+// 12288 at 128 tokens 32.8 -> 25.0; 4096 x 8192 at 100 tokens 22.7 -> 19.6;
+// 8192 x 28672 at 65 tokens 78.8 -> 78.4 us.  Layers with more tiles lose
+// (4096 x 16384 at 512 tokens, one tile per CU: 55.0 plain, 93.3 in two
+// splits) and are not split; the earlier split form (128 x 128 tiles, two
+// workgroups of four waves per CU) took 49.0 / 50.7 / 42.3 / 23.9 / 78.3 us
+// on the shapes above.
+int64_t splitk_tiles(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 63) / 64); }
+
 int splitk_splits(int64_t M, int64_t N, int64_t K) {
-    if (M <= 64 || N % 4 != 0 || K % 128 != 0 || K < 12288) return 1;
-    if (M > 128 && K < 24576) return 1;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t slots = 2 * (int64_t)cu_count();
-    if (tiles > kSplitkCounters || 4 * tiles > slots) return 1;
+    if (M <= 64 || N % 4 != 0 || K % 256 != 0 || K < 8192) return 1;
+    const int64_t tiles = splitk_tiles(M, N), cus = cu_count();
+    if (tiles > kSplitkCounters || 2 * tiles > cus) return 1;
     int S = 1;
-    while (S < 8 && tiles * (2 * S) <= slots && K % (2 * S * 128) == 0 && K / (2 * S) >= 1024) S *= 2;
+    while (S < 8 && tiles * (2 * S) <= cus && K % (2 * S * 256) == 0 && K / (2 * S) >= 2048) S *= 2;
     return S;
 }
 
@@ -957,9 +986,9 @@ hipError_t splitk_out(const int8_t* xq, const float* sx, const int8_t* w, const 
     Epi epi;
     epi.ws = ws;
     epi.splits = S;
-    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    hipLaunchKernelGGL((gemm_dma_kernel<128, 128, 128, 64, 64, O, PACKED, 2, 2, false, false, true>),
-                       dim3(tiles, S), dim3(256), 0, s, xq, w, sx, sw, y, M, N, K, epi);
+    const int tiles = (int)splitk_tiles(M, N);
+    hipLaunchKernelGGL((gemm_dma_kernel<128, 64, 128, 64, 32, O, PACKED, 1, 3, false, false, true, 2>),
+                       dim3(tiles, S), dim3(512), 0, s, xq, w, sx, sw, y, M, N, K, epi);
     return hipGetLastError();
 }
 }  // namespace
@@ -988,12 +1017,12 @@ hipError_t launch_gemm_splitk(const int8_t* xq, const float* x_scale, const int8
 // Split-K with the library's own scratch, for callers that cannot allocate a
 // workspace (graph capture, serving loops).  The scratch is one static device
 // array per GPU, sized for every split the library takes on a 256-CU device:
-// the tiles x splits of a split launch number at most the workgroup slots
-// (tiles * S <= 2 * CUs), and a tile holds 128 x 128 int32 sums, so the
-// slices take at most 2 * CUs * 16384 * 4 bytes = 32 MiB there.  The array's
-// name is only a host-side stand-in: its device address comes from
-// hipGetSymbolAddress, once per device.
-constexpr int64_t kNoallocSlices = 32 << 20;
+// the tiles x splits of a split launch number at most the CUs (tiles * S <=
+// CUs), and a tile holds 128 x 64 int32 sums, so the slices take at most
+// 256 * 8192 * 4 bytes = 8 MiB there.  The array's name is only a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, once per
+// device.
+constexpr int64_t kNoallocSlices = 8 << 20;
 constexpr int64_t kNoallocBytes = 4 * (int64_t)kSplitkCounters + kNoallocSlices;
 static __device__ __align__(256) int32_t scratch[kNoallocBytes / 4];
 
@@ -1033,7 +1062,7 @@ hipError_t launch_gemm_splitk_noalloc(const int8_t* xq, const float* x_scale, co
     // but the array keeps whatever the last call on this GPU left, so they are
     // cleared by a small kernel (not a memset node, which graph capture would
     // record) ahead of every split launch
-    const int tiles = (int)(((M + 127) / 128) * ((N + 127) / 128));
+    const int tiles = (int)splitk_tiles(M, N);
     hipLaunchKernelGGL(zero_counters_kernel, dim3((tiles + 255) / 256), dim3(256), 0, s, ws, tiles);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
