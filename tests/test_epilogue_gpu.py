@@ -97,7 +97,8 @@ def test_gemm_dequant_ex(ref, dev, M, N, K, ydt, mode):
 PACKED_EX_SHAPES = [(1, 4096, 16384), (16, 300, 128), (33, 200, 1280), (64, 1000, 2048),
                     (300, 130, 128), (512, 2048, 4096), (2048, 12288, 256), (2000, 12300, 128),
                     (40, 12288, 256), (100, 300, 16384), (129, 8320, 16384),  # wide 17-64; deep
-                    (130, 16400, 8192)]  # 129-256 rows, wide and deep: 256 x 128 tiles
+                    (130, 16400, 8192),  # 129-256 rows, wide and deep: 256 x 128 tiles
+                    (16, 20000, 512)]    # 9-16 tokens, > 1024 blocks: 4-block 4-wave workgroups
 
 
 @pytest.mark.parametrize("M,N,K", PACKED_EX_SHAPES)

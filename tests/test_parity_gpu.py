@@ -276,7 +276,9 @@ def test_pack_weight_layout(dev, N, K):
 PACKED_SHAPES = [s for s in GEMM_SHAPES if s[2] % 128 == 0] + [
     (1, 4096, 16384), (16, 300, 128),
     # 4 to 16 tokens over 2 or 4 16-channel blocks per workgroup (ragged N too)
-    (4, 8192, 256), (16, 12288, 512), (8, 12300, 1024), (5, 8200, 384), (16, 16384, 128)]
+    (4, 8192, 256), (16, 12288, 512), (8, 12300, 1024), (5, 8200, 384), (16, 16384, 128),
+    # 9 to 16 tokens on layers of more than 1024 blocks: 4 blocks per 4-wave workgroup
+    (12, 20000, 1024), (16, 28672, 512), (9, 16400, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", PACKED_SHAPES)

@@ -284,6 +284,7 @@ template <int RB, int NW, int U, Out O, bool EXT>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_rb_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
+    static_assert(RB <= NW, "wave i sums and stores block i");
     __shared__ v4i red[NW][RB][64];
     batch_entry<O>(X, Wp, sx, sw, Y, M, N, K, (int64_t)((N + 15) / 16) * 16 * K);
     const int lane = threadIdx.x & 63;
@@ -637,7 +638,12 @@ hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const f
     // HBM stream).  Measured on one box, 16 tokens: 28672 x 8192 48.6 -> 40.9
     // us (RB 4), 8192 x 28672 52.6 -> 40.9 us (RB 2), 12288 x 4096 14.7 ->
     // 12.1 us (RB 4); narrower layers take the lean kernel (4096 x 16384 at 16
-    // tokens 15.3 us either way).
+    // tokens 15.3 us either way).  The RB 4 kernel holds 229 registers, so
+    // one 8-wave workgroup fits a CU; where its grid would take more than one
+    // round, 4-wave workgroups (two per CU) run it in one (28672 x 8192 at 16 /
+    // 12 tokens 41.2 / 41.7 -> 39.6 / 38.6 us; on layers of at most 1024
+    // blocks the 8-wave form stays ahead: 16384 x 4096 at 16 tokens 13.7
+    // against 14.2 us).
     const bool lean = packed && TB == 1 &&
                       (M <= 2 || (M <= 8 && nb >= 768) || nb < 512 || M < 4);
     if (lean) {
@@ -648,7 +654,11 @@ hipError_t skinny_tb(const int8_t* xq, const float* sx, const int8_t* w, const f
             hipLaunchKernelGGL((gemm_skinny_lean_kernel<1, O, EXT>), grid, block, 0, s, xq, w, sx,
                                sw, y, M, N, K, epi);
     } else if (packed && TB == 1 && M >= 4 && nb >= 512) {
-        if (nb >= 768)
+        if (nb >= 768 && (int64_t)((nb + 3) / 4) * batch > device_cu_count())
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, 4, kU, O, EXT>),
+                               dim3((unsigned)((nb + 3) / 4), (unsigned)batch), dim3(256), 0, s, xq,
+                               w, sx, sw, y, M, N, K, epi);
+        else if (nb >= 768)
             hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, kNW, kU, O, EXT>),
                                dim3((unsigned)((nb + 3) / 4), (unsigned)batch), block, 0, s, xq, w,
                                sx, sw, y, M, N, K, epi);
