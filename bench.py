@@ -231,6 +231,16 @@ def time_rotation(fns, iters, warmup, min_calls=4):
     return time_graphs([g], reps, wreps) / len(seq)
 
 
+def time_rotation_median(fns, iters, warmup, reps=3, min_calls=4):
+    """As time_rotation, the median of `reps` timed runs of one captured
+    graph (for the short decode steps, where one run can catch a hiccup)."""
+    seq = list(fns) * max(1, -(-min_calls // len(fns)))
+    g = capture(lambda: [f() for f in seq])
+    n = max(1, -(-iters // len(seq)))
+    w = max(1, -(-warmup // len(seq)))
+    return float(np.median([time_graphs([g], n, w) / len(seq) for _ in range(reps)]))
+
+
 def time_steps(fns, steps, warmup, repeats=REPEATS):
     """Median ms per call of fns (one graph each, replayed in rotation):
     `warmup` untimed calls, then `repeats` timed runs of exactly `steps`
@@ -432,8 +442,8 @@ def decode_llama70b(dev, args):
         for key, which in (("step", (0, 1)), ("up", (0,)), ("down", (1,))):
             nbytes = sum(lys[i][0].N * lys[i][0].K + 4 * lys[i][0].N + 2 * Md * lys[i][0].K
                          + 2 * Md * lys[i][0].N + 4 * Md for i in which)
-            ms = time_rotation([lambda b=b, w_=which: run(b, w_) for b in sets],
-                               max(args.steps, 4 * R), args.warmup)
+            ms = time_rotation_median([lambda b=b, w_=which: run(b, w_) for b in sets],
+                                      max(args.steps, 4 * R), args.warmup)
             gbs = nbytes / (ms * 1e-3) / 1e9
             ent[key] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
                         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
@@ -719,9 +729,10 @@ def decode_phase(layers, dev, args):
         entry = {"buffer_sets": R}
         for packed in (True, False):
             sets = [Bufs(layers, Md, dev, packed) for _ in range(R)]
-            ms_d = time_rotation([b.step for b in sets], max(args.steps, 4 * R), args.warmup)
-            ms_g = time_rotation([b.gemm_only for b in sets], max(args.steps, 4 * R),
-                                 args.warmup) / len(layers)
+            ms_d = time_rotation_median([b.step for b in sets], max(args.steps, 4 * R),
+                                        args.warmup)
+            ms_g = time_rotation_median([b.gemm_only for b in sets], max(args.steps, 4 * R),
+                                        args.warmup) / len(layers)
             gbs = nbytes / (ms_d * 1e-3) / 1e9
             gbs_g = nbytes / len(layers) / (ms_g * 1e-3) / 1e9
             key = "packed" if packed else "row_major"
