@@ -139,6 +139,12 @@ class Bufs:
         # split-K entry point ("ws"): one zero-filled workspace per set, the
         # size of its largest layer's need (the calls run one after another)
         self.ws = None
+        # one-call layer ("o1", packed): the few-token entry point's workspace
+        # (the fragment-packed copy of the codes; the calls run one after another)
+        self.lws = None
+        if mode == "o1" and packed:
+            need = max(sq.sq_linear_workspace_bytes(ly.x_hat.dtype, M, ly.N, ly.K) for ly in layers)
+            self.lws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
         if mode == "ws":
             need = max(sq.sq_gemm_workspace_bytes(M, ly.N, ly.K) for ly in layers)
             self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
@@ -172,8 +178,8 @@ class Bufs:
             elif self.mode == "ws":
                 sq.sq_quant_act_pertoken(x_hat, xq, sx)
                 sq.sq_w8a8_gemm_dequant_packed_ws(xq, sx, w, sw, N, y, self.ws)
-            elif self.packed:  # one call per layer; one kernel for few tokens
-                sq.sq_w8a8_linear_packed(x_hat, w, sw, xq, sx, y)
+            elif self.packed:  # one call per layer; one kernel for one or two tokens
+                sq.sq_w8a8_linear_packed_ws(x_hat, w, sw, xq, sx, y, self.lws)
             else:
                 sq.sq_quant_act_pertoken(x_hat, xq, sx)
                 self._gemm(xq, sx, w, sw, y, N)
@@ -407,8 +413,9 @@ def decode_llama70b(dev, args):
     """The decode configuration of the workload set: Llama-70B-like up
     [8192 x 28672] and down [28672 x 8192] layers, fp16, N(0, 0.015) weights
     quantised per output channel, 8 persistent outlier channels x50, 1 to 16
-    tokens; one call per layer (sq_w8a8_linear_packed), weights rotated over
-    buffer sets so that every call streams them from HBM."""
+    tokens; one call per layer (sq_w8a8_linear_packed_ws: at 13-16 tokens the
+    GEMM reads the quantiser's fragment-packed copy of the codes), weights
+    rotated over buffer sets so that every call streams them from HBM."""
     cfg = synth.CONFIGS[5]
     lys = []
     for ly in cfg.layers:
@@ -431,14 +438,15 @@ def decode_llama70b(dev, args):
             sets.append([(x[:Md].clone(), wp.clone(), sw.clone(),
                           torch.empty(Md, ly.K, dtype=torch.int8, device=dev),
                           torch.empty(Md, dtype=torch.float32, device=dev),
-                          torch.empty(Md, ly.N, dtype=torch.float16, device=dev))
+                          torch.empty(Md, ly.N, dtype=torch.float16, device=dev),
+                          sq.linear_workspace(x.dtype, Md, ly.N, ly.K, dev))
                          for ly, wp, sw, x in lys])
         ent = {"buffer_sets": R}
 
         def run(bset, which):
             for i in which:
-                xh, wp, sw, xq, sx, y = bset[i]
-                sq.sq_w8a8_linear_packed(xh, wp, sw, xq, sx, y)
+                xh, wp, sw, xq, sx, y, lws = bset[i]
+                sq.sq_w8a8_linear_packed_ws(xh, wp, sw, xq, sx, y, lws)
         for key, which in (("step", (0, 1)), ("up", (0,)), ("down", (1,))):
             nbytes = sum(lys[i][0].N * lys[i][0].K + 4 * lys[i][0].N + 2 * Md * lys[i][0].K
                          + 2 * Md * lys[i][0].N + 4 * Md for i in which)
@@ -454,7 +462,7 @@ def decode_llama70b(dev, args):
         res["M=%d" % Md] = ent
         del sets
         torch.cuda.synchronize()
-    res["step"] = ("per layer sq_w8a8_linear_packed (per-token quantisation + packed INT8 GEMM "
+    res["step"] = ("per layer sq_w8a8_linear_packed_ws (per-token quantisation + packed INT8 GEMM "
                    "+ scale back), up then down; bytes: weights + w_scale + fp16 x + fp16 y")
     del lys
     torch.cuda.synchronize()
@@ -497,7 +505,8 @@ def prefill_512(layers, dev, args, M5=512):
                100 * floor_ms / ms5))
     del sets
     torch.cuda.synchronize()
-    p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed, "
+    p512["step"] = ("per layer: sq_quant_act_pertoken + packed GEMM; plain: sq_w8a8_linear_packed_ws "
+                    "(as sq_w8a8_linear_packed at this size), "
                     "split_k: sq_w8a8_gemm_dequant_packed_ws")
     return p512
 
@@ -850,7 +859,8 @@ def main():
     out["opt6.7b_2048"] = {
         "workload": "OPT-6.7B-like linear layers QKV 4096x12288, FC1 4096x16384, FC2 16384x4096; "
                     "fp16; 2048 tokens; 0.5% persistent outlier channels x60; alpha 0.5",
-        "step": "per layer: sq_w8a8_linear_packed (quantiser + packed GEMM)",
+        "step": "per layer: sq_w8a8_linear_packed_ws (quantiser + packed GEMM; as "
+                "sq_w8a8_linear_packed at this size)",
         "ms_per_step": round(ms, 4), "tops": round(tops67, 2),
         "frac_of_int8_peak": round(tops67 / PEAK_I8_TOPS, 4),
         "row_major_ms_per_step": round(res[False][0], 4),

@@ -383,6 +383,31 @@ sq_status sq_w8a8_linear_packed_static(const void* x, sq_dtype xdt, int64_t M, i
                                        const float* step_in, int8_t* xq, float* x_scale, void* y,
                                        sq_dtype ydt, void* stream);
 
+/* sq_w8a8_linear_packed with a caller workspace that holds a second copy of
+ * the activation codes in the fragment-packed layout (the weights' layout of
+ * one 16-row block: 64-byte k-group c of token row m, inputs 64c + 16g ..
+ * +15, at byte c * 1024 + (16 g + m) * 16), written by the quantiser beside
+ * xq; the GEMM then reads each activation fragment as one contiguous
+ * kilobyte rather than 16 row pieces K bytes apart.  Used at 13-16 tokens on
+ * layers of at least 512 16-channel blocks (N > 8176), where the two-launch
+ * layer runs [P1 推論方法: per-token quantisation, then the INT8 GEMM];
+ * results identical to sq_w8a8_linear_packed (xq, x_scale and y).  Other
+ * shapes run exactly as sq_w8a8_linear_packed and do not touch the
+ * workspace.
+ *
+ * workspace: device memory owned by the caller, 16-byte aligned, at least
+ * sq_linear_workspace_bytes(xdt, M, N, K) bytes (16 * K where the copy is
+ * used, else 0; -1 for invalid arguments); no initial contents needed.
+ * Calls that run at the same time must not share a workspace.  Errors:
+ * SQ_ERR_WORKSPACE for a NULL, misaligned or too small workspace where one
+ * is needed, SQ_ERR_ALIAS when it, xq, x_scale or y overlap one another or
+ * an input; else as sq_w8a8_linear_packed. */
+int64_t sq_linear_workspace_bytes(sq_dtype xdt, int64_t M, int64_t N, int64_t K);
+sq_status sq_w8a8_linear_packed_ws(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                   const int8_t* wq_packed, const float* w_scale, int64_t N,
+                                   int8_t* xq, float* x_scale, void* y, sq_dtype ydt,
+                                   void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Library version string (static storage). */
 const char* sq_version(void);
 

@@ -224,3 +224,33 @@ def test_noalloc_validation_and_scratch_bound(lib):
             for K in (12288, 16384, 24576, 28672, 49152, 131072):
                 worst = max(worst, sq.sq_gemm_workspace_bytes(M, N, K))
     assert 0 < worst <= cap, (worst, cap)
+
+
+def test_linear_ws_query_and_validation(lib):
+    """sq_w8a8_linear_packed_ws: the workspace need by shape, and every
+    rejection before any HIP call (fake, aligned, distinct addresses)."""
+    F16, F32 = 1, 0
+    q = lib.sq_linear_workspace_bytes
+    assert q(F16, 16, 8192, 28672) == 16 * 28672      # 13-16 tokens, >= 512 channel blocks
+    assert q(F16, 13, 28672, 8192) == 16 * 8192
+    assert q(F32, 16, 8192, 28672) == 16 * 28672
+    assert q(F16, 12, 8192, 28672) == 0                # fewer tokens: the plain layer
+    assert q(F16, 17, 8192, 28672) == 0
+    assert q(F16, 16, 8176, 4096) == 0                 # 511 channel blocks
+    assert q(F16, 16, 8177, 4096) == 16 * 4096
+    assert q(F32, 16, 8192, 131072) == 0               # row beyond the register-resident quantiser
+    assert q(F16, 16, 8192, 4000) == -1 and q(F16, 0, 8192, 4096) == -1 and q(5, 16, 8192, 4096) == -1
+    x, wp, sw, xq, sx, y, ws = (1 << 20) * 16, (2 << 20) * 16, (3 << 20) * 16, (4 << 20) * 16, \
+        (5 << 20) * 16, (6 << 20) * 16, (7 << 20) * 16
+    f = lib.sq_w8a8_linear_packed_ws
+    need = 16 * 4096
+    args = lambda **k: [k.get("x", x), 1, 16, 4096, wp, sw, 8192, k.get("xq", xq), sx,
+                        k.get("y", y), 1, k.get("ws", ws), k.get("wb", need), None]
+    assert f(*args(ws=None)) == 11
+    assert f(*args(wb=need - 1)) == 11
+    assert f(*args(ws=ws + 8)) == 11
+    assert f(*args(x=None)) == 1
+    assert f(*args(ws=xq + 1024)) == 8            # workspace inside xq
+    assert f(*args(xq=x + 4096)) == 8             # codes over the activations
+    assert f(*args(y=wp + 65536)) == 8            # output over the weights
+    assert f(*args(ws=sx)) == 8

@@ -34,7 +34,8 @@ __all__ = [
     "sq_layernorm_quant_pertoken", "layernorm_quant_pertoken", "sq_w8a8_bmm_dequant",
     "sq_w8a8_bmm_i32", "sq_quant_weight_perchannel_batched", "w8a8_bmm_dequant", "w8a8_bmm_i32",
     "quant_weight_perchannel_batched", "sq_w8a8_gemm_dequant_packed_noalloc",
-    "sq_noalloc_scratch_bytes",
+    "sq_noalloc_scratch_bytes", "sq_w8a8_linear_packed_ws", "sq_linear_workspace_bytes",
+    "linear_workspace", "linear_w8a8_packed_ws",
     "calibrate_absmax", "smooth_fold", "quant_weight_perchannel", "quant_act_pertoken",
     "w8a8_gemm_dequant", "w8a8_gemm_i32", "smooth_activation", "linear_w8a8",
 ]
@@ -94,6 +95,7 @@ def load_library() -> ctypes.CDLL:
             "sq_w8a8_gemm_dequant_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
             "sq_w8a8_gemm_dequant_packed_ws": [P, P, P, P, I64, I64, I64, P, E, P, I64, P],
             "sq_w8a8_gemm_dequant_packed_noalloc": [P, P, P, P, I64, I64, I64, P, E, P],
+            "sq_w8a8_linear_packed_ws": [P, E, I64, I64, P, P, I64, P, P, P, E, P, I64, P],
         }
         for name, args in sigs.items():
             fn = getattr(lib, name)
@@ -105,6 +107,8 @@ def load_library() -> ctypes.CDLL:
         lib.sq_gemm_workspace_bytes.restype = I64
         lib.sq_noalloc_scratch_bytes.argtypes = []
         lib.sq_noalloc_scratch_bytes.restype = I64
+        lib.sq_linear_workspace_bytes.argtypes = [E, I64, I64, I64]
+        lib.sq_linear_workspace_bytes.restype = I64
         lib.sq_version.argtypes = []
         lib.sq_version.restype = ctypes.c_char_p
         _lib = lib
@@ -412,6 +416,26 @@ def sq_w8a8_linear_packed(x, wq_packed, w_scale, xq, x_scale, y, stream=None):
           _DT[y.dtype], _stream(x, stream))
 
 
+def sq_linear_workspace_bytes(x_dtype, M: int, N: int, K: int) -> int:
+    n = load_library().sq_linear_workspace_bytes(_DT[x_dtype], M, N, K)
+    if n < 0:
+        raise ValueError("invalid shape")
+    return n
+
+
+def sq_w8a8_linear_packed_ws(x, wq_packed, w_scale, xq, x_scale, y, workspace, stream=None):
+    M, K = x.shape
+    N = w_scale.shape[0]
+    if tuple(xq.shape) != (M, K) or tuple(y.shape) != (M, N) or x_scale.shape[0] != M:
+        raise ValueError("shape mismatch")
+    _check_packed(wq_packed, N, K)
+    wp, wb = _ws(workspace)
+    _call("sq_w8a8_linear_packed_ws", _dev(x, "x"), _DT[x.dtype], M, K,
+          _dev(wq_packed, "wq_packed", torch.int8), _dev(w_scale, "w_scale", torch.float32), N,
+          _dev(xq, "xq", torch.int8), _dev(x_scale, "x_scale", torch.float32), _dev(y, "y"),
+          _DT[y.dtype], wp, wb, _stream(x, stream))
+
+
 # --------------------------------------------------------------------------
 # Allocating conveniences (outputs from torch.empty on the input's device)
 
@@ -597,6 +621,27 @@ def linear_w8a8_packed(x_hat, wq_packed, w_scale, out_dtype=torch.float16, strea
     sx = torch.empty(M, dtype=torch.float32, device=x_hat.device)
     y = torch.empty(M, N, dtype=out_dtype, device=x_hat.device)
     sq_w8a8_linear_packed(x_hat, wq_packed, w_scale, xq, sx, y, stream)
+    return y, xq, sx
+
+
+def linear_workspace(x_dtype, M: int, N: int, K: int, device) -> torch.Tensor:
+    """A workspace for sq_w8a8_linear_packed_ws (at least 16 bytes, so that a
+    shape that needs none still gets a valid pointer)."""
+    n = max(sq_linear_workspace_bytes(x_dtype, M, N, K), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def linear_w8a8_packed_ws(x_hat, wq_packed, w_scale, out_dtype=torch.float16, workspace=None,
+                          stream=None):
+    """sq_w8a8_linear_packed_ws: (y, xq, sx)."""
+    M, K = x_hat.shape
+    N = w_scale.shape[0]
+    if workspace is None:
+        workspace = linear_workspace(x_hat.dtype, M, N, K, x_hat.device)
+    xq = torch.empty(M, K, dtype=torch.int8, device=x_hat.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x_hat.device)
+    y = torch.empty(M, N, dtype=out_dtype, device=x_hat.device)
+    sq_w8a8_linear_packed_ws(x_hat, wq_packed, w_scale, xq, sx, y, workspace, stream)
     return y, xq, sx
 
 

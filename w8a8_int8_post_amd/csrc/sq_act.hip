@@ -38,8 +38,10 @@ __device__ inline void load_smoothed(const typename D::T* p, const float* smooth
     }
 }
 
+// dst2 (nullable): a second place for the same codes (the fragment-packed copy).
 template <bool FAST, int V, bool SAT = false>
-__device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowStep& step) {
+__device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowStep& step,
+                                   int8_t* dst2 = nullptr) {
     if constexpr (V == 8) {
         uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -47,12 +49,23 @@ __device__ inline void store_codes(int8_t* dst, const float (&v)[V], const RowSt
 #pragma unroll
         for (int e = 0; e < 4; ++e) hi |= (uint32_t)(uint8_t)quant_code<FAST, SAT>(v[4 + e], step) << (8 * e);
         *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        if (dst2) *reinterpret_cast<uint2*>(dst2) = make_uint2(lo, hi);
     } else {
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w |= (uint32_t)(uint8_t)quant_code<FAST, SAT>(v[e], step) << (8 * e);
         *reinterpret_cast<uint32_t*>(dst) = w;
+        if (dst2) *reinterpret_cast<uint32_t*>(dst2) = w;
     }
+}
+
+// Byte offset of code k of token row m (m < 16) in the fragment-packed copy:
+// 64-byte k-group c is one 1 KB block whose 16-byte piece g * 16 + m holds
+// row m, inputs 64c + 16g .. +15 (the weights' packed layout for one block of
+// 16 rows, so that a few-token GEMM reads each activation fragment as one
+// contiguous kilobyte).
+__device__ inline int64_t packed_code_offset(int64_t m, int64_t k) {
+    return (k >> 6) * 1024 + ((((k & 63) >> 4) << 4) + m) * 16 + (k & 15);
 }
 
 // Max over aligned groups of G lanes (G a power of two, at most 64).
@@ -78,7 +91,8 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
                                                            const float* __restrict__ smooth,
                                                            int64_t M, int64_t K,
                                                            int8_t* __restrict__ xq,
-                                                           float* __restrict__ sx) {
+                                                           float* __restrict__ sx,
+                                                           int8_t* __restrict__ xp) {
     static_assert(LPR == 64 || WPR == 1, "rows shorter than a wave take one wave part");
     constexpr int V = D::VEC;
     constexpr int RPV = 64 / LPR;               // rows per wave
@@ -143,17 +157,19 @@ __global__ __launch_bounds__(NT) void act_quant_reg_kernel(const typename D::T* 
     const RowStep step = row_step(amax);
     if (part == 0 && sub == 0) sx[m] = step.step;
     int8_t* qrow = xq + m * K;
+    // xp (nullable, fewer than 16 rows): the fragment-packed copy as well
+    auto pk = [&](int64_t ci) { return xp ? xp + packed_code_offset(m, ci * V) : nullptr; };
     if (step.fast) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
-            if (ci < nch) store_codes<true, V>(qrow + ci * V, v[c], step);
+            if (ci < nch) store_codes<true, V>(qrow + ci * V, v[c], step, pk(ci));
         }
     } else {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int64_t ci = ((int64_t)c * WPR + part) * LPR + sub;
-            if (ci < nch) store_codes<false, V>(qrow + ci * V, v[c], step);
+            if (ci < nch) store_codes<false, V>(qrow + ci * V, v[c], step, pk(ci));
         }
     }
 }
@@ -186,7 +202,7 @@ __global__ __launch_bounds__(NT) void act_quant_2pass_kernel(const typename D::T
 
 template <class D, bool SMOOTH>
 hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* smooth, int8_t* xq,
-                           float* sx, hipStream_t s) {
+                           float* sx, hipStream_t s, int8_t* xp) {
     const typename D::T* x = static_cast<const typename D::T*>(xv);
     const int64_t nch = K / D::VEC;  // 16-byte pieces per row
     auto grid = [&](int rows_per_wg) { return dim3((unsigned)((M + rows_per_wg - 1) / rows_per_wg)); };
@@ -205,48 +221,48 @@ hipError_t act_quant_typed(const void* xv, int64_t M, int64_t K, const float* sm
         // Infinity Cache, same box).
         if (nch <= 8)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 2, SMOOTH, 4>), grid(64), dim3(256),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 16)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH, 4>), grid(64), dim3(256),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 32)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH, 8>), grid(32), dim3(256),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 64)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH, 16>), grid(16), dim3(256),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 64 * 2)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 2, SMOOTH>), grid(4), dim3(256), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 64 * 4)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 1, 4, SMOOTH>), grid(4), dim3(256), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 128 * 4)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 2, 4, SMOOTH>), grid(2), dim3(256), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 128 * 8)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 2, 8, SMOOTH>), grid(2), dim3(256), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 512 * 3)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 8, 3, SMOOTH>), grid(1), dim3(512), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 512 * 4)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 512, 8, 4, SMOOTH>), grid(1), dim3(512), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else if (nch <= 1024 * 6)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 6, SMOOTH>), grid(1), dim3(1024),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
         else
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 8, SMOOTH>), grid(1), dim3(1024),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
     } else {
         // Few rows (decode): spread each row over up to 16 waves.
         if (nch <= 256 * 4)
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 256, 4, 4, SMOOTH>), grid(1), dim3(256), 0,
-                               s, x, smooth, M, K, xq, sx);
+                               s, x, smooth, M, K, xq, sx, xp);
         else
             hipLaunchKernelGGL((act_quant_reg_kernel<D, 1024, 16, 8, SMOOTH>), grid(1), dim3(1024),
-                               0, s, x, smooth, M, K, xq, sx);
+                               0, s, x, smooth, M, K, xq, sx, xp);
     }
     return hipGetLastError();
 }
@@ -726,20 +742,29 @@ hipError_t launch_static_act_step(const float* a, const float* smooth, int64_t K
 }
 
 hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
-                            int8_t* xq, float* x_scale, hipStream_t s) {
+                            int8_t* xq, float* x_scale, hipStream_t s, int8_t* xp) {
     const bool sm = smooth != nullptr;
+    if (xp && !act_quant_packs(dt, M, K)) return hipErrorInvalidValue;
     switch (dt) {
         case Dt::F32:
-            return sm ? act_quant_typed<F32, true>(x, M, K, smooth, xq, x_scale, s)
-                      : act_quant_typed<F32, false>(x, M, K, smooth, xq, x_scale, s);
+            return sm ? act_quant_typed<F32, true>(x, M, K, smooth, xq, x_scale, s, xp)
+                      : act_quant_typed<F32, false>(x, M, K, smooth, xq, x_scale, s, xp);
         case Dt::F16:
-            return sm ? act_quant_typed<F16, true>(x, M, K, smooth, xq, x_scale, s)
-                      : act_quant_typed<F16, false>(x, M, K, smooth, xq, x_scale, s);
+            return sm ? act_quant_typed<F16, true>(x, M, K, smooth, xq, x_scale, s, xp)
+                      : act_quant_typed<F16, false>(x, M, K, smooth, xq, x_scale, s, xp);
         case Dt::BF16:
-            return sm ? act_quant_typed<BF16, true>(x, M, K, smooth, xq, x_scale, s)
-                      : act_quant_typed<BF16, false>(x, M, K, smooth, xq, x_scale, s);
+            return sm ? act_quant_typed<BF16, true>(x, M, K, smooth, xq, x_scale, s, xp)
+                      : act_quant_typed<BF16, false>(x, M, K, smooth, xq, x_scale, s, xp);
     }
     return hipErrorInvalidValue;
+}
+
+// The register-resident kernel (which alone writes the fragment-packed copy)
+// takes the rows: at most 16 rows (the copy's block), K a multiple of the
+// 16-byte piece and at most 8192 pieces.
+bool act_quant_packs(Dt dt, int64_t M, int64_t K) {
+    const int64_t vec = dt == Dt::F32 ? 4 : 8;
+    return M >= 1 && M <= 16 && K % vec == 0 && K / vec <= 16 * 64 * 8;
 }
 
 hipError_t launch_smooth_act(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,

@@ -396,4 +396,40 @@ sq_status sq_w8a8_linear_packed_static(const void* x, sq_dtype xdt, int64_t M, i
                                                       as_stream(stream)));
 }
 
+int64_t sq_linear_workspace_bytes(sq_dtype xdt, int64_t M, int64_t N, int64_t K) {
+    if (!dims_ok(M, N) || !dims_ok(K, 1) || K % 128 != 0 || K > SQ_MAX_K || !dt_ok(xdt)) return -1;
+    return sq::linear_workspace_bytes(to_dt(xdt), M, N, K);
+}
+
+sq_status sq_w8a8_linear_packed_ws(const void* x, sq_dtype xdt, int64_t M, int64_t K,
+                                   const int8_t* wq_packed, const float* w_scale, int64_t N,
+                                   int8_t* xq, float* x_scale, void* y, sq_dtype ydt,
+                                   void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!x || !wq_packed || !w_scale || !xq || !x_scale || !y) return SQ_ERR_NULL;
+    if (!dims_ok(M, N) || !dims_ok(K, 1) || K % 128 != 0) return SQ_ERR_SHAPE;
+    if (K > SQ_MAX_K) return SQ_ERR_K_OVERFLOW;
+    if (!dt_ok(xdt) || !dt_ok(ydt)) return SQ_ERR_DTYPE;
+    if (!aligned16(x) || !aligned16(wq_packed) || !aligned16(w_scale) || !aligned16(xq) ||
+        !aligned16(x_scale) || !aligned16(y))
+        return SQ_ERR_ALIGN;
+    const int64_t need = sq::linear_workspace_bytes(to_dt(xdt), M, N, K);
+    if (need > 0) {
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need) return SQ_ERR_WORKSPACE;
+        const void* ins[] = {x, wq_packed, w_scale};
+        const int64_t inn[] = {M * K * dt_bytes(xdt), sq::packed_weight_bytes(N, K), 4 * N};
+        const void* outs[] = {workspace, xq, x_scale, y};
+        const int64_t outn[] = {need, M * K, 4 * M, M * N * dt_bytes(ydt)};
+        for (int o = 0; o < 4; ++o) {
+            for (int i = 0; i < 3; ++i)
+                if (overlaps(outs[o], outn[o], ins[i], inn[i])) return SQ_ERR_ALIAS;
+            for (int p = o + 1; p < 4; ++p)
+                if (overlaps(outs[o], outn[o], outs[p], outn[p])) return SQ_ERR_ALIAS;
+        }
+    }
+    sq::Out out = ydt == SQ_F16 ? sq::Out::F16 : (ydt == SQ_BF16 ? sq::Out::BF16 : sq::Out::F32);
+    return hip_status(sq::launch_linear_packed_ws(
+        x, to_dt(xdt), M, K, wq_packed, w_scale, N, xq, x_scale, y, out,
+        need > 0 ? static_cast<int8_t*>(workspace) : nullptr, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -280,7 +280,10 @@ __global__ __launch_bounds__(kNW * 64) void gemm_skinny_lean_kernel(
 // fragments (RB MFMAs), so with many tokens the activation reads (one
 // kilobyte per fragment, 16 distinct rows) stop doubling the bytes each CU
 // loads per weight byte.
-template <int RB, int NW, int U, Out O, bool EXT>
+// PX: X is the fragment-packed copy of the codes (one 16-row block, 1 KB per
+// 64-byte k-group, as the quantiser's packed output), so each activation
+// fragment is one contiguous kilobyte instead of 16 row pieces K bytes apart.
+template <int RB, int NW, int U, Out O, bool EXT, bool PX = false>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_rb_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
@@ -318,7 +321,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_rb_kernel(
             for (int t = 0; t < 4; ++t) {
                 const int c = (st + u * NW) * 4 + t;
                 const int tt = r < M ? r : M - 1, cc = c < KG ? c : KG - 1;
-                const v4i v = *reinterpret_cast<const v4i*>(X + (int64_t)tt * K + cc * 64 + g * 16);
+                const v4i v = PX ? *reinterpret_cast<const v4i*>(X + (int64_t)cc * 1024 + lane * 16)
+                                 : *reinterpret_cast<const v4i*>(X + (int64_t)tt * K + cc * 64 + g * 16);
                 x[u][t] = (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
             }
     };
@@ -689,6 +693,44 @@ hipError_t skinny_out(const int8_t* xq, const float* sx, const int8_t* w, const 
 
 }  // namespace
 
+// The packed-activation GEMM applies where the two-launch layer runs the
+// RB-block kernel at 13-16 tokens: there each activation fragment spans 16
+// token rows, and reading it as one kilobyte of the packed copy saves 1-2 us
+// per layer on the Llama-70B-like layers (28672 x 8192 at 16 tokens 40.1 ->
+// 38.0 us, 8192 x 28672 42.2 -> 41.2 us; at 4-12 tokens no gain).
+bool packed_x_applies(int64_t M, int64_t N) { return M >= 13 && M <= 16 && (N + 15) / 16 >= 512; }
+
+hipError_t launch_skinny_px(const int8_t* xp, const float* sx, const int8_t* wp, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* y, Out out, hipStream_t s) {
+    if (!packed_x_applies(M, N)) return hipErrorInvalidValue;
+    const int nb = (int)((N + 15) / 16), m = (int)M, n = (int)N, k = (int)K;
+    const Epi epi;
+#define SQ_PX(O)                                                                                   \
+    do {                                                                                           \
+        if (nb >= 768 && (nb + 3) / 4 > device_cu_count())                                         \
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, 4, kU, O, false, true>),           \
+                               dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, xp, wp, sx, sw, y, \
+                               m, n, k, epi);                                                      \
+        else if (nb >= 768)                                                                        \
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, kNW, kU, O, false, true>),         \
+                               dim3((unsigned)((nb + 3) / 4)), dim3(kNW * 64), 0, s, xp, wp, sx,   \
+                               sw, y, m, n, k, epi);                                               \
+        else                                                                                       \
+            hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<2, kNW, kU, O, false, true>),         \
+                               dim3((unsigned)((nb + 1) / 2)), dim3(kNW * 64), 0, s, xp, wp, sx,   \
+                               sw, y, m, n, k, epi);                                               \
+        return hipGetLastError();                                                                  \
+    } while (0)
+    switch (out) {
+        case Out::F16: SQ_PX(Out::F16);
+        case Out::BF16: SQ_PX(Out::BF16);
+        case Out::F32: SQ_PX(Out::F32);
+        default: break;
+    }
+#undef SQ_PX
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, const float* sw,
                          int M, int N, int K, void* y, Out out, bool packed, hipStream_t s,
                          Epi epi, int batch) {
@@ -713,6 +755,24 @@ hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, con
     hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s);
     if (e != hipSuccess) return e;
     return launch_gemm_packed(xq, x_scale, wp, w_scale, M, N, K, y, out, s);
+}
+
+int64_t linear_workspace_bytes(Dt xdt, int64_t M, int64_t N, int64_t K) {
+    if (fused_fits(xdt, M, K) || !packed_x_applies(M, N) || !act_quant_packs(xdt, M, K)) return 0;
+    return 16 * K;
+}
+
+// As launch_linear_packed; at 13-16 tokens on layers of >= 512 channel
+// blocks the quantiser also writes the fragment-packed copy of the codes
+// into xp, which the GEMM then reads.
+hipError_t launch_linear_packed_ws(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
+                                   const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
+                                   void* y, Out out, int8_t* xp, hipStream_t s) {
+    if (linear_workspace_bytes(xdt, M, N, K) == 0)
+        return launch_linear_packed(x, xdt, M, K, wp, w_scale, N, xq, x_scale, y, out, s);
+    hipError_t e = launch_act_quant(x, xdt, M, K, nullptr, xq, x_scale, s, xp);
+    if (e != hipSuccess) return e;
+    return launch_skinny_px(xp, x_scale, wp, w_scale, M, N, K, y, out, s);
 }
 
 hipError_t launch_linear_packed_static(const void* x, Dt xdt, int64_t M, int64_t K,

@@ -30,8 +30,11 @@ hipError_t launch_smooth_fold(const float* a, const void* w, Dt dt, int64_t K, i
                               hipStream_t s);
 hipError_t launch_quant_weight(const void* w, Dt dt, int64_t K, int64_t N, int8_t* wq,
                                float* w_scale, hipStream_t s);
+// xp (nullable): also write the codes in the fragment-packed layout of one
+// 16-row block (act_quant_packs must hold).
 hipError_t launch_act_quant(const void* x, Dt dt, int64_t M, int64_t K, const float* smooth,
-                            int8_t* xq, float* x_scale, hipStream_t s);
+                            int8_t* xq, float* x_scale, hipStream_t s, int8_t* xp = nullptr);
+bool act_quant_packs(Dt dt, int64_t M, int64_t K);
 hipError_t launch_act_quant_pertensor(const void* x, Dt dt, int64_t M, int64_t K,
                                       const float* smooth, const float* step, int8_t* xq,
                                       float* x_scale, hipStream_t s);
@@ -90,6 +93,10 @@ hipError_t launch_skinny(const int8_t* xq, const float* sx, const int8_t* w, con
 hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
                                 const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
                                 void* y, Out out, hipStream_t s);
+int64_t linear_workspace_bytes(Dt xdt, int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_packed_ws(const void* x, Dt xdt, int64_t M, int64_t K, const int8_t* wp,
+                                   const float* w_scale, int64_t N, int8_t* xq, float* x_scale,
+                                   void* y, Out out, int8_t* xp, hipStream_t s);
 hipError_t launch_linear_packed_static(const void* x, Dt xdt, int64_t M, int64_t K,
                                        const int8_t* wp, const float* w_scale, int64_t N,
                                        const float* step, int8_t* xq, float* x_scale, void* y,
