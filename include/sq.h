@@ -389,8 +389,9 @@ sq_status sq_w8a8_linear_packed_static(const void* x, sq_dtype xdt, int64_t M, i
  * +15, at byte c * 1024 + (16 g + m) * 16), written by the quantiser beside
  * xq; the GEMM then reads each activation fragment as one contiguous
  * kilobyte rather than 16 row pieces K bytes apart.  Used at 13-16 tokens on
- * layers of at least 512 16-channel blocks (N > 8176), where the two-launch
- * layer runs [P1 推論方法: per-token quantisation, then the INT8 GEMM];
+ * layers of at least 512 16-channel blocks (N > 8176) or of K >= 16384, where
+ * the two-launch layer runs [P1 推論方法: per-token quantisation, then the
+ * INT8 GEMM];
  * results identical to sq_w8a8_linear_packed (xq, x_scale and y).  Other
  * shapes run exactly as sq_w8a8_linear_packed and do not touch the
  * workspace.

@@ -238,6 +238,10 @@ def test_linear_ws_query_and_validation(lib):
     assert q(F16, 17, 8192, 28672) == 0
     assert q(F16, 16, 8176, 4096) == 0                 # 511 channel blocks
     assert q(F16, 16, 8177, 4096) == 16 * 4096
+    assert q(F16, 16, 4096, 16384) == 16 * 16384       # narrower, but K >= 16384
+    assert q(F16, 13, 16, 16384) == 16 * 16384
+    assert q(F16, 16, 4096, 16256) == 0                # narrower and K < 16384
+    assert q(F16, 12, 4096, 16384) == 0
     assert q(F32, 16, 8192, 131072) == 0               # row beyond the register-resident quantiser
     assert q(F16, 16, 8192, 4000) == -1 and q(F16, 0, 8192, 4096) == -1 and q(5, 16, 8192, 4096) == -1
     x, wp, sw, xq, sx, y, ws = (1 << 20) * 16, (2 << 20) * 16, (3 << 20) * 16, (4 << 20) * 16, \

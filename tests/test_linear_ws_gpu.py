@@ -92,6 +92,9 @@ CASES = [
     (15, 12290, 1024, "bf16", "bf16"),  # ragged, four blocks per workgroup
     (16, 8192, 4096, "bf16", "f32"),
     (16, 8192, 28672, "f32", "f16"),    # fp32 rows of 7168 pieces
+    (16, 4096, 16384, "f16", "f16"),    # 256 blocks, K >= 16384: the lean kernel on the packed copy
+    (13, 4100, 16384, "bf16", "f32"),   # ragged last block
+    (15, 16, 20480, "f32", "bf16"),     # one block
     # shapes that run as sq_w8a8_linear_packed (workspace untouched)
     (12, 8192, 4096, "f16", "f16"), (16, 4096, 4096, "f16", "f16"), (1, 4096, 4096, "f16", "f16"),
     (17, 8192, 1024, "f16", "f16"), (16, 8177, 32896, "f32", "f16"),  # fp32 row past 8192 pieces

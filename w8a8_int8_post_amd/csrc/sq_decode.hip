@@ -221,7 +221,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_packed_kernel(
 // 13.27 -> 11.93 us, 28672 x 8192 38.7 -> 35.9 us, 8192 x 28672 37.1 -> 36.2
 // us (U = 2); 4 tokens x 28672 x 8192 40.0 -> 35.5 us (against four blocks
 // per workgroup).
-template <int U, Out O, bool EXT>
+// PX: X is the fragment-packed copy of the codes (as in the RB-block kernel
+// below): each activation fragment is one contiguous kilobyte.
+template <int U, Out O, bool EXT, bool PX = false>
 __global__ __launch_bounds__(kNW * 64) void gemm_skinny_lean_kernel(
     const int8_t* __restrict__ X, const int8_t* __restrict__ Wp, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, Epi epi) {
@@ -251,7 +253,9 @@ __global__ __launch_bounds__(kNW * 64) void gemm_skinny_lean_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int c = (st + u * NW) * 4 + t;
-                const v4i v = *reinterpret_cast<const v4i*>(xrow + (c < KG ? c : KG - 1) * 64);
+                const int cc = c < KG ? c : KG - 1;
+                const v4i v = PX ? *reinterpret_cast<const v4i*>(X + (int64_t)cc * 1024 + lane * 16)
+                                 : *reinterpret_cast<const v4i*>(xrow + cc * 64);
                 x[u][0][t] = (r < M && c < KG) ? v : v4i{0, 0, 0, 0};
             }
         mfma_stage<1, U>(acc, w, x);
@@ -694,20 +698,33 @@ hipError_t skinny_out(const int8_t* xq, const float* sx, const int8_t* w, const 
 }  // namespace
 
 // The packed-activation GEMM applies where the two-launch layer runs the
-// RB-block kernel at 13-16 tokens: there each activation fragment spans 16
+// RB-block kernel at 13-16 tokens (and on deep narrow layers, below): there
+// each activation fragment spans 16
 // token rows, and reading it as one kilobyte of the packed copy saves 1-2 us
 // per layer on the Llama-70B-like layers (28672 x 8192 at 16 tokens 40.1 ->
 // 38.0 us, 8192 x 28672 42.2 -> 41.2 us; at 4-12 tokens no gain).
-bool packed_x_applies(int64_t M, int64_t N) { return M >= 13 && M <= 16 && (N + 15) / 16 >= 512; }
+// Narrower layers (< 512 blocks) run the lean kernel on the packed copy where
+// K >= 16384, where each workgroup's 16 x K codes are as many bytes as its
+// weights.  Measured on one box (quantiser + GEMM per call, fp16, medians of
+// interleaved rounds, weights past the Infinity Cache; row-major codes ->
+// packed copy): 16 x 4096 x 16384 (M x N x K) 19.9 -> 18.2 us, 16 x 2048 x
+// 16384 18.3 -> 17.1 us, 13 x 4096 x 16384 18.3 -> 18.2 us; shallower layers
+// lose (16 x 4096 x 4096 12.5 -> 13.0 us, 16 x 1024 x 8192 13.4 -> 13.8 us).
+bool packed_x_applies(int64_t M, int64_t N, int64_t K) {
+    return M >= 13 && M <= 16 && ((N + 15) / 16 >= 512 || K >= 16384);
+}
 
 hipError_t launch_skinny_px(const int8_t* xp, const float* sx, const int8_t* wp, const float* sw,
                             int64_t M, int64_t N, int64_t K, void* y, Out out, hipStream_t s) {
-    if (!packed_x_applies(M, N)) return hipErrorInvalidValue;
+    if (!packed_x_applies(M, N, K)) return hipErrorInvalidValue;
     const int nb = (int)((N + 15) / 16), m = (int)M, n = (int)N, k = (int)K;
     const Epi epi;
 #define SQ_PX(O)                                                                                   \
     do {                                                                                           \
-        if (nb >= 768 && (nb + 3) / 4 > device_cu_count())                                         \
+        if (nb < 512)                                                                              \
+            hipLaunchKernelGGL((gemm_skinny_lean_kernel<1, O, false, true>), dim3((unsigned)nb),   \
+                               dim3(kNW * 64), 0, s, xp, wp, sx, sw, y, m, n, k, epi);             \
+        else if (nb >= 768 && (nb + 3) / 4 > device_cu_count())                                    \
             hipLaunchKernelGGL((gemm_skinny_packed_rb_kernel<4, 4, kU, O, false, true>),           \
                                dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, s, xp, wp, sx, sw, y, \
                                m, n, k, epi);                                                      \
@@ -758,7 +775,7 @@ hipError_t launch_linear_packed(const void* x, Dt xdt, int64_t M, int64_t K, con
 }
 
 int64_t linear_workspace_bytes(Dt xdt, int64_t M, int64_t N, int64_t K) {
-    if (fused_fits(xdt, M, K) || !packed_x_applies(M, N) || !act_quant_packs(xdt, M, K)) return 0;
+    if (fused_fits(xdt, M, K) || !packed_x_applies(M, N, K) || !act_quant_packs(xdt, M, K)) return 0;
     return 16 * K;
 }
 
